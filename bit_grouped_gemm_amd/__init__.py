@@ -1,0 +1,220 @@
+"""Python binding of the MI355X low-bit MoE expert layer (libmoe.so).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI in ``include/moe.h``.  PyTorch provides device memory and
+the current stream.  There is no CPU or PyTorch fallback: if the library is
+missing, importing the entry points raises.
+
+Entry points (same names as the C ABI):
+    moe_workspace_size(cfg) -> int
+    moe_permute(cfg, x, topk_ids) -> (counts, offsets, expand_idx, row_token, xq, xs)
+    moe_grouped_gemm1_swiglu(cfg, xq, xs, row_token, offsets, weights, ws) -> (hq, hs)
+    moe_grouped_gemm2(cfg, hq, hs, offsets, weights, ws) -> y
+    moe_combine(cfg, y, expand_idx, offsets, topk_weights) -> out
+    moe_layer(cfg, x, topk_ids, topk_weights, weights, ws=None, out=None) -> out
+"""
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+import os
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_build", "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_NULL_ARG = 1
+MOE_ERR_BAD_SHAPE = 2
+MOE_ERR_UNSUPPORTED = 3
+MOE_ERR_WORKSPACE = 4
+MOE_ERR_MISALIGNED = 5
+MOE_ERR_HIP = 6
+
+WFMT_FP8_BLOCK = 0
+WFMT_MXFP4 = 1
+
+EXPORTS = ("moe_workspace_size", "moe_permute", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm2",
+           "moe_combine", "moe_layer", "moe_status_str")
+
+
+class MoeCfg(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("T", "H", "I", "E", "topk", "wfmt", "wblk", "act_group",
+                                          "has_shared")]
+
+
+class MoeWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("w1", "w1s", "w2", "w2s", "sw1", "sw1s", "sw2", "sw2s")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({status_str(status)})")
+
+
+_lib: Optional[C.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> C.CDLL:
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with bit_grouped_gemm_amd.build.build() "
+                          "(hipcc, gfx950); there is no fallback implementation")
+    L = C.CDLL(path)
+    vp, sz = C.c_void_p, C.c_size_t
+    cfgp = C.POINTER(MoeCfg)
+    wp = C.POINTER(MoeWeights)
+    L.moe_workspace_size.argtypes = [cfgp, C.POINTER(sz)]
+    L.moe_permute.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_grouped_gemm1_swiglu.argtypes = [cfgp, vp, vp, vp, vp, wp, vp, vp, vp, sz, vp]
+    L.moe_grouped_gemm2.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp]
+    L.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
+    L.moe_layer.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp]
+    L.moe_status_str.argtypes = [C.c_int]
+    L.moe_status_str.restype = C.c_char_p
+    for n in EXPORTS:
+        if n != "moe_status_str":
+            getattr(L, n).restype = C.c_int
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return load().moe_status_str(int(status)).decode()
+
+
+# ------------------------------------------------------------------ helpers
+@dataclasses.dataclass(frozen=True)
+class Cfg:
+    T: int
+    H: int
+    I: int
+    E: int
+    topk: int
+    wfmt: int
+    wblk: int
+    act_group: int
+    has_shared: int = 0
+
+    def c(self) -> MoeCfg:
+        return MoeCfg(self.T, self.H, self.I, self.E, self.topk, self.wfmt, self.wblk, self.act_group,
+                      self.has_shared)
+
+    @classmethod
+    def for_workload(cls, wl, T: int) -> "Cfg":
+        return cls(T, wl.H, wl.I, wl.E, wl.topk, wl.wfmt, wl.wblk, wl.act_group, int(wl.shared))
+
+    def with_T(self, T: int) -> "Cfg":
+        return dataclasses.replace(self, T=T)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the HIP library must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the HIP library must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != MOE_OK:
+        raise MoeError(fn, rc)
+
+
+def weights_struct(w) -> MoeWeights:
+    """moe_weights from an object with w1, w1s, w2, w2s[, sw1, sw1s, sw2, sw2s] tensors."""
+    g = lambda n: _ptr(getattr(w, n, None))
+    return MoeWeights(g("w1"), g("w1s"), g("w2"), g("w2s"), g("sw1"), g("sw1s"), g("sw2"), g("sw2s"))
+
+
+def _u16(x: torch.Tensor) -> torch.Tensor:
+    return x.view(torch.int16) if x.dtype == torch.bfloat16 else x
+
+
+# ------------------------------------------------------------------ entry points
+def moe_workspace_size(cfg: Cfg) -> int:
+    n = C.c_size_t(0)
+    c = cfg.c()
+    _check("moe_workspace_size", load().moe_workspace_size(C.byref(c), C.byref(n)))
+    return int(n.value)
+
+
+def workspace(cfg: Cfg, device="cuda") -> torch.Tensor:
+    return torch.empty(moe_workspace_size(cfg), dtype=torch.uint8, device=device)
+
+
+def moe_permute(cfg: Cfg, x: torch.Tensor, topk_ids: torch.Tensor):
+    dev = x.device
+    T, k, E, sh = cfg.T, cfg.topk, cfg.E, cfg.has_shared
+    counts = torch.empty(E + sh, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1 + sh, dtype=torch.int32, device=dev)
+    eidx = torch.empty(T * k, dtype=torch.int32, device=dev)
+    rtok = torch.empty(T * k + T * sh, dtype=torch.int32, device=dev)
+    xq = torch.empty(T, cfg.H, dtype=torch.uint8, device=dev)
+    xs = torch.empty(T, cfg.H // cfg.act_group, dtype=torch.float32, device=dev)
+    c = cfg.c()
+    _check("moe_permute", load().moe_permute(C.byref(c), _ptr(_u16(x)), _ptr(topk_ids), _ptr(counts),
+                                             _ptr(offsets), _ptr(eidx), _ptr(rtok), _ptr(xq), _ptr(xs),
+                                             None, 0, _stream()))
+    return counts, offsets, eidx, rtok, xq, xs
+
+
+def moe_grouped_gemm1_swiglu(cfg: Cfg, xq, xs, row_token, offsets, weights, ws: Optional[torch.Tensor] = None,
+                             rows: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    dev = xq.device
+    R = rows if rows is not None else cfg.T * cfg.topk + cfg.T * cfg.has_shared
+    hq = torch.empty(R, cfg.I, dtype=torch.uint8, device=dev)
+    hs = torch.empty(R, cfg.I // cfg.act_group, dtype=torch.float32, device=dev)
+    ws = workspace(cfg, dev) if ws is None else ws
+    c, w = cfg.c(), weights_struct(weights)
+    _check("moe_grouped_gemm1_swiglu",
+           load().moe_grouped_gemm1_swiglu(C.byref(c), _ptr(xq), _ptr(xs), _ptr(row_token), _ptr(offsets),
+                                           C.byref(w), _ptr(hq), _ptr(hs), _ptr(ws), ws.numel(), _stream()))
+    return hq, hs
+
+
+def moe_grouped_gemm2(cfg: Cfg, hq, hs, offsets, weights, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    dev = hq.device
+    y = torch.empty(hq.shape[0], cfg.H, dtype=torch.float32, device=dev)
+    ws = workspace(cfg, dev) if ws is None else ws
+    c, w = cfg.c(), weights_struct(weights)
+    _check("moe_grouped_gemm2",
+           load().moe_grouped_gemm2(C.byref(c), _ptr(hq), _ptr(hs), _ptr(offsets), C.byref(w), _ptr(y),
+                                    _ptr(ws), ws.numel(), _stream()))
+    return y
+
+
+def moe_combine(cfg: Cfg, y, expand_idx, offsets, topk_weights) -> torch.Tensor:
+    out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device=y.device)
+    c = cfg.c()
+    _check("moe_combine", load().moe_combine(C.byref(c), _ptr(y), _ptr(expand_idx), _ptr(offsets),
+                                             _ptr(topk_weights), _ptr(_u16(out)), _stream()))
+    return out
+
+
+def moe_layer(cfg: Cfg, x, topk_ids, topk_weights, weights, ws: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device=x.device)
+    ws = workspace(cfg, x.device) if ws is None else ws
+    c, w = cfg.c(), weights_struct(weights)
+    _check("moe_layer", load().moe_layer(C.byref(c), _ptr(_u16(x)), _ptr(topk_ids), _ptr(topk_weights), C.byref(w),
+                                         _ptr(_u16(out)), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def raw_call(name: str, *args) -> int:
+    """Call a C entry point with raw ctypes arguments (for argument-check tests)."""
+    return int(getattr(load(), name)(*args))

@@ -1,0 +1,277 @@
+// moe_api.hip -- the C ABI declared in include/moe.h: argument checks, shape
+// heuristics, workspace carve-up and the launch sequence.  Host code only;
+// the kernels live in moe_kernels.hip.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <initializer_list>
+#include <utility>
+
+#include "../../include/moe.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+static int choose_split(long units, int nks) {
+  // more workgroups than ~4 per CU buy nothing; fewer than ~2 per CU leave
+  // HBM bandwidth idle at decode, so K is split until the unit count fills
+  // the 256 CUs, keeping at least 4 K steps (512 K) per workgroup
+  int best = 1;
+  for (int d = 2; d <= nks; ++d) {
+    if (nks % d) continue;
+    if (units * d > 1024 || nks / d < 4) break;
+    best = d;
+  }
+  return best;
+}
+
+static int choose_ntt(int T, int k, int E) {
+  const double rows = double(T) * k;
+  const double groups = std::fmin(double(E), rows);
+  if (groups <= 0) return 1;
+  const double avg = rows / groups;
+  const double est = avg + 3.0 * std::sqrt(avg) + 1.0;
+  return est <= 16 ? 1 : (est <= 32 ? 2 : 4);
+}
+
+Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, int shared) {
+  Shape s{};
+  s.T = T; s.H = H; s.I = I; s.E = E; s.k = k; s.wfmt = wfmt; s.wblk = wblk; s.G = G; s.shared = shared;
+  s.ngroups = E + shared;
+  s.rows_cap = T * k + T * shared;
+  s.slots_max = (T > 0) ? (std::min(E, T * k) + shared) : 0;
+  s.g1_tiles = I / 128;
+  s.g2_tiles = H / 128;
+  s.g1_ntt = s.g2_ntt = choose_ntt(T, k, E);
+  s.g1_split = choose_split(long(s.slots_max) * s.g1_tiles, H / 128);
+  s.g2_split = choose_split(long(s.slots_max) * s.g2_tiles, I / 128);
+  return s;
+}
+
+static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+WsLayout make_ws_layout(const Shape& s) {
+  WsLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + std::max<size_t>(bytes, 1));
+    return at;
+  };
+  const size_t T = size_t(s.T), R = size_t(s.rows_cap);
+  L.counts = take(4 * size_t(s.E + 1));
+  L.offsets = take(4 * size_t(s.E + 2));
+  L.expand_idx = take(4 * T * s.k);
+  L.row_token = take(4 * R);
+  L.xq = take(T * s.H);
+  L.xs = take(4 * T * (s.H / s.G));
+  L.hq = take(R * s.I);
+  L.hs = take(4 * R * (s.I / s.G));
+  L.y = take(4 * R * s.H);
+  L.part1 = take(s.g1_split > 1 ? 4 * size_t(s.g1_split) * R * 2 * s.I : 0);
+  L.part2 = take(s.g2_split > 1 ? 4 * size_t(s.g2_split) * R * s.H : 0);
+  // the two counter arrays are adjacent so one clear covers both
+  L.cnt1 = o;
+  L.cnt2 = L.cnt1 + 4 * size_t(s.E + 1) * s.g1_tiles;
+  o = align256(L.cnt2 + 4 * size_t(s.E + 1) * s.g2_tiles);
+  L.total = o;
+  return L;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int check_cfg(const moe_cfg* c) {
+  if (!c) return MOE_ERR_NULL_ARG;
+  if (c->T < 0 || c->H < 1 || c->I < 1 || c->E < 1 || c->topk < 1 || c->topk > c->E) return MOE_ERR_BAD_SHAPE;
+  if (c->topk > 32 || c->E > 1024) return MOE_ERR_BAD_SHAPE;
+  if (c->H % 128 || c->I % 128) return MOE_ERR_BAD_SHAPE;
+  if (int64_t(c->T) * c->topk >= (int64_t(1) << 24)) return MOE_ERR_BAD_SHAPE;
+  if (c->has_shared != 0 && c->has_shared != 1) return MOE_ERR_BAD_SHAPE;
+  if (c->wfmt == MOE_WFMT_FP8_BLOCK) {
+    if (c->wblk != 32 && c->wblk != 128) return MOE_ERR_UNSUPPORTED;
+    if (c->act_group != c->wblk) return MOE_ERR_BAD_SHAPE;
+  } else if (c->wfmt == MOE_WFMT_MXFP4) {
+    if (c->wblk != 32) return MOE_ERR_BAD_SHAPE;
+    if (c->act_group != 128) return MOE_ERR_UNSUPPORTED;
+  } else {
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+Shape shape_of(const moe_cfg* c) {
+  return make_shape(c->T, c->H, c->I, c->E, c->topk, c->wfmt, c->wblk, c->act_group, c->has_shared);
+}
+
+// Weight pointers: all four routed tensors, plus the shared four when used.
+int check_weights(const moe_cfg* c, const moe_weights* w) {
+  if (!w || !w->w1 || !w->w1s || !w->w2 || !w->w2s) return MOE_ERR_NULL_ARG;
+  if (c->has_shared && (!w->sw1 || !w->sw1s || !w->sw2 || !w->sw2s)) return MOE_ERR_NULL_ARG;
+  const void* ps[8] = {w->w1, w->w1s, w->w2, w->w2s, w->sw1, w->sw1s, w->sw2, w->sw2s};
+  for (int i = 0; i < (c->has_shared ? 8 : 4); ++i)
+    if (misaligned(ps[i])) return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+// Required pointers: NULL is accepted only for buffers of zero bytes (T == 0).
+int check_ptrs(std::initializer_list<std::pair<const void*, bool>> ps) {
+  for (auto& pr : ps)
+    if (pr.second && !pr.first) return MOE_ERR_NULL_ARG;
+  for (auto& pr : ps)
+    if (pr.first && misaligned(pr.first)) return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_workspace_size(const moe_cfg* cfg, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL_ARG;
+  const int rc = check_cfg(cfg);
+  if (rc) return rc;
+  *bytes = make_ws_layout(shape_of(cfg)).total;
+  return MOE_OK;
+}
+
+int moe_permute(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, int32_t* counts,
+                int32_t* offsets, int32_t* expand_idx, int32_t* row_token, uint8_t* xq, float* xs, void* ws,
+                size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  const bool has_rows = cfg->T > 0;
+  rc = check_ptrs({{x, has_rows}, {topk_ids, has_rows}, {counts, true}, {offsets, true},
+                   {expand_idx, has_rows}, {row_token, has_rows}, {xq, has_rows}, {xs, has_rows}});
+  if (rc) return rc;
+  const Shape s = shape_of(cfg);
+  return hip_status(launch_route_quant(s, x, topk_ids, counts, offsets, expand_idx, row_token, xq, xs, nullptr,
+                                       0, static_cast<hipStream_t>(stream)));
+}
+
+int moe_grouped_gemm1_swiglu(const moe_cfg* cfg, const uint8_t* xq, const float* xs, const int32_t* row_token,
+                             const int32_t* offsets, const moe_weights* w, uint8_t* hq, float* hs, void* ws,
+                             size_t ws_bytes, void* stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  const bool has_rows = cfg->T > 0;
+  rc = check_ptrs({{xq, has_rows}, {xs, has_rows}, {row_token, has_rows}, {offsets, true}, {hq, has_rows},
+                   {hs, has_rows}, {ws, true}});
+  if (rc) return rc;
+  if ((rc = check_weights(cfg, w))) return rc;
+  const Shape s = shape_of(cfg);
+  const WsLayout L = make_ws_layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!has_rows) return MOE_OK;
+  char* base = static_cast<char*>(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* cnt = reinterpret_cast<int32_t*>(base + L.cnt1);
+  if (s.g1_split > 1) {
+    if ((rc = hip_status(launch_clear(cnt, (s.E + 1) * s.g1_tiles, st)))) return rc;
+  }
+  return hip_status(launch_gemm1(s, xq, xs, row_token, offsets,
+                                 WeightPtrs{static_cast<const uint8_t*>(w->w1), w->w1s,
+                                            static_cast<const uint8_t*>(w->sw1), w->sw1s},
+                                 hq, hs, reinterpret_cast<float*>(base + L.part1), cnt, st));
+}
+
+int moe_grouped_gemm2(const moe_cfg* cfg, const uint8_t* hq, const float* hs, const int32_t* offsets,
+                      const moe_weights* w, float* y, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  const bool has_rows = cfg->T > 0;
+  rc = check_ptrs({{hq, has_rows}, {hs, has_rows}, {offsets, true}, {y, has_rows}, {ws, true}});
+  if (rc) return rc;
+  if ((rc = check_weights(cfg, w))) return rc;
+  const Shape s = shape_of(cfg);
+  const WsLayout L = make_ws_layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!has_rows) return MOE_OK;
+  char* base = static_cast<char*>(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* cnt = reinterpret_cast<int32_t*>(base + L.cnt2);
+  if (s.g2_split > 1) {
+    if ((rc = hip_status(launch_clear(cnt, (s.E + 1) * s.g2_tiles, st)))) return rc;
+  }
+  return hip_status(launch_gemm2(s, hq, hs, offsets,
+                                 WeightPtrs{static_cast<const uint8_t*>(w->w2), w->w2s,
+                                            static_cast<const uint8_t*>(w->sw2), w->sw2s},
+                                 y, reinterpret_cast<float*>(base + L.part2), cnt, st));
+}
+
+int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* expand_idx, const int32_t* offsets,
+                const float* topk_weights, uint16_t* out, void* stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  const bool has_rows = cfg->T > 0;
+  rc = check_ptrs({{y, has_rows}, {expand_idx, has_rows}, {offsets, true}, {topk_weights, has_rows},
+                   {out, has_rows}});
+  if (rc) return rc;
+  const Shape s = shape_of(cfg);
+  return hip_status(launch_combine(s, y, expand_idx, offsets, topk_weights, out, static_cast<hipStream_t>(stream)));
+}
+
+int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+              const moe_weights* w, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  const bool has_rows = cfg->T > 0;
+  rc = check_ptrs({{x, has_rows}, {topk_ids, has_rows}, {topk_weights, has_rows}, {out, has_rows}, {ws, true}});
+  if (rc) return rc;
+  if ((rc = check_weights(cfg, w))) return rc;
+  const Shape s = shape_of(cfg);
+  const WsLayout L = make_ws_layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  char* b = static_cast<char*>(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* counts = reinterpret_cast<int32_t*>(b + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  int32_t* eidx = reinterpret_cast<int32_t*>(b + L.expand_idx);
+  int32_t* rtok = reinterpret_cast<int32_t*>(b + L.row_token);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(b + L.xq);
+  float* xs = reinterpret_cast<float*>(b + L.xs);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(b + L.hq);
+  float* hs = reinterpret_cast<float*>(b + L.hs);
+  float* y = reinterpret_cast<float*>(b + L.y);
+  int32_t* cnt1 = reinterpret_cast<int32_t*>(b + L.cnt1);
+  int32_t* cnt2 = reinterpret_cast<int32_t*>(b + L.cnt2);
+  const int nclear = int((L.total - L.cnt1) / 4);
+  if ((rc = hip_status(launch_route_quant(s, x, topk_ids, counts, offsets, eidx, rtok, xq, xs, cnt1, nclear, st))))
+    return rc;
+  if (!has_rows) return MOE_OK;
+  if ((rc = hip_status(launch_gemm1(s, xq, xs, rtok, offsets,
+                                    WeightPtrs{static_cast<const uint8_t*>(w->w1), w->w1s,
+                                               static_cast<const uint8_t*>(w->sw1), w->sw1s},
+                                    hq, hs, reinterpret_cast<float*>(b + L.part1), cnt1, st))))
+    return rc;
+  if ((rc = hip_status(launch_gemm2(s, hq, hs, offsets,
+                                    WeightPtrs{static_cast<const uint8_t*>(w->w2), w->w2s,
+                                               static_cast<const uint8_t*>(w->sw2), w->sw2s},
+                                    y, reinterpret_cast<float*>(b + L.part2), cnt2, st))))
+    return rc;
+  return hip_status(launch_combine(s, y, eidx, offsets, topk_weights, out, st));
+}
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL_ARG: return "a required pointer is NULL";
+    case MOE_ERR_BAD_SHAPE: return "invalid shape";
+    case MOE_ERR_UNSUPPORTED: return "unsupported format / block / group combination";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case MOE_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

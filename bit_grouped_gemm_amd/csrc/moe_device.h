@@ -1,0 +1,114 @@
+// moe_device.h -- device-side building blocks shared by the gfx950 kernels:
+// number-format codecs, wave reductions and the scaled-MFMA operand layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ codecs
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// fp32 -> e4m3 (OCP E4M3FN) code: round to nearest, ties to even, |v| >= 448
+// saturates to 448, the sign bit is kept (values that round to zero keep
+// their sign).  Integer formulation: subnormal codes are multiples of 2^-9
+// (rint of v * 2^9, whose result 8 is the smallest normal code); normal
+// codes keep the top three mantissa bits with the 20 dropped bits rounded
+// to nearest-even, a carry stepping into the exponent field.
+__device__ __forceinline__ uint32_t enc_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  const float af = __uint_as_float(a);
+  uint32_t code;
+  if (!(af < 448.0f)) {
+    code = 0x7Eu;
+  } else if (af < 0x1p-6f) {
+    code = uint32_t(__builtin_rintf(af * 512.0f));
+  } else {
+    code = ((((a >> 23) - 127u + 7u) << 3) | ((a >> 20) & 7u));
+    const uint32_t rem = a & 0xFFFFFu;
+    code += (rem > 0x80000u) | ((rem == 0x80000u) & (code & 1u));
+  }
+  return code | sign;
+}
+
+// Quantisation multiplier and dequant scale of a group with absolute max a.
+__device__ __forceinline__ float quant_mult(float amax) { return 448.0f / fmaxf(amax, 0x1p-64f); }
+
+// ------------------------------------------------------------------ waves
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+
+// ------------------------------------------------------------------ MFMA
+// v_mfma_scale_f32_16x16x128_f8f6f4, layout measured on gfx950:
+//   operand lane l: row (A) / column (B) = l % 16, lane group g = l / 16.
+//   e4m3 operand: bytes 0..15 hold K = 16g + j, bytes 16..31 hold
+//     K = 64 + 16g + (j - 16).  For a K-contiguous row in memory the lane
+//     loads 16 bytes at offset 16g and 16 bytes at offset 64 + 16g.
+//   e2m1 operand (first four registers): nibble j (low nibble first) holds
+//     K = 32g + j, i.e. 16 bytes at offset 16g of a packed row.
+//   e8m0 scale operand: lane b*16 + m holds the scale of row/column m for
+//     K block b (K = 32b .. 32b+31), byte 0 of the register.
+//   result: lane l holds column l % 16, rows 4g .. 4g+3.
+template <int FA, int FB>
+__device__ __forceinline__ v4f mfma_scaled(const v8i& a, const v8i& b, int sa, int sb) {
+  v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, FA, FB, 0, sa, 0, sb);
+}
+
+constexpr int kFmtE4M3 = 0;
+constexpr int kFmtE2M1 = 4;
+constexpr int kUnitScale = 127;  // e8m0 code of 1.0
+
+__device__ __forceinline__ v4u ldg16(const uint8_t* p) { return *reinterpret_cast<const v4u*>(p); }
+
+// Load one 16-row x 128-K e4m3 operand fragment for this lane from a
+// K-contiguous row (row already selected by the caller).
+__device__ __forceinline__ v8i load_e4m3_frag(const uint8_t* row_k0, int g) {
+  const v4u lo = ldg16(row_k0 + 16 * g);
+  const v4u hi = ldg16(row_k0 + 64 + 16 * g);
+  v8i r;
+  r[0] = int(lo[0]); r[1] = int(lo[1]); r[2] = int(lo[2]); r[3] = int(lo[3]);
+  r[4] = int(hi[0]); r[5] = int(hi[1]); r[6] = int(hi[2]); r[7] = int(hi[3]);
+  return r;
+}
+
+// e2m1 fragment: 16 bytes (32 nibbles) at offset 16g of the packed row's
+// 64-byte K step.
+__device__ __forceinline__ v8i load_e2m1_frag(const uint8_t* row_k0, int g) {
+  const v4u lo = ldg16(row_k0 + 16 * g);
+  v8i r;
+  r[0] = int(lo[0]); r[1] = int(lo[1]); r[2] = int(lo[2]); r[3] = int(lo[3]);
+  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  return r;
+}
+
+// Keep only the bytes of 32-wide K block `blk` in an e4m3 fragment (used
+// when the weight scales change every 32 along K): block blk lives in lane
+// groups with (g >> 1) == (blk & 1), in byte half (blk >> 1).
+__device__ __forceinline__ v8i mask_e4m3_block(const v8i& a, int g, int blk) {
+  v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
+  if ((g >> 1) == (blk & 1)) {
+    if (blk >> 1) { r[4] = a[4]; r[5] = a[5]; r[6] = a[6]; r[7] = a[7]; }
+    else { r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3]; }
+  }
+  return r;
+}
+
+}  // namespace moe

@@ -1,0 +1,62 @@
+// moe_launch.h -- internal interface between the C-ABI layer (moe_api.hip)
+// and the kernels (moe_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Shape facts derived once on the host from a validated moe_cfg.
+struct Shape {
+  int T, H, I, E, k, wfmt, wblk, G, shared;
+  int ngroups;      // E + shared
+  int rows_cap;     // T*k + T*shared: upper bound on permuted rows
+  int slots_max;    // upper bound on non-empty groups: min(E, T*k) + shared
+  // GEMM1: unit = 128 h-columns (128 gate + 128 up weight rows) of one group
+  int g1_tiles;     // I / 128
+  int g1_split;     // K splits over H/128 steps
+  int g1_ntt;       // 16-token tiles per pass (1, 2 or 4)
+  // GEMM2: unit = 128 output rows of one group
+  int g2_tiles;     // H / 128
+  int g2_split;     // K splits over I/128 steps
+  int g2_ntt;
+};
+
+// Workspace carve (byte offsets from the caller's ws base; 256-aligned).
+struct WsLayout {
+  size_t counts, offsets, expand_idx, row_token;  // layer-internal permute outputs
+  size_t xq, xs, hq, hs, y;                       // layer-internal activations
+  size_t part1, part2;                            // split-K partial sums (fp32)
+  size_t cnt1, cnt2;                              // split-K arrival counters (int32)
+  size_t total;
+};
+
+Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, int shared);
+WsLayout make_ws_layout(const Shape& s);
+
+struct WeightPtrs {
+  const uint8_t* w;   // routed [E][N][Kbytes]
+  const void* ws;     // routed scales
+  const uint8_t* sw;  // shared expert (or null)
+  const void* sws;
+};
+
+hipError_t launch_route_quant(const Shape& s, const uint16_t* x, const int32_t* ids, int32_t* counts,
+                              int32_t* offsets, int32_t* expand_idx, int32_t* row_token, uint8_t* xq,
+                              float* xs, int32_t* clear, int nclear, hipStream_t st);
+
+hipError_t launch_clear(int32_t* p, int n, hipStream_t st);
+
+hipError_t launch_gemm1(const Shape& s, const uint8_t* xq, const float* xs, const int32_t* row_token,
+                        const int32_t* offsets, WeightPtrs w1, uint8_t* hq, float* hs, float* part,
+                        int32_t* cnt, hipStream_t st);
+
+hipError_t launch_gemm2(const Shape& s, const uint8_t* hq, const float* hs, const int32_t* offsets,
+                        WeightPtrs w2, float* y, float* part, int32_t* cnt, hipStream_t st);
+
+hipError_t launch_combine(const Shape& s, const float* y, const int32_t* expand_idx, const int32_t* offsets,
+                          const float* topk_w, uint16_t* out, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,163 @@
+/* moe.h -- C ABI of the MI355X (gfx950) low-bit MoE expert layer.
+ *
+ * One GPU's share of a mixture-of-experts FFN layer, for decode (1-256
+ * tokens) and prefill: top-k routing result -> local token permute ->
+ * per-token FP8 activation quantisation -> grouped GEMM1 (gate|up) over FP8
+ * e4m3 or MXFP4 block-scaled expert weights with fused SwiGLU and
+ * requantisation -> grouped GEMM2 -> top-k weighted combine back to token
+ * order.  This is the local compute of the FP8/FP4 MoE operator in the
+ * GC-MoE abstract ("grouped GEMMs, and a combine step"; "fused SwiGLU,
+ * requantization, and optional shared experts") and the GMM1 -> SwiGLU ->
+ * GMM2 -> combine chain of the FusedDeepMoE family analysis (unified
+ * execution flow figure); the cross-GPU dispatch / all-to-all is not part
+ * of it.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns
+ *     every buffer; the library never allocates, frees or synchronises.
+ *     Scratch comes from the caller's workspace `ws` of `ws_bytes` bytes
+ *     (size from moe_workspace_size; the workspace may hold any bytes on
+ *     entry).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work; results are ready when the stream is.
+ *     Calls on different streams need distinct workspaces.
+ *   - Outputs are fully overwritten; nothing accumulates into caller memory.
+ *   - Return value: MOE_OK or an error code below.  Every error except
+ *     MOE_ERR_HIP is detected on the host before anything is enqueued.
+ *     Device faults surface at the caller's next synchronisation.
+ *   - Pointers must be 16-byte aligned (MOE_ERR_MISALIGNED otherwise).
+ *
+ * Number formats
+ *   e4m3 = OCP FP8 E4M3FN (bias 7, max 448, no infinities); e2m1 = OCP FP4
+ *   (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6); e8m0 = 2^(c-127).  bf16 values
+ *   are uint16 bit patterns.
+ *
+ * Activation quantisation rule (per token, per group of G = act_group
+ * consecutive channels; the FusedDeepMoE analysis's QuantToken / BlockQuant
+ * with 448 in place of 127): a = max |x| in fp32, m = 448 / max(a, 2^-64)
+ * (fp32, correctly rounded), code = e4m3(x * m) round-to-nearest-even with
+ * saturation and the sign kept, scale = 1 / m (fp32).  Value = dec(code) *
+ * scale.  The same rule requantises the SwiGLU output per row.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL_ARG = 1,    /* a required pointer is NULL */
+  MOE_ERR_BAD_SHAPE = 2,   /* T < 0; H, I, E or topk < 1; topk > E; sizes not multiples of the blocks */
+  MOE_ERR_UNSUPPORTED = 3, /* a format / block / group combination that is not built */
+  MOE_ERR_WORKSPACE = 4,   /* ws_bytes smaller than moe_workspace_size() */
+  MOE_ERR_MISALIGNED = 5,  /* a pointer is not 16-byte aligned */
+  MOE_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+};
+
+enum { MOE_WFMT_FP8_BLOCK = 0, MOE_WFMT_MXFP4 = 1 };
+
+/* Layer shape (host struct).
+ *   T tokens on this GPU, H hidden size, I expert FFN width, E local experts,
+ *   topk slots per token.
+ *   wfmt = MOE_WFMT_FP8_BLOCK: e4m3 weights, one fp32 scale per
+ *          wblk x wblk block (wblk 32 or 128), act_group must equal wblk.
+ *   wfmt = MOE_WFMT_MXFP4: e2m1 weights packed two per byte (even K index in
+ *          the low nibble) with one e8m0 scale per 32 along K (wblk = 32);
+ *          act_group must be 128.
+ *   has_shared = 1 adds one always-on shared expert (same format and I) to
+ *   every token with weight 1 (GC-MoE abstract, "optional shared experts";
+ *   FusedDeepMoE shared-expert path: all tokens in one group).
+ * Limits: 1 <= E <= 1024, topk <= 32, H and I multiples of 128,
+ *   T * topk < 2^24. */
+typedef struct moe_cfg {
+  int32_t T, H, I, E, topk;
+  int32_t wfmt;
+  int32_t wblk;
+  int32_t act_group;
+  int32_t has_shared;
+} moe_cfg;
+
+/* Expert weights in canonical row-major layout (host struct of device
+ * pointers).  FP8:   w1 uint8 [E][2I][H] (rows 0..I-1 gate, I..2I-1 up, K
+ * contiguous), w1s float [E][2I/wblk][H/wblk]; w2 uint8 [E][H][I], w2s float
+ * [E][H/wblk][I/wblk].  MXFP4: w1 uint8 [E][2I][H/2], w1s uint8 [E][2I][H/32];
+ * w2 uint8 [E][H][I/2], w2s uint8 [E][H][I/32].  sw1..sw2s: the shared
+ * expert with a leading dimension of 1 (may be NULL when has_shared == 0). */
+typedef struct moe_weights {
+  const void *w1, *w1s, *w2, *w2s;
+  const void *sw1, *sw1s, *sw2, *sw2s;
+} moe_weights;
+
+/* Bytes of workspace moe_layer and the stage calls need for this shape
+ * (host only; no device work).  *bytes is written on MOE_OK. */
+int moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
+
+/* Steps 1-4: expert histogram, exclusive prefix-scan offsets (the group
+ * list), stable expand index, and per-token FP8 activation quantisation
+ * (FusedDeepMoE analysis: CalAndSendTokenCount, gmGroupList, gmExpandIdx and
+ * QuantToken).
+ *   x          bf16 [T][H]
+ *   topk_ids   int32 [T][topk]; ids outside [0, E) are masked slots (not
+ *              counted, expand_idx = -1, no contribution)
+ *   counts     int32 [E + has_shared] rows per expert (counts[E] = T for the
+ *              shared expert)
+ *   offsets    int32 [E + 1 + has_shared] exclusive scan of counts
+ *   expand_idx int32 [T*topk]: row of slot i = t*topk + j; rows of one
+ *              expert hold its slots in ascending i (stable)
+ *   row_token  int32 [T*topk + T*has_shared]: token of each row, -1 after
+ *              the last row; shared rows are offsets[E] + t
+ *   xq, xs     e4m3 codes uint8 [T][H] and fp32 scales [T][H/act_group]
+ * ws / ws_bytes are unused (may be NULL / 0). */
+int moe_permute(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, int32_t* counts,
+                int32_t* offsets, int32_t* expand_idx, int32_t* row_token, uint8_t* xq, float* xs,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Step 5 (+ shared rows): for every row r of group e (e = E is the shared
+ * expert), G[r][n] = sum_k xq_deq[row_token[r]][k] * w1_deq[e][n][k] for
+ * n < 2I with fp32 accumulation, h = silu(G[:, :I]) * G[:, I:], then h
+ * requantised per row and act_group with the activation rule (FusedDeepMoE
+ * analysis: GmmDeqSwigluQuant, OpDequant, OpSwiglu, OpBlockQuant).
+ *   xq, xs      as produced by moe_permute
+ *   row_token   int32 [rows]; offsets int32 [E + 1 + has_shared]
+ *   hq, hs      outputs: uint8 [rows][I] and fp32 [rows][I/act_group],
+ *               rows = offsets[E + has_shared] (rows past that untouched) */
+int moe_grouped_gemm1_swiglu(const moe_cfg* cfg, const uint8_t* xq, const float* xs,
+                             const int32_t* row_token, const int32_t* offsets, const moe_weights* w,
+                             uint8_t* hq, float* hs, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 6: y[r][n] = sum_k hq_deq[r][k] * w2_deq[e][n][k], n < H, fp32
+ * accumulation (FusedDeepMoE analysis: GmmDeq).
+ *   hq, hs   uint8 [rows][I], fp32 [rows][I/act_group]
+ *   offsets  int32 [E + 1 + has_shared]
+ *   y        fp32 [rows][H] output */
+int moe_grouped_gemm2(const moe_cfg* cfg, const uint8_t* hq, const float* hs, const int32_t* offsets,
+                      const moe_weights* w, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 8: out[t][:] = sum over j ascending of valid slots
+ * topk_weights[t][j] * y[expand_idx[t*topk + j]][:] (+ y[offsets[E] + t][:]
+ * with weight 1 when has_shared), fp32 accumulation, bf16 round-to-nearest-
+ * even (FusedDeepMoE analysis: ReducePermute; GC-MoE abstract's combine).
+ *   y fp32 [rows][H]; expand_idx int32 [T*topk]; offsets int32 [E+1+has_shared];
+ *   topk_weights fp32 [T][topk]; out bf16 [T][H] */
+int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* expand_idx, const int32_t* offsets,
+                const float* topk_weights, uint16_t* out, void* stream);
+
+/* Steps 1-8 in one call (internally fused where it pays):
+ *   x bf16 [T][H], topk_ids int32 [T][topk], topk_weights fp32 [T][topk],
+ *   out bf16 [T][H]; ws of at least moe_workspace_size(cfg) bytes. */
+int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+              const moe_weights* w, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Static description of an error code (host only). */
+const char* moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

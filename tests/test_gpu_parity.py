@@ -1,0 +1,398 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Every call goes through the C ABI (bit_grouped_gemm_amd -> libmoe.so).
+Index outputs and activation codes must be bit-exact; the layer output
+must satisfy |gpu - ref| <= 1e-2 * max|ref| + 1e-3 with ref the oracle's
+fp64 result.  Requantised SwiGLU codes cannot be bit-exact (fp32
+accumulation order moves h by ulps), so they are checked for agreement and
+for being at most one code step away from the oracle's.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_grouped_gemm_amd as moe
+    moe.load()
+    oracle.build(force=False)
+    yield
+
+
+def M():
+    import bit_grouped_gemm_amd as moe
+    return moe
+
+
+# ------------------------------------------------------------------ cases
+def reduced(name, **kw):
+    return synth.WORKLOADS[name].with_shape(**kw)
+
+
+REDUCED = {
+    # several 128-tiles and a ragged token count in every case
+    "tiny_fp8": synth.WORKLOADS["tiny_fp8"],
+    "fp8_b128": reduced("decode_fp8", H=512, I=384, E=16, topk=4),
+    "fp8_b32": reduced("tiny_fp8", H=384, I=256, E=6, topk=3),
+    "mxfp4": reduced("decode_mxfp4", H=512, I=384, E=16, topk=4),
+    "fp8_zipf_shared": reduced("decode_fp8_zipf_shared", H=512, I=256, E=32, topk=8),
+    "mxfp4_shared": reduced("decode_mxfp4", H=384, I=256, E=12, topk=2, shared=True),
+}
+
+_WCACHE = {}
+
+
+def weights_for(wl, seed=0):
+    key = (wl, seed)
+    if key not in _WCACHE:
+        if len(_WCACHE) > 3:
+            _WCACHE.clear()
+            torch.cuda.empty_cache()
+        w = synth.gen_weights(wl, seed=seed, device=DEV)
+        _WCACHE[key] = (w, w.to("cpu"))
+    return _WCACHE[key]
+
+
+def inputs_for(wl, T, seed=0):
+    x, ids, tw = synth.gen_inputs(wl, T, seed=seed, device=DEV)
+    return x, ids, tw
+
+
+def tol_check(got, ref, what):
+    err = np.abs(got - ref).max() if got.size else 0.0
+    bound = 1e-2 * (np.abs(ref).max() if ref.size else 0.0) + 1e-3
+    _note(f"  {what}: max|gpu-ref| = {err:.3e}  bound {bound:.3e}")
+    assert err <= bound, f"{what}: {err} > {bound}"
+    return err
+
+
+def run_permute(wl, T, x, ids):
+    moe = M()
+    cfg = moe.Cfg.for_workload(wl, T)
+    outs = moe.moe_permute(cfg, x, ids)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in outs]
+
+
+# ------------------------------------------------------------------ permute + quant
+PERMUTE_CASES = [
+    ("tiny_fp8", 16), ("decode_fp8", 1), ("decode_fp8", 8), ("decode_fp8", 256),
+    ("decode_fp8_zipf_shared", 256), ("prefill_mxfp4", 4096), ("fp8_b32", 37), ("mxfp4_shared", 5),
+]
+
+
+@pytest.mark.parametrize("name,T", PERMUTE_CASES)
+def test_permute_and_quant_bitexact(name, T):
+    wl = synth.WORKLOADS.get(name) or REDUCED[name]
+    _note(f"permute {name} T={T}")
+    x, ids, _ = inputs_for(wl, T, seed=1)
+    counts, offsets, eidx, rtok, xq, xs = run_permute(wl, T, x, ids)
+    rc, ro, re_, rr = oracle.permute(ids.cpu(), wl.E, wl.shared)
+    assert np.array_equal(counts, rc) and np.array_equal(offsets, ro)
+    assert np.array_equal(eidx, re_) and np.array_equal(rtok, rr)
+    qx, qs = oracle.quant_act(x.cpu(), wl.act_group)
+    assert np.array_equal(xq, qx)
+    assert np.array_equal(xs.view(np.uint32), qs.view(np.uint32))
+
+
+def test_permute_masked_duplicate_and_odd_expert_counts():
+    moe = M()
+    rng = np.random.default_rng(3)
+    for E, k, T in ((5, 3, 300), (64, 8, 1000), (1000, 4, 700), (1, 1, 129)):
+        ids = rng.integers(0, E, size=(T, k)).astype(np.int32)     # duplicates allowed
+        ids[rng.random((T, k)) < 0.15] = -1
+        ids[0, 0] = E + 7
+        for shared in (0, 1):
+            cfg = moe.Cfg(T, 128, 128, E, k, 0, 128, 128, shared)
+            x = torch.randn(T, 128, device=DEV).to(torch.bfloat16)
+            out = moe.moe_permute(cfg, x, torch.from_numpy(ids).to(DEV))
+            torch.cuda.synchronize()
+            ref = oracle.permute(ids, E, bool(shared))
+            for a, b in zip(out[:4], ref):
+                assert np.array_equal(a.cpu().numpy(), b), (E, k, T, shared)
+
+
+def test_quant_special_values_bitexact():
+    moe = M()
+    T, H = 64, 256
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(T, H, generator=g)
+    x[0] = 0.0
+    x[1, :128] = 1e-38
+    x[2, 5] = -0.0
+    x[3] *= 1e30
+    x[4] = torch.tensor(448.0)
+    x[5, :] = torch.arange(H) * 2.0 ** -12
+    x[6, ::2] = -x[6, 1::2]
+    # every bf16 bit pattern that is finite, paired with a large group maximum
+    allb = torch.arange(0, 65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).float()
+    allb = allb[torch.isfinite(allb)]
+    xb = x.to(torch.bfloat16)
+    for G in (32, 128):
+        cfg = moe.Cfg(T, H, 128, 4, 1, 0, G, G, 0)
+        ids = torch.zeros(T, 1, dtype=torch.int32, device=DEV)
+        got = moe.moe_permute(cfg, xb.to(DEV), ids)
+        torch.cuda.synchronize()
+        qx, qs = oracle.quant_act(xb, G)
+        assert np.array_equal(got[4].cpu().numpy(), qx)
+        assert np.array_equal(got[5].cpu().numpy().view(np.uint32), qs.view(np.uint32))
+    n = allb.numel()
+    Hb = 128
+    rows = (n + Hb - 1) // Hb
+    flat = torch.zeros(rows * Hb)
+    flat[:n] = allb
+    xb2 = flat.reshape(rows, Hb).to(torch.bfloat16)
+    cfg = moe.Cfg(rows, Hb, 128, 4, 1, 0, 128, 128, 0)
+    got = moe.moe_permute(cfg, xb2.to(DEV), torch.zeros(rows, 1, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    qx, qs = oracle.quant_act(xb2, 128)
+    assert np.array_equal(got[4].cpu().numpy(), qx)
+    assert np.array_equal(got[5].cpu().numpy().view(np.uint32), qs.view(np.uint32))
+
+
+def test_permute_T0():
+    moe = M()
+    wl = REDUCED["fp8_zipf_shared"]
+    cfg = moe.Cfg.for_workload(wl, 0)
+    x = torch.empty(0, wl.H, dtype=torch.bfloat16, device=DEV)
+    ids = torch.empty(0, wl.topk, dtype=torch.int32, device=DEV)
+    counts, offsets, *_ = moe.moe_permute(cfg, x, ids)
+    torch.cuda.synchronize()
+    assert counts.abs().sum().item() == 0 and offsets.abs().sum().item() == 0
+
+
+# ------------------------------------------------------------------ stages
+def dec_e4m3_np(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_gemm1_stage(name):
+    moe = M()
+    wl = REDUCED[name]
+    T = 37 if name != "tiny_fp8" else 16
+    _note(f"gemm1 {name} T={T}")
+    w, wc = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=2)
+    cfg = moe.Cfg.for_workload(wl, T)
+    counts, offsets, eidx, rtok, xq, xs = moe.moe_permute(cfg, x, ids)
+    ws = moe.workspace(cfg)
+    hq, hs = moe.moe_grouped_gemm1_swiglu(cfg, xq, xs, rtok, offsets, w, ws)
+    torch.cuda.synchronize()
+    R = int(offsets[-1].item())
+    lay = oracle.layer_for(wl, T, wc)
+    h_ref, hq_ref, hs_ref = lay.gemm1(xq.cpu(), xs.cpu(), rtok.cpu(), offsets.cpu(), range(R))
+    hq_g, hs_g = hq.cpu().numpy()[:R], hs.cpu().numpy()[:R]
+    # group maxima move with the fp32 / MFMA accumulation order, so the scales agree closely
+    # but not bitwise
+    rel = np.abs(hs_g - hs_ref) / np.abs(hs_ref)
+    _note(f"  max rel scale difference {rel.max():.3e}")
+    assert rel.max() <= 1e-3, rel.max()
+    agree = (hq_g == hq_ref).mean()
+    _note(f"  h code agreement {agree:.5f}")
+    assert agree >= 0.99
+    G = wl.act_group
+    dg = dec_e4m3_np(hq_g) * np.repeat(hs_g, G, axis=1)
+    dr = dec_e4m3_np(hq_ref) * np.repeat(hs_ref, G, axis=1)
+    # a differing code is a neighbour: within one e4m3 step (1/8 relative, or 2^-9 * scale)
+    # a differing code is a neighbour (one e4m3 step: 1/8 relative, 2^-9 of the scale when
+    # subnormal), up to fp32 accumulation noise measured against the group's full scale 448*hs
+    scale = np.repeat(hs_ref, G, axis=1)
+    step = np.maximum(np.abs(dr) / 8, 2.0 ** -9 * scale) + 1e-4 * 448 * scale
+    bad = np.argwhere(np.abs(dg - dr) > step * 1.0001)
+    for r, c in bad[:8]:
+        _note(f"  row {r} col {c}: gpu code {hq_g[r, c]:#x} ({dg[r, c]:.6g}) oracle {hq_ref[r, c]:#x} "
+              f"({dr[r, c]:.6g}) h {h_ref[r, c]:.6g} scale g/o {hs_g[r, c // G]:.6g}/{hs_ref[r, c // G]:.6g}")
+    assert len(bad) == 0
+    # and every dequantised GPU value is within one code step of the oracle's unquantised h
+    assert np.all(np.abs(dg - h_ref) <= step * 1.0001 + 1e-30)
+    _note(f"  max |gpu deq h - oracle h| / group scale = {(np.abs(dg - h_ref) / (448 * scale)).max():.3e}")
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_gemm2_stage(name):
+    moe = M()
+    wl = REDUCED[name]
+    T = 29
+    _note(f"gemm2 {name} T={T}")
+    w, wc = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=3)
+    cfg = moe.Cfg.for_workload(wl, T)
+    counts, offsets, eidx, rtok, xq, xs = moe.moe_permute(cfg, x, ids)
+    torch.cuda.synchronize()
+    R = int(offsets[-1].item())
+    lay = oracle.layer_for(wl, T, wc)
+    _, hq_r, hs_r = lay.gemm1(xq.cpu(), xs.cpu(), rtok.cpu(), offsets.cpu(), range(R))
+    hq = torch.zeros(rtok.numel(), wl.I, dtype=torch.uint8)
+    hs = torch.ones(rtok.numel(), wl.I // wl.act_group)
+    hq[:R] = torch.from_numpy(hq_r)
+    hs[:R] = torch.from_numpy(hs_r)
+    y = moe.moe_grouped_gemm2(cfg, hq.to(DEV), hs.to(DEV), offsets, w)
+    torch.cuda.synchronize()
+    y_ref = lay.gemm2(hq, hs, offsets.cpu(), range(R))
+    # identical codes on both sides: the only difference is accumulation (fp8 products summed
+    # inside the MFMA per 128-K block, then fp32 across blocks) against the oracle's fp64
+    err = np.abs(y.cpu().numpy()[:R] - y_ref).max()
+    _note(f"  gemm2 max|gpu-ref| / max|ref| = {err / np.abs(y_ref).max():.3e}")
+    assert err <= 3e-4 * np.abs(y_ref).max(), err
+
+
+def test_combine_stage():
+    moe = M()
+    wl = REDUCED["fp8_zipf_shared"]
+    T = 41
+    x, ids, tw = inputs_for(wl, T, seed=4)
+    ids_c = ids.clone()
+    ids_c[3, 2] = -1
+    cfg = moe.Cfg.for_workload(wl, T)
+    counts, offsets, eidx, rtok, xq, xs = moe.moe_permute(cfg, x, ids_c)
+    y = torch.randn(rtok.numel(), wl.H, device=DEV)
+    out = moe.moe_combine(cfg, y, eidx, offsets, tw)
+    torch.cuda.synchronize()
+    lay = oracle.layer_for(wl, T, weights_for(wl)[1])
+    ref = lay.combine(y.cpu(), eidx.cpu(), offsets.cpu(), tw.cpu())
+    got = out.float().cpu().numpy()
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+
+# ------------------------------------------------------------------ whole layer
+@pytest.mark.parametrize("name", list(REDUCED))
+@pytest.mark.parametrize("T", [1, 3, 37])
+def test_layer_reduced(name, T):
+    moe = M()
+    wl = REDUCED[name]
+    _note(f"layer {name} T={T}")
+    w, wc = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=6)
+    cfg = moe.Cfg.for_workload(wl, T)
+    out = moe.moe_layer(cfg, x, ids, tw, w)
+    torch.cuda.synchronize()
+    ref = oracle.layer_for(wl, T, wc).layer(x.cpu(), ids.cpu(), tw.cpu())
+    tol_check(out.float().cpu().numpy(), ref, f"{name} T={T}")
+
+
+FULL = [(n, T) for n in ("decode_fp8", "decode_mxfp4") for T in synth.WORKLOADS[n].tokens] + \
+       [("decode_fp8_zipf_shared", T) for T in synth.WORKLOADS["decode_fp8_zipf_shared"].tokens] + \
+       [("prefill_mxfp4", 4096)]
+
+
+@pytest.mark.parametrize("name,T", FULL)
+def test_layer_full_size_sampled(name, T):
+    """Full workload shapes, launched exactly as the bench launches them;
+    every index output checked bit-exact, the output on sampled tokens."""
+    moe = M()
+    wl = synth.WORKLOADS[name]
+    _note(f"full {name} T={T}")
+    w, wc = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=0)
+    cfg = moe.Cfg.for_workload(wl, T)
+    ws = moe.workspace(cfg)
+    out = moe.moe_layer(cfg, x, ids, tw, w, ws=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(T)
+    toks = sorted(set([0, T - 1] + list(rng.choice(T, size=min(T, 10), replace=False))))
+    ref = oracle.layer_for(wl, T, wc).layer(x.cpu(), ids.cpu(), tw.cpu(), toks=toks)
+    tol_check(out.float().cpu().numpy()[toks], ref, f"{name} T={T} sampled {len(toks)}")
+    assert torch.isfinite(out.float()).all()
+
+
+# ------------------------------------------------------------------ edge cases
+def test_layer_T0_is_a_no_op():
+    moe = M()
+    wl = REDUCED["fp8_zipf_shared"]
+    w, _ = weights_for(wl)
+    cfg = moe.Cfg.for_workload(wl, 0)
+    out = moe.moe_layer(cfg, torch.empty(0, wl.H, dtype=torch.bfloat16, device=DEV),
+                        torch.empty(0, wl.topk, dtype=torch.int32, device=DEV),
+                        torch.empty(0, wl.topk, device=DEV), w)
+    torch.cuda.synchronize()
+    assert out.numel() == 0
+
+
+def test_layer_masked_slots_and_zero_weights():
+    moe = M()
+    wl = REDUCED["mxfp4"]
+    T = 20
+    w, wc = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=8)
+    ids[2, 0] = -1
+    ids[5, :] = wl.E + 1          # a token with every slot masked: output is exactly zero
+    tw[7, 1] = 0.0
+    cfg = moe.Cfg.for_workload(wl, T)
+    out = moe.moe_layer(cfg, x, ids, tw, w)
+    torch.cuda.synchronize()
+    ref = oracle.layer_for(wl, T, wc).layer(x.cpu(), ids.cpu(), tw.cpu())
+    got = out.float().cpu().numpy()
+    tol_check(got, ref, "masked")
+    assert np.all(got[5] == 0)
+
+
+def test_poisoned_workspace_and_determinism():
+    moe = M()
+    for name, T in (("fp8_zipf_shared", 37), ("mxfp4", 1), ("fp8_b128", 2)):
+        wl = REDUCED[name]
+        w, _ = weights_for(wl)
+        x, ids, tw = inputs_for(wl, T, seed=9)
+        cfg = moe.Cfg.for_workload(wl, T)
+        ws = moe.workspace(cfg)
+        ws.fill_(0xFF)
+        a = moe.moe_layer(cfg, x, ids, tw, w, ws=ws).clone()
+        ws.fill_(0x00)
+        b = moe.moe_layer(cfg, x, ids, tw, w, ws=ws).clone()
+        c = moe.moe_layer(cfg, x, ids, tw, w, ws=ws).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        assert torch.equal(b.view(torch.int16), c.view(torch.int16))
+
+
+def test_layer_matches_its_stages():
+    """moe_layer equals the four stage calls chained through the C ABI."""
+    moe = M()
+    wl = REDUCED["fp8_zipf_shared"]
+    T = 19
+    w, _ = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=10)
+    cfg = moe.Cfg.for_workload(wl, T)
+    out = moe.moe_layer(cfg, x, ids, tw, w)
+    counts, offsets, eidx, rtok, xq, xs = moe.moe_permute(cfg, x, ids)
+    ws = moe.workspace(cfg)
+    hq, hs = moe.moe_grouped_gemm1_swiglu(cfg, xq, xs, rtok, offsets, w, ws)
+    y = moe.moe_grouped_gemm2(cfg, hq, hs, offsets, w, ws)
+    out2 = moe.moe_combine(cfg, y, eidx, offsets, tw)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_worked_examples_on_gpu():
+    import test_oracle_pins as pins
+    moe = M()
+    for ex in pins.golden_examples():
+        wl, wc, x, ids, tw = pins._golden_case(ex)
+        T = x.shape[0]
+        cfg = moe.Cfg.for_workload(wl, T)
+        out = moe.moe_layer(cfg, x.to(DEV), ids.to(DEV), tw.to(DEV), wc.to(DEV))
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        for t in range(T):
+            want = np.zeros(wl.H)
+            for i, v in ex["expect_out"][str(t)]:
+                want[i] = v
+            assert np.array_equal(got[t], want), (ex["name"], t, got[t][:4])
