@@ -12,15 +12,25 @@
 
 namespace moe {
 
+#ifndef MOE_SPLIT_TARGET_WG
+#define MOE_SPLIT_TARGET_WG 256
+#endif
+#ifndef MOE_SPLIT_MIN_KSTEPS
+#define MOE_SPLIT_MIN_KSTEPS 4
+#endif
+
 static int choose_split(long units, int nks) {
-  // more workgroups than ~4 per CU buy nothing; fewer than ~2 per CU leave
-  // HBM bandwidth idle at decode, so K is split until the unit count fills
-  // the 256 CUs, keeping at least 4 K steps (512 K) per workgroup
+  // Split K (a divisor of the K-step count) only until the launch has about
+  // one workgroup per CU: small decode layers then reach every CU, while
+  // larger ones avoid the partial-sum round trip through memory, which costs
+  // more than the tail of a half-filled last round.  Each workgroup keeps at
+  // least MOE_SPLIT_MIN_KSTEPS steps of 128 K.
   int best = 1;
-  for (int d = 2; d <= nks; ++d) {
+  for (int d = 1; d <= nks; ++d) {
     if (nks % d) continue;
-    if (units * d > 1024 || nks / d < 4) break;
+    if (nks / d < MOE_SPLIT_MIN_KSTEPS) break;
     best = d;
+    if (units * d >= MOE_SPLIT_TARGET_WG) break;
   }
   return best;
 }
@@ -45,6 +55,17 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   s.g1_ntt = s.g2_ntt = choose_ntt(T, k, E);
   s.g1_split = choose_split(long(s.slots_max) * s.g1_tiles, H / 128);
   s.g2_split = choose_split(long(s.slots_max) * s.g2_tiles, I / 128);
+  // partial sums are addressed with 32-bit byte offsets: keep them under 2 GiB
+  auto fit = [&](int S, int nks, long row_floats) {
+    while (S > 1 && 4L * S * s.rows_cap * row_floats >= (1L << 31)) {
+      int d = S - 1;
+      while (d > 1 && nks % d) --d;
+      S = d;
+    }
+    return S;
+  };
+  s.g1_split = fit(s.g1_split, H / 128, 2L * I);
+  s.g2_split = fit(s.g2_split, I / 128, H);
   return s;
 }
 

@@ -24,6 +24,10 @@
 namespace moe {
 
 constexpr int kThreads = 256;  // 4 waves per workgroup everywhere
+#ifndef MOE_KSTAGES
+#define MOE_KSTAGES 2
+#endif
+constexpr int kStages = MOE_KSTAGES;  // register stages of the K loop
 
 // =====================================================================
 // route + quant
@@ -270,65 +274,105 @@ __device__ __forceinline__ void mma_frag(v4f (&acc)[NJ][NTT], const Frag<WF, NJ,
       }
     }
   } else {
+    // one token tile at a time: the NJ products land in separate registers
+    // first, so the MFMAs issue back to back, then they are scaled into acc
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+    for (int t = 0; t < NTT; ++t) {
+      v4f d[NJ];
 #pragma unroll
-      for (int t = 0; t < NTT; ++t) {
-        if (WF == 0) {
-          const v4f d = mfma_scaled<kFmtE4M3, kFmtE4M3>(f.a[j], f.b[t], kUnitScale, kUnitScale);
-          acc[j][t] += d * (f.wsc[j] * f.xsv[t]);
-        } else {
-          const v4f d = mfma_scaled<kFmtE2M1, kFmtE4M3>(f.a[j], f.b[t], f.wsb[j], kUnitScale);
-          acc[j][t] += d * f.xsv[t];
-        }
+      for (int j = 0; j < NJ; ++j) {
+        if (WF == 0) d[j] = mfma_scaled<kFmtE4M3, kFmtE4M3>(f.a[j], f.b[t], kUnitScale, kUnitScale);
+        else d[j] = mfma_scaled<kFmtE2M1, kFmtE4M3>(f.a[j], f.b[t], f.wsb[j], kUnitScale);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // all NJ products in flight before they are consumed
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if (WF == 0) acc[j][t] += d[j] * (f.wsc[j] * f.xsv[t]);
+        else acc[j][t] += d[j] * f.xsv[t];
       }
     }
   }
 }
 
-// acc += sum over K steps [ks0, ks1) with the next step's operands loaded
-// while the current one is multiplied.
-template <int WF, int NJ, int NTT, int B32>
+// acc += sum over K steps [ks0, ks1).  Operands travel through a ring of ST
+// register stages: the loads for step ks + ST - 1 are issued before step ks
+// is multiplied, so ST - 1 steps of weight bytes are in flight per wave.
+// The loads are unconditional (past the end they repeat the last step and
+// hit in cache) so the compiler can count outstanding loads exactly and
+// wait only for the stage about to be used; only the MFMAs are predicated.
+template <int WF, int NJ, int NTT, int B32, int ST>
 __device__ __forceinline__ void kloop(v4f (&acc)[NJ][NTT], const uint8_t* const (&wrow)[NJ],
                                       const float* const (&wsc)[NJ], const uint8_t* const (&wsb)[NJ],
                                       const uint8_t* const (&brow)[NTT], const float* const (&bsc)[NTT],
                                       int ks0, int ks1, int g) {
-  Frag<WF, NJ, NTT> cur, nxt;
-  load_frag<WF, NJ, NTT, B32>(cur, wrow, wsc, wsb, brow, bsc, ks0, g);
-  for (int ks = ks0; ks < ks1; ++ks) {
-    if (ks + 1 < ks1) load_frag<WF, NJ, NTT, B32>(nxt, wrow, wsc, wsb, brow, bsc, ks + 1, g);
-    mma_frag<WF, NJ, NTT, B32>(acc, cur, wsc, bsc, ks, g);
-    cur = nxt;
+  Frag<WF, NJ, NTT> f[ST];
+#pragma unroll
+  for (int s = 0; s < ST - 1; ++s) {
+    load_frag<WF, NJ, NTT, B32>(f[s], wrow, wsc, wsb, brow, bsc, min(ks0 + s, ks1 - 1), g);
+    __builtin_amdgcn_sched_barrier(0);  // keep each stage's loads together, in stage order
+  }
+  for (int ks = ks0; ks < ks1; ks += ST) {
+#pragma unroll
+    for (int s = 0; s < ST; ++s) {
+      load_frag<WF, NJ, NTT, B32>(f[(s + ST - 1) % ST], wrow, wsc, wsb, brow, bsc, min(ks + s + ST - 1, ks1 - 1), g);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + s < ks1) mma_frag<WF, NJ, NTT, B32>(acc, f[s], wsc, bsc, ks + s, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
 struct GemmParams {
-  const uint8_t* act;     // GEMM1: xq [T][H] by token; GEMM2: hq [rows][I] by row
-  const float* act_s;     // matching scales
+  const uint8_t* act;        // GEMM1: xq [T][H] by token; GEMM2: hq [rows][I] by row
+  const float* act_s;        // matching scales
   const int32_t* row_token;  // GEMM1 only
   const int32_t* offsets;
   const uint8_t* w;
   const void* ws;
   const uint8_t* sw;
   const void* sws;
-  uint8_t* hq;            // GEMM1 outputs
+  uint8_t* hq;               // GEMM1 outputs
   float* hs;
-  float* y;               // GEMM2 output
+  float* y;                  // GEMM2 output
   float* part;
   int32_t* cnt;
   int H, I, E, G, wblk, ngroups, S, ntiles, rows_cap;
 };
 
-// Split-K arrival: every workgroup has stored its partial sums; returns true
-// in exactly one workgroup of the unit (the last to arrive).
+// Split-K hand-off between workgroups that may sit on different XCDs (each
+// XCD has its own L2).  Partial sums travel through device-coherent (sc1)
+// stores and loads, which bypass the non-coherent L2 contents, so no L2
+// writeback or invalidate is needed: a workgroup waits until its sc1 stores
+// have completed, then counts itself in with a device-scope atomic; the
+// workgroup that brings the count to S reads every partial back with sc1
+// loads and finishes the unit.  Sums are taken in split order, so the result
+// does not depend on which workgroup arrives last.
+// Buffer resource over the partial-sum array; 16-byte accesses with the sc1
+// cache policy bit are device-coherent.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+constexpr int kSc1 = 16;  // cache-policy operand of the buffer intrinsics: sc1
+
+__device__ __forceinline__ void st_coherent(__amdgpu_buffer_rsrc_t r, long elem, const v4f& v) {
+  const v4u u = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+  __builtin_amdgcn_raw_buffer_store_b128(u, r, int(elem * 4), 0, kSc1);
+}
+
+__device__ __forceinline__ v4f ld_coherent(__amdgpu_buffer_rsrc_t r, long elem) {
+  const v4u u = __builtin_amdgcn_raw_buffer_load_b128(r, int(elem * 4), 0, kSc1);
+  return v4f{__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]), __uint_as_float(u[3])};
+}
+
+// Every workgroup has issued its partial sums; returns true in exactly one
+// workgroup of the unit (the last to arrive).
 __device__ __forceinline__ bool arrive_last(int32_t* counter, int S, int* s_flag) {
-  __threadfence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) *s_flag = (atomicAdd(counter, 1) == S - 1);
+  if (threadIdx.x == 0)
+    *s_flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
   __syncthreads();
-  const bool last = *s_flag;
-  if (last) __threadfence();
-  return last;
+  return *s_flag;
 }
 
 // ---------------------------------------------------------------------
@@ -340,7 +384,7 @@ __device__ __forceinline__ bool arrive_last(int32_t* counter, int S, int* s_flag
 template <int NTT>
 __device__ __forceinline__ void swiglu_requant_store(const v4f (&acc)[4][NTT], const GemmParams& p, int row0,
                                                      int ne, int pass, int n0, float (*s_red)[4][16]) {
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 15, g = lane >> 4;
   float h[NTT][8];
   float amax[NTT];
 #pragma unroll
@@ -401,8 +445,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
   const int e = nth_nonempty_group(p.offsets, p.ngroups, slot, s_wsum, &s_res);
   if (e < 0) return;
   const int row0 = p.offsets[e], ne = p.offsets[e + 1] - row0;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 15, g = lane >> 4;
   const int H = p.H, I = p.I, n0 = tile * 128;
+  const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(p.part);
   const bool shared = e == p.E;
   const long ee = shared ? 0 : e;
   const long kbytes = WF == 0 ? H : H / 2;
@@ -442,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int t = 0; t < NTT; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    kloop<WF, 4, NTT, B32>(acc, wrow, wsc, wsb, brow, bsc, ks0, ks1, g);
+    kloop<WF, 4, NTT, B32, kStages>(acc, wrow, wsc, wsb, brow, bsc, ks0, ks1, g);
     if (S == 1) {
       swiglu_requant_store<NTT>(acc, p, row0, ne, pass, n0, s_red);
     } else {
@@ -450,11 +495,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
       for (int t = 0; t < NTT; ++t) {
         const int idx = pass * 16 * NTT + t * 16 + m;
         if (idx >= ne) continue;
-        float* dst = p.part + ((long(split) * nt + tile) * p.rows_cap + row0 + idx) * 256;
+        const long dst = ((long(split) * nt + tile) * p.rows_cap + row0 + idx) * 256;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int col = (j >> 1) * 128 + 32 * w + 16 * (j & 1) + 4 * g;
-          *reinterpret_cast<v4f*>(dst + col) = acc[j][t];
+          st_coherent(prs, dst + col, acc[j][t]);
         }
       }
     }
@@ -471,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
         const int col = (j >> 1) * 128 + 32 * w + 16 * (j & 1) + 4 * g;
         v4f s = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int sp = 0; sp < S; ++sp)
-          s += *reinterpret_cast<const v4f*>(p.part + ((long(sp) * nt + tile) * p.rows_cap + row0 + idx) * 256 + col);
+          s += ld_coherent(prs, ((long(sp) * nt + tile) * p.rows_cap + row0 + idx) * 256 + col);
         acc[j][t] = s;
       }
     }
@@ -492,8 +537,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
   const int e = nth_nonempty_group(p.offsets, p.ngroups, slot, s_wsum, &s_res);
   if (e < 0) return;
   const int row0 = p.offsets[e], ne = p.offsets[e + 1] - row0;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 15, g = lane >> 4;
   const int H = p.H, I = p.I, n0 = tile * 128;
+  const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(p.part);
   const bool shared = e == p.E;
   const long ee = shared ? 0 : e;
   const long kbytes = WF == 0 ? I : I / 2;
@@ -532,7 +578,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int t = 0; t < NTT; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    kloop<WF, 2, NTT, B32>(acc, wrow, wsc, wsb, brow, bsc, ks0, ks1, g);
+    kloop<WF, 2, NTT, B32, kStages>(acc, wrow, wsc, wsb, brow, bsc, ks0, ks1, g);
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
       const int idx = pass * 16 * NTT + t * 16 + m;
@@ -544,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
         if (S == 1)
           *reinterpret_cast<v4f*>(p.y + r * H + n0 + col) = acc[j][t];
         else
-          *reinterpret_cast<v4f*>(p.part + ((long(split) * nt + tile) * p.rows_cap + r) * 128 + col) = acc[j][t];
+          st_coherent(prs, ((long(split) * nt + tile) * p.rows_cap + r) * 128 + col, acc[j][t]);
       }
     }
   }
@@ -556,7 +602,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
     const int col = (q % 32) * 4;
     v4f s = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int sp = 0; sp < S; ++sp)
-      s += *reinterpret_cast<const v4f*>(p.part + ((long(sp) * nt + tile) * p.rows_cap + r) * 128 + col);
+      s += ld_coherent(prs, ((long(sp) * nt + tile) * p.rows_cap + r) * 128 + col);
     *reinterpret_cast<v4f*>(p.y + r * H + n0 + col) = s;
   }
 }

@@ -39,6 +39,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <thread>
 #include <vector>
@@ -121,11 +122,22 @@ void quant_group(const float* v, int G, uint8_t* q, float* s) {
 }
 
 // ---------------------------------------------------------------- threading
+// Worker count: oracle_set_threads(n) if called, else OMP_NUM_THREADS, else
+// the hardware concurrency capped at 16.
+int default_threads() {
+  if (g_threads > 0) return g_threads;
+  if (const char* e = std::getenv("OMP_NUM_THREADS")) {
+    const int v = std::atoi(e);
+    if (v > 0) return v;
+  }
+  const int hw = int(std::thread::hardware_concurrency());
+  return std::max(1, std::min(hw, 16));
+}
+
 template <class F>
 void parallel_for(int64_t n, F f) {
-  int nt = g_threads > 0 ? g_threads : int(std::thread::hardware_concurrency());
-  if (nt < 1) nt = 1;
-  if (n < 2 * nt) nt = n > 0 ? 1 : 0;
+  int nt = default_threads();
+  if (n < nt) nt = int(n);
   if (nt <= 1) {
     for (int64_t i = 0; i < n; ++i) f(i);
     return;
@@ -219,9 +231,7 @@ void dequant_row(const uint8_t* q, const float* s, int64_t len, int G, double* o
 extern "C" {
 
 void oracle_set_threads(int n) { g_threads = n; }
-int oracle_get_threads() {
-  return g_threads > 0 ? g_threads : int(std::thread::hardware_concurrency());
-}
+int oracle_get_threads() { return default_threads(); }
 // Test-only: plant a known mistake (0 = none, 1 = gate/up swapped,
 // 2 = first K-block weight scale dropped, 3 = unstable row order inside an
 // expert, 4 = offsets shifted by one) so tests can show their pins catch it.

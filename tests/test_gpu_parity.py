@@ -55,6 +55,9 @@ REDUCED = {
     "mxfp4": reduced("decode_mxfp4", H=512, I=384, E=16, topk=4),
     "fp8_zipf_shared": reduced("decode_fp8_zipf_shared", H=512, I=256, E=32, topk=8),
     "mxfp4_shared": reduced("decode_mxfp4", H=384, I=256, E=12, topk=2, shared=True),
+    # long K with few experts: both GEMMs take the split-K path
+    "fp8_split": reduced("decode_fp8", H=2048, I=1024, E=8, topk=2),
+    "mxfp4_split_shared": reduced("decode_mxfp4", H=2048, I=1024, E=8, topk=2, shared=True),
 }
 
 _WCACHE = {}
