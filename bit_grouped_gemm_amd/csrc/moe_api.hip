@@ -15,6 +15,9 @@ namespace moe {
 #ifndef MOE_SPLIT_TARGET_WG
 #define MOE_SPLIT_TARGET_WG 256
 #endif
+#ifndef MOE_BIG_MIN_AVG_ROWS
+#define MOE_BIG_MIN_AVG_ROWS 48
+#endif
 #ifndef MOE_SPLIT_MIN_KSTEPS
 #define MOE_SPLIT_MIN_KSTEPS 4
 #endif
@@ -66,6 +69,14 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   };
   s.g1_split = fit(s.g1_split, H / 128, 2L * I);
   s.g2_split = fit(s.g2_split, I / 128, H);
+  // Big-tile kernels once experts hold enough rows that one 256-token pass
+  // beats the decode kernel's 16..64-token passes; they need 128-wide
+  // activation groups (one MFMA K step per scale), 128x128 e4m3 blocks or
+  // MXFP4, and H a multiple of 256.
+  const double groups = std::fmin(double(E), double(T) * k);
+  const double avg_rows = groups > 0 ? double(T) * k / groups : 0.0;
+  s.big = (G == 128 && (wfmt == 1 || wblk == 128) && H % 256 == 0 && avg_rows >= MOE_BIG_MIN_AVG_ROWS) ? 1 : 0;
+  if (s.big) s.g1_split = s.g2_split = 1;
   return s;
 }
 
@@ -195,6 +206,11 @@ int moe_grouped_gemm1_swiglu(const moe_cfg* cfg, const uint8_t* xq, const float*
   if (!has_rows) return MOE_OK;
   char* base = static_cast<char*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s.big)
+    return hip_status(launch_gemm1_big(s, xq, xs, row_token, offsets,
+                                       WeightPtrs{static_cast<const uint8_t*>(w->w1), w->w1s,
+                                                  static_cast<const uint8_t*>(w->sw1), w->sw1s},
+                                       hq, hs, 1, st));
   int32_t* cnt = reinterpret_cast<int32_t*>(base + L.cnt1);
   if (s.g1_split > 1) {
     if ((rc = hip_status(launch_clear(cnt, (s.E + 1) * s.g1_tiles, st)))) return rc;
@@ -219,6 +235,11 @@ int moe_grouped_gemm2(const moe_cfg* cfg, const uint8_t* hq, const float* hs, co
   if (!has_rows) return MOE_OK;
   char* base = static_cast<char*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s.big)
+    return hip_status(launch_gemm2_big(s, hq, hs, offsets,
+                                       WeightPtrs{static_cast<const uint8_t*>(w->w2), w->w2s,
+                                                  static_cast<const uint8_t*>(w->sw2), w->sw2s},
+                                       y, 1, st));
   int32_t* cnt = reinterpret_cast<int32_t*>(base + L.cnt2);
   if (s.g2_split > 1) {
     if ((rc = hip_status(launch_clear(cnt, (s.E + 1) * s.g2_tiles, st)))) return rc;
@@ -269,16 +290,19 @@ int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, co
   if ((rc = hip_status(launch_route_quant(s, x, topk_ids, counts, offsets, eidx, rtok, xq, xs, cnt1, nclear, st))))
     return rc;
   if (!has_rows) return MOE_OK;
-  if ((rc = hip_status(launch_gemm1(s, xq, xs, rtok, offsets,
-                                    WeightPtrs{static_cast<const uint8_t*>(w->w1), w->w1s,
-                                               static_cast<const uint8_t*>(w->sw1), w->sw1s},
-                                    hq, hs, reinterpret_cast<float*>(b + L.part1), cnt1, st))))
-    return rc;
-  if ((rc = hip_status(launch_gemm2(s, hq, hs, offsets,
-                                    WeightPtrs{static_cast<const uint8_t*>(w->w2), w->w2s,
-                                               static_cast<const uint8_t*>(w->sw2), w->sw2s},
-                                    y, reinterpret_cast<float*>(b + L.part2), cnt2, st))))
-    return rc;
+  const WeightPtrs w1{static_cast<const uint8_t*>(w->w1), w->w1s, static_cast<const uint8_t*>(w->sw1), w->sw1s};
+  const WeightPtrs w2{static_cast<const uint8_t*>(w->w2), w->w2s, static_cast<const uint8_t*>(w->sw2), w->sw2s};
+  if (s.big) {
+    if ((rc = hip_status(launch_gemm1_big(s, xq, xs, rtok, offsets, w1, hq, hs, 1, st)))) return rc;
+    if ((rc = hip_status(launch_gemm2_big(s, hq, hs, offsets, w2, y, 1, st)))) return rc;
+  } else {
+    if ((rc = hip_status(launch_gemm1(s, xq, xs, rtok, offsets, w1, hq, hs,
+                                      reinterpret_cast<float*>(b + L.part1), cnt1, st))))
+      return rc;
+    if ((rc = hip_status(launch_gemm2(s, hq, hs, offsets, w2, y, reinterpret_cast<float*>(b + L.part2), cnt2,
+                                      st))))
+      return rc;
+  }
   return hip_status(launch_combine(s, y, eidx, offsets, topk_weights, out, st));
 }
 

@@ -22,6 +22,8 @@ struct Shape {
   int g2_tiles;     // H / 128
   int g2_split;     // K splits over I/128 steps
   int g2_ntt;
+  // groups with many rows (prefill) run the 256 x 256-token LDS-staged kernels
+  int big;          // 1: both GEMMs use the big-tile kernels
 };
 
 // Workspace carve (byte offsets from the caller's ws base; 256-aligned).
@@ -55,6 +57,13 @@ hipError_t launch_gemm1(const Shape& s, const uint8_t* xq, const float* xs, cons
 
 hipError_t launch_gemm2(const Shape& s, const uint8_t* hq, const float* hs, const int32_t* offsets,
                         WeightPtrs w2, float* y, float* part, int32_t* cnt, hipStream_t st);
+
+hipError_t launch_gemm1_big(const Shape& s, const uint8_t* xq, const float* xs, const int32_t* row_token,
+                            const int32_t* offsets, WeightPtrs w1, uint8_t* hq, float* hs, int min_rows,
+                            hipStream_t st);
+
+hipError_t launch_gemm2_big(const Shape& s, const uint8_t* hq, const float* hs, const int32_t* offsets,
+                            WeightPtrs w2, float* y, int min_rows, hipStream_t st);
 
 hipError_t launch_combine(const Shape& s, const float* y, const int32_t* expand_idx, const int32_t* offsets,
                           const float* topk_w, uint16_t* out, hipStream_t st);

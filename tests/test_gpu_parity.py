@@ -317,6 +317,49 @@ def test_layer_full_size_sampled(name, T):
     assert torch.isfinite(out.float()).all()
 
 
+# ------------------------------------------------------------------ big-tile (prefill) path
+BIG = {
+    # many rows per expert select the 256-row x 192-token kernels; the shared group of
+    # T rows needs two 192-token passes when T > 192
+    "big_mxfp4_shared": reduced("decode_mxfp4", H=512, I=256, E=4, topk=2, shared=True),
+    "big_fp8": reduced("decode_fp8", H=512, I=384, E=6, topk=2),
+}
+
+
+@pytest.mark.parametrize("name", list(BIG))
+@pytest.mark.parametrize("T", [200, 700])
+def test_layer_big_tiles(name, T):
+    moe = M()
+    wl = BIG[name]
+    _note(f"big {name} T={T}")
+    w, wc = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=11)
+    cfg = moe.Cfg.for_workload(wl, T)
+    out = moe.moe_layer(cfg, x, ids, tw, w)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(T + 1)
+    toks = sorted(set([0, T - 1] + list(rng.choice(T, size=40, replace=False))))
+    ref = oracle.layer_for(wl, T, wc).layer(x.cpu(), ids.cpu(), tw.cpu(), toks=toks)
+    tol_check(out.float().cpu().numpy()[toks], ref, f"{name} T={T}")
+    # the stage calls take the same path
+    counts, offsets, eidx, rtok, xq, xs = moe.moe_permute(cfg, x, ids)
+    ws = moe.workspace(cfg)
+    hq, hs = moe.moe_grouped_gemm1_swiglu(cfg, xq, xs, rtok, offsets, w, ws)
+    y = moe.moe_grouped_gemm2(cfg, hq, hs, offsets, w, ws)
+    out2 = moe.moe_combine(cfg, y, eidx, offsets, tw)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    # requantised codes of a sample of rows against the oracle's
+    R = int(offsets[-1].item())
+    rows = sorted(set(rng.choice(R, size=60, replace=False).tolist() + [R - 1]))
+    lay = oracle.layer_for(wl, T, wc)
+    _, hq_ref, hs_ref = lay.gemm1(xq.cpu(), xs.cpu(), rtok.cpu(), offsets.cpu(), rows)
+    agree = (hq.cpu().numpy()[rows] == hq_ref).mean()
+    _note(f"  h code agreement {agree:.5f}")
+    assert agree >= 0.99
+    assert np.abs(hs.cpu().numpy()[rows] / hs_ref - 1).max() <= 1e-3
+
+
 # ------------------------------------------------------------------ edge cases
 def test_layer_T0_is_a_no_op():
     moe = M()
