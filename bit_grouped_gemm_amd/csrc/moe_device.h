@@ -72,6 +72,12 @@ __device__ __forceinline__ v4f mfma_scaled(const v8i& a, const v8i& b, int sa, i
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, FA, FB, 0, sa, 0, sb);
 }
 
+// Same, accumulating into c (D = C + A.B in the matrix core).
+template <int FA, int FB>
+__device__ __forceinline__ v4f mfma_scaled_acc(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
+}
+
 constexpr int kFmtE4M3 = 0;
 constexpr int kFmtE2M1 = 4;
 constexpr int kUnitScale = 127;  // e8m0 code of 1.0

@@ -3,16 +3,27 @@
 // When an expert holds ~100+ token rows (prefill: T = 4096, top-8 over 256
 // experts gives ~128 rows per expert) a workgroup must cover all of them
 // per pass, or each weight byte is read from HBM once per pass.  Here a
-// workgroup of 8 waves owns 256 weight rows and up to 192 token rows:
-//   * weights stream from HBM straight into registers in MFMA layout, one
-//     128-K step ahead; the group's token rows of each step are staged
-//     through LDS (two buffers, one barrier per step) and read by all waves;
-//   * each of the 8 waves owns 32 of the 256 weight rows (two 16-row MFMA
-//     tiles: in GEMM1 one gate and one up tile, so SwiGLU pairs meet in one
-//     lane) across all 12 token tiles, which keeps 2 x 12 accumulator tiles
-//     and a K step of weight operands in flight within 256 registers;
-//   * LDS rows are XOR-swizzled by 16-byte chunk so the MFMA-layout reads
-//     (16 lanes on 16 consecutive rows, same chunk) hit distinct banks;
+// workgroup of 8 waves owns 256 weight rows and up to 192 token rows, and
+// walks K in steps of 128:
+//   * both operands of a step travel HBM/L2 -> LDS by direct-to-LDS loads
+//     (global_load_lds_dwordx4: 64 lanes x 16 B into 1 KB of LDS per
+//     instruction, no registers held while in flight) through a ring of
+//     stages (three for MXFP4 weights, two for e4m3 weights whose steps are
+//     twice as large), so two steps of weights and token rows are in
+//     flight while one is multiplied;
+//   * in LDS every 16-row x 128-K operand tile is stored in the lane order
+//     of the scaled-MFMA fragment (lane l's 16 bytes at l * 16 of a 1 KB
+//     block), so fragment reads are linear ds_read_b128 with no bank
+//     conflicts and the address permutation is paid on the global side;
+//   * the 8 waves form a 4 x 2 grid: a wave owns 4 weight tiles (64 rows;
+//     in GEMM1 two gate and the two matching up tiles, so SwiGLU pairs meet
+//     in one lane) and every second token tile, which keeps up to 4 x 6
+//     fp32 accumulator tiles in registers and reads each token fragment
+//     once per 4 MFMAs;
+//   * one vmcnt wait and one barrier per step: each wave waits for its own
+//     loads of the step, the barrier makes every wave's loads visible, and
+//     the loads two steps ahead are issued after the barrier, into the
+//     stage every wave has finished reading;
 //   * all tiles of one expert are dispatched to the same XCD (workgroup
 //     ids are dealt round-robin over the 8 XCDs), so the expert's token rows
 //     are fetched into that XCD's L2 once and re-read from there.
@@ -27,13 +38,32 @@ namespace moe {
 namespace {
 
 constexpr int kBigThreads = 512;
-constexpr int kRows = 256;      // weight rows per workgroup
-constexpr int kTokCap = 192;    // token rows per pass
-constexpr int kTokTiles = kTokCap / 16;
-constexpr int kBChunks = kTokCap * 8;      // 16-byte chunks of one staged token tile
-constexpr int kBPT = kBChunks / kBigThreads;  // 3 token-row chunks per thread per step
-static_assert(kBChunks % kBigThreads == 0, "every thread stages the same number of chunks");
-constexpr int kBigStages = 2;  // weight register stages (ring positions 0, 1)
+constexpr int kTokCap = 160;                 // token rows per pass
+constexpr int kTokTiles = kTokCap / 16;      // 10
+constexpr int kWTiles = 16;                  // 256 weight rows
+constexpr int kBBytes = kTokTiles * 2048;     // token tiles: 16 rows x 128 B, chunk-swizzled
+constexpr int kXsBytes = 8 * 64 * 4;         // token scales: one dword slot per lane of 8 waves
+constexpr int kAsBytes = 8 * 64 * 4;         // MXFP4 scales: one dword (4 x e8m0) per lane of 8 waves
+constexpr int kTokPerWave = kTokTiles / 2;   // token tiles of one wave column
+constexpr int kSinkBytes = 1024;             // target of token loads past the pass's tiles
+
+template <int WF> struct BigGeo {
+  static constexpr int kStages = WF == 1 ? 3 : 2;
+  static constexpr int kABytes = kWTiles * 1024 * (WF == 1 ? 1 : 2);
+  static constexpr int kXsOff = kBBytes;
+  static constexpr int kAOff = kBBytes + kXsBytes;
+  static constexpr int kAsOff = kAOff + kABytes;
+  static constexpr int kSinkOff = kAsOff + (WF == 1 ? kAsBytes : 0);
+  static constexpr int kStageBytes = kSinkOff + kSinkBytes;
+  // direct-to-LDS loads per wave per stage: token rows 3, token scales 1,
+  // weight tiles 2 (MXFP4) or 4 (e4m3 halves), MXFP4 scales 1
+  static constexpr int kLoadsPerStage = 3 + 1 + (WF == 1 ? 2 + 1 : 4);
+  static constexpr int kLdsBytes = kStages * kStageBytes;
+};
+static_assert(BigGeo<1>::kLdsBytes <= 160 * 1024, "MXFP4 ring fits the 160 KB LDS");
+static_assert(4 * kTokCap * 4 <= BigGeo<0>::kStageBytes, "epilogue maxima fit one stage");
+static_assert(BigGeo<0>::kLdsBytes <= 160 * 1024, "e4m3 ring fits the 160 KB LDS");
+static_assert(kTokTiles * 2 <= 3 * 8, "at most three token-row loads per wave");
 
 struct BigParams {
   const uint8_t* act;        // GEMM1: xq [T][H] by token; GEMM2: hq [rows][I] by row
@@ -50,23 +80,49 @@ struct BigParams {
   int H, I, E, G, wblk, ngroups, ntiles, units, per_xcd, min_rows;
 };
 
-// byte offset of 16-byte chunk c (0..7) of token row r in LDS: rows of 128 B,
-// chunk index XOR-ed with r & 7 so 8 lanes reading one chunk of 8
-// consecutive rows hit 8 distinct 4-bank groups
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// one 16-byte-per-lane direct load into LDS: lane l's bytes land at
+// lds_base + 16 * l (lds_base wave-uniform)
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 4, 0, 0);
+}
 
-struct Lds {
-  uint8_t b[2][kTokCap * 128];   // token rows of one 128-K step, two buffers
-  float xs[2][kBigThreads];      // their scales (one slot per thread; slots >= rows unused)
-  float red[8][kTokCap];         // requantisation group maxima: [wave][token]
-};
+// wait until at most N vector-memory operations of this wave are pending
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, other counters at
+// their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// byte offset of 16-byte chunk c (0..7) of row r (0..15) in a 2 KB token
+// tile of 128-byte rows: the chunk index is XOR-ed with r & 7, so the MFMA
+// fragment reads (16 lanes on 16 rows, one chunk each) hit distinct banks
+// while a direct-to-LDS load still covers 8 whole rows (full cache lines)
+__device__ __forceinline__ int tok_swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+
+// workgroup barrier that the compiler may not move memory operations across;
+// the waits for the ring's direct-to-LDS loads are explicit (wait_vmcnt)
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 }  // namespace
 
 template <int WF, int MODE>
 __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
-  extern __shared__ __align__(16) uint8_t lds_raw[];
-  Lds& L = *reinterpret_cast<Lds*>(lds_raw);
+  using Geo = BigGeo<WF>;
+  constexpr int S = Geo::kStages;
+  // one array per ring stage: the compiler's alias analysis then tells the
+  // stages apart and waits for a stage's own direct-to-LDS loads only
+  __shared__ __align__(1024) uint8_t st0[Geo::kStageBytes];
+  __shared__ __align__(1024) uint8_t st1[Geo::kStageBytes];
+  __shared__ __align__(1024) uint8_t st2[S == 3 ? Geo::kStageBytes : 16];
   __shared__ int s_wsum[8], s_res;
 
   // ---- unit: XCD-aware order (blockIdx -> XCD is round-robin over 8)
@@ -110,192 +166,287 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
   if (e < 0) return;
   const int row0 = p.offsets[e], ne = p.offsets[e + 1] - row0;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 15, g = lane >> 4;
+  const int wr = w & 3, wc = w >> 2;     // wave row (weight tiles), wave column (token tiles)
   const int H = p.H, I = p.I;
   const int K = MODE == 0 ? H : I;       // reduction length
   const int NR = MODE == 0 ? 2 * I : H;  // weight rows of the matrix
   const int n0 = tile * (MODE == 0 ? 128 : 256);
   const bool shared = e == p.E;
   const long ee = shared ? 0 : e;
-  const long kb = WF == 0 ? K : K / 2;   // bytes per weight row
+  const int kb = WF == 0 ? K : K / 2;    // bytes per weight row
   const uint8_t* wmat = (shared ? p.sw : p.w) + ee * long(NR) * kb;
   const void* smat = shared ? p.sws : p.ws;
   const int nks = K / 128;
+  // first matrix row of weight tile j (0..15): GEMM1 tiles 0..7 are gate
+  // rows, 8..15 the up rows of the same h columns; GEMM2 rows in order
+  auto wtile_row = [&](int j) { return MODE == 0 ? (j < 8 ? n0 + 16 * j : I + n0 + 16 * (j - 8)) : n0 + 16 * j; };
 
-  // this wave's two 16-row weight tiles; GEMM1: gate rows n0+16w and up
-  // rows I+n0+16w (h columns 16w..16w+15); GEMM2: output rows n0+32w+16j
-  const uint8_t* wrow[2];
-  const float* wsc[2];
-  const uint8_t* wsb[2];
+  // ---- loader side: this lane's sources for the weight tiles of wave w
+  // (tiles 2w, 2w+1; e4m3: both K halves of each) and the MXFP4 scales
+  const uint8_t* a_src[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rb = MODE == 0 ? (j == 0 ? n0 + 16 * w : I + n0 + 16 * w) : n0 + 32 * w + 16 * j;
-    wrow[j] = wmat + long(rb + m) * kb;
-    if (WF == 0) {
-      const int b = p.wblk;
-      wsc[j] = static_cast<const float*>(smat) + ee * long(NR / b) * (K / b) + long(rb / b) * (K / b);
-      wsb[j] = nullptr;
-    } else {
-      wsb[j] = static_cast<const uint8_t*>(smat) + ee * long(NR) * (K / 32) + long(rb + m) * (K / 32);
-      wsc[j] = nullptr;
-    }
+  for (int q = 0; q < 2; ++q) a_src[q] = wmat + long(wtile_row(2 * w + q) + m) * kb + 16 * g;
+  const uint8_t* as_src = nullptr;
+  if (WF == 1) {
+    const int jt = 2 * w + (lane >> 5);
+    as_src = static_cast<const uint8_t*>(smat) + ee * long(NR) * (K / 32) + long(wtile_row(jt) + m) * (K / 32);
   }
+  // ---- consumer side: this wave's weight tiles
+  int ja[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ja[q] = MODE == 0 ? (q < 2 ? 2 * wr + q : 8 + 2 * wr + (q - 2)) : 4 * wr + q;
+  const float* wsc[4];  // e4m3: scale row of each tile's 128 x 128 block (one scale per K step)
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    wsc[q] = WF == 0 ? static_cast<const float*>(smat) + ee * long(NR / 128) * (K / 128) +
+                           long(wtile_row(ja[q]) / 128) * (K / 128)
+                     : nullptr;
 
   for (int pass0 = 0; pass0 < ne; pass0 += kTokCap) {
     const int npass = min(kTokCap, ne - pass0);
     const int ntt = (npass + 15) / 16;
-    // staging assignment: chunk ch = tid + i*512 -> token ch>>3, 16-byte chunk ch&7
-    int boff[kBPT];
+    const int ntw = (ntt + 1 - wc) / 2;  // token tiles of this wave: t = 2 * tt + wc
+    // token-row sources: the pass's ntt tiles take 2 * ntt loads of 8 rows x
+    // 128 B (load i: tile i / 2, rows 8 (i % 2) .. + 7), dealt round-robin to
+    // the waves (load q of wave w is i = w + 8 q).  Lane l fills LDS chunk
+    // l % 8 of row l / 8, i.e. global chunk (l % 8) ^ (row & 7).  Rows past
+    // the group repeat its last row.  Every wave issues three such loads per
+    // step; the ones past the pass's tiles read one 16-byte chunk with all
+    // lanes into the stage's sink, so every step has the same load count.
+    const uint8_t* b_src[3];
+    int b_dst[3];
 #pragma unroll
-    for (int i = 0; i < kBPT; ++i) {
-      const int ch = tid + i * kBigThreads;
-      const int tk = min(ch >> 3, npass - 1);
+    for (int q = 0; q < 3; ++q) {
+      const int i = w + 8 * q;
+      const int rl = (i & 1) * 8 + (lane >> 3);
+      const bool real = i < 2 * ntt;
+      const int tk = real ? min((i >> 1) * 16 + rl, npass - 1) : npass - 1;
       const long arow = MODE == 0 ? long(p.row_token[row0 + pass0 + tk]) : long(row0 + pass0 + tk);
-      boff[i] = int(arow * K) + (ch & 7) * 16;
+      b_src[q] = p.act + arow * K + (real ? ((lane & 7) ^ (rl & 7)) << 4 : 0);
+      b_dst[q] = real ? i * 1024 : Geo::kSinkOff;
     }
-    const float* xs_src = p.act_s;
-    if (tid < npass) {
-      const long arow = MODE == 0 ? long(p.row_token[row0 + pass0 + tid]) : long(row0 + pass0 + tid);
-      xs_src = p.act_s + arow * (K / p.G);
+    const float* xs_src;
+    {
+      const int tk = min(w * 64 + lane, npass - 1);
+      const long arow = MODE == 0 ? long(p.row_token[row0 + pass0 + tk]) : long(row0 + pass0 + tk);
+      xs_src = p.act_s + arow * (K / 128);
     }
 
-    v4f acc[2][kTokTiles];
+    // the direct-to-LDS loads of step ks into stage buffer st, in three
+    // parts (0: token scales and weights, 1: weight scales and the first
+    // token-row load, 2: the other two token-row loads)
+    auto issue = [&](int ks, uint8_t* st, int part) __attribute__((always_inline)) {
+      if (part == 0) {
+        dma4(xs_src + ks, st + Geo::kXsOff + w * 256);
+        if (WF == 1) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int t = 0; t < kTokTiles; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-    // Weights travel through two register stages (loads for step ks + 1 are
-    // issued while step ks is multiplied).  The
-    // token rows of a step go through two register stages and two LDS
-    // buffers: loaded two steps ahead, stored to LDS at the top of their
-    // step, read after the barrier.  Each step issues its token-row loads
-    // before its weight loads, so waiting for a token stage never waits for
-    // younger weight stages.  Every load and LDS store is unconditional (rows
-    // past the group repeat its last row, the step index is clamped at the
-    // end): with no divergent branches around them the compiler counts
-    // outstanding loads exactly instead of waiting for all of them.
-    v8i af[kBigStages][2];
-    int sa[kBigStages][2];
-    float wsv[kBigStages][2];
-    v4u bst[2][kBPT];
-    float xst[2] = {0.0f, 0.0f};
-    auto load_a = [&](int ks, int slot) __attribute__((always_inline)) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (WF == 0) {
-          af[slot][j] = load_e4m3_frag(wrow[j] + long(ks) * 128, g);
-          wsv[slot][j] = wsc[j][ks];
-          sa[slot][j] = kUnitScale;
+          for (int q = 0; q < 2; ++q) dma16(a_src[q] + long(ks) * 64, st + Geo::kAOff + (2 * w + q) * 1024);
         } else {
-          af[slot][j] = load_e2m1_frag(wrow[j] + long(ks) * 64, g);
-          sa[slot][j] = wsb[j][ks * 4 + g];
-          wsv[slot][j] = 1.0f;
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              dma16(a_src[q] + long(ks) * 128 + 64 * h, st + Geo::kAOff + (2 * (2 * w + q) + h) * 1024);
+        }
+      } else if (part == 1) {
+        if (WF == 1) dma4(as_src + ks * 4, st + Geo::kAsOff + w * 256);
+        dma16(b_src[0] + long(ks) * 128, st + b_dst[0]);
+      } else {
+        dma16(b_src[1] + long(ks) * 128, st + b_dst[1]);
+        dma16(b_src[2] + long(ks) * 128, st + b_dst[2]);
+      }
+    };
+    // pinned in place among the MFMAs: the load pipeline drains while the
+    // matrix cores work instead of taking every wave's loads in one burst
+    auto issue_part = [&](int ks, uint8_t* st, int part) __attribute__((always_inline)) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ks, st, part);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // accumulators: e4m3 weights promote each step's MFMA result with a VALU
+    // FMA (acc += d * ws * xs).  MXFP4 weights carry their scales inside
+    // the MFMA, and the accumulator is kept in units of the current step's
+    // token scale: before a step it is multiplied by xs_prev / xs_cur (a
+    // multiply that depends only on the previous step), then the MFMA adds
+    // the step's product in place; after the last step it is multiplied by
+    // that step's xs.  Token scales are positive (at least 2^-64 / 448), so
+    // the ratio is always defined.
+    v4f acc[4][kTokPerWave];
+    float xsp[kTokPerWave];  // MXFP4: the token scales of the previous step
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int t = 0; t < kTokPerWave; ++t) acc[q][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < kTokPerWave; ++t) xsp[t] = 0.0f;
+
+    // multiply one stage: A fragments of the wave's 4 weight tiles, then its
+    // token tiles two at a time, with the next stage's loads issued in
+    // between
+    auto compute = [&](int ks, const uint8_t* st, int ksn, uint8_t* nxt) __attribute__((always_inline)) {
+      v8i af[4];
+      int sa[4];
+      float wsv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (WF == 1) {
+          const v4u a = *reinterpret_cast<const v4u*>(st + Geo::kAOff + ja[q] * 1024 + lane * 16);
+          af[q] = v8i{int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
+          sa[q] = st[Geo::kAsOff + ((ja[q] >> 1) * 64 + (ja[q] & 1) * 32 + m) * 4 + g];
+          wsv[q] = 1.0f;
+        } else {
+          const v4u lo = *reinterpret_cast<const v4u*>(st + Geo::kAOff + (2 * ja[q]) * 1024 + lane * 16);
+          const v4u hi = *reinterpret_cast<const v4u*>(st + Geo::kAOff + (2 * ja[q] + 1) * 1024 + lane * 16);
+          af[q] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+          sa[q] = kUnitScale;
+          wsv[q] = wsc[q][ks];
+        }
+      }
+      float xsv[kTokPerWave];
+#pragma unroll
+      for (int tt = 0; tt < kTokPerWave; ++tt)
+        xsv[tt] = *reinterpret_cast<const float*>(st + Geo::kXsOff + ((2 * tt + wc) * 16 + m) * 4);
+      if (WF == 1) {
+        // rescale to this step's token scales
+#pragma unroll
+        for (int tt = 0; tt < kTokPerWave; ++tt) {
+          if (tt < ntw) {
+            const float r = xsp[tt] * __builtin_amdgcn_rcpf(xsv[tt]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q][tt] *= r;
+          }
+          xsp[tt] = xsv[tt];
+        }
+      }
+      static_assert(kTokPerWave <= 6, "three pairs of token tiles, one load part after each");
+#pragma unroll
+      for (int t0 = 0; t0 < 6; t0 += 2) {
+        issue_part(ksn, nxt, t0 / 2);
+        if (t0 < kTokPerWave && t0 < ntw) {
+          // a pair of token tiles (the last one alone when the count is odd)
+          v8i bf[2];
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            if (t0 + r >= kTokPerWave) continue;
+            const int t = 2 * (t0 + r) + wc;
+            const v4u lo = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, g));
+            const v4u hi = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, 4 + g));
+            bf[r] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+          }
+          if (WF == 1) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (t0 + r < kTokPerWave)
+                  acc[q][t0 + r] = mfma_scaled_acc<kFmtE2M1, kFmtE4M3>(af[q], bf[r], acc[q][t0 + r], sa[q], kUnitScale);
+          } else {
+            v4f d[2][4];
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (t0 + r < kTokPerWave) d[r][q] = mfma_scaled<kFmtE4M3, kFmtE4M3>(af[q], bf[r], kUnitScale, kUnitScale);
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (t0 + r < kTokPerWave) acc[q][t0 + r] += d[r][q] * (wsv[q] * xsv[t0 + r]);
+          }
         }
       }
     };
-    auto load_b = [&](int ks, int slot) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < kBPT; ++i) bst[slot][i] = ldg16(p.act + boff[i] + long(ks) * 128);
-      xst[slot] = xs_src[tid < npass ? ks : 0];
+
+    // ---- the K loop over the ring, unrolled by the ring depth so that each
+    // step's stage buffers are fixed arrays.  Every step issues the loads of
+    // the step S - 1 ahead, clamped to the last step (past the end they
+    // re-load it into a stage that is not read again), so every step has
+    // the same count of loads in flight and waits for the same count.
+    auto step = [&](int ks, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+      wait_vmcnt<(S - 2) * Geo::kLoadsPerStage>();
+      ring_barrier();
+      compute(ks, cur, min(ks + S - 1, nks - 1), nxt);
     };
-    load_b(0, 0);
-    load_b(min(1, nks - 1), 1);
-    load_a(0, 0);
-    // one 128-K step at ring position SIDX (0 or 1, a compile-time constant
-    // after unrolling): store the staged token rows, barrier, issue the loads
-    // two steps (token rows) and one step (weights) ahead, multiply
-#define MOE_BIG_STEP(KS, SIDX)                                                                              \
-  {                                                                                                         \
-    const int ks_ = (KS);                                                                                   \
-    const int buf = (SIDX);                                                                                 \
-    _Pragma("unroll") for (int i = 0; i < kBPT; ++i) {                                                      \
-      const int ch = tid + i * kBigThreads;                                                                 \
-      *reinterpret_cast<v4u*>(&L.b[buf][swz(ch >> 3, ch & 7)]) = bst[buf][i];                               \
-    }                                                                                                       \
-    L.xs[buf][tid] = xst[buf];                                                                              \
-    __syncthreads();                                                                                        \
-    load_b(min(ks_ + 2, nks - 1), buf);                                                                     \
-    load_a(min(ks_ + 1, nks - 1), buf ^ 1);                                                                 \
-    _Pragma("unroll") for (int t0 = 0; t0 < kTokTiles; t0 += 2) {                                          \
-      if (t0 < ntt) {                                                                                       \
-        v8i bf[2];                                                                                          \
-        float xsv[2];                                                                                       \
-        _Pragma("unroll") for (int q = 0; q < 2; ++q) {                                                     \
-          const int tk = (t0 + q) * 16 + m;                                                                 \
-          const v4u lo = *reinterpret_cast<const v4u*>(&L.b[buf][swz(tk, g)]);                              \
-          const v4u hi = *reinterpret_cast<const v4u*>(&L.b[buf][swz(tk, 4 + g)]);                          \
-          bf[q] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])}; \
-          xsv[q] = L.xs[buf][tk];                                                                           \
-        }                                                                                                   \
-        v4f d[2][2];                                                                                        \
-        _Pragma("unroll") for (int q = 0; q < 2; ++q)                                                       \
-          _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                   \
-            if (WF == 0) d[q][j] = mfma_scaled<kFmtE4M3, kFmtE4M3>(af[buf][j], bf[q], kUnitScale, kUnitScale); \
-            else d[q][j] = mfma_scaled<kFmtE2M1, kFmtE4M3>(af[buf][j], bf[q], sa[buf][j], kUnitScale);     \
-          }                                                                                                 \
-        _Pragma("unroll") for (int q = 0; q < 2; ++q)                                                       \
-          _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                     \
-            acc[j][t0 + q] += d[q][j] * (WF == 0 ? wsv[buf][j] * xsv[q] : xsv[q]);                          \
-      }                                                                                                     \
-    }                                                                                                       \
-  }
-    // whole ring periods without per-step guards (no branch joins around
-    // loads), then at most one guarded remainder step
-    int ks0 = 0;
-    for (; ks0 + 2 <= nks; ks0 += 2) {
-#pragma unroll
-      for (int sidx = 0; sidx < 2; ++sidx) MOE_BIG_STEP(ks0 + sidx, sidx)
+    for (int part = 0; part < 3; ++part) issue(0, st0, part);
+    int ks = 0;
+    if (S == 3) {
+      for (int part = 0; part < 3; ++part) issue(min(1, nks - 1), st1, part);
+      for (; ks + 3 <= nks; ks += 3) {
+        step(ks, st0, st2);
+        step(ks + 1, st1, st0);
+        step(ks + 2, st2, st1);
+      }
+      if (ks < nks) step(ks, st0, st2);
+      if (ks + 1 < nks) step(ks + 1, st1, st0);
+    } else {
+      for (; ks + 2 <= nks; ks += 2) {
+        step(ks, st0, st1);
+        step(ks + 1, st1, st0);
+      }
+      if (ks < nks) step(ks, st0, st1);
     }
-    if (ks0 < nks) MOE_BIG_STEP(ks0, 0)
-#undef MOE_BIG_STEP
+
+    if (WF == 1)  // back from units of the last step's token scale
+#pragma unroll
+      for (int tt = 0; tt < kTokPerWave; ++tt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q][tt] *= xsp[tt];
 
     // ---- epilogue
+    wait_vmcnt<0>();  // the clamped loads past the last step land in the ring too
+    __syncthreads();  // all waves are done reading the ring
     if (MODE == 0) {
-      // h = silu(gate) * up in place of the gate accumulator: h column
-      // 16w + 4g + i, token column m of each tile
-      float amax[kTokTiles];
+      // h = silu(gate) * up in place of the gate accumulators: h column
+      // n0 + 32 wr + 16 q + 4 g + i, token 16 t + m with t = 2 tt + wc
+      float* red = reinterpret_cast<float*>(st0);  // [4 wave rows][kTokCap]
+      float amax[kTokPerWave];
 #pragma unroll
-      for (int t = 0; t < kTokTiles; ++t) {
-        amax[t] = 0.0f;
+      for (int tt = 0; tt < kTokPerWave; ++tt) {
+        amax[tt] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float gt = acc[0][t][i], up = acc[1][t][i];
-          const float v = gt / (1.0f + expf(-gt)) * up;
-          acc[0][t][i] = v;
-          amax[t] = fmaxf(amax[t], fabsf(v));
-        }
-        amax[t] = wave_max_xor(amax[t], 16);
-        amax[t] = wave_max_xor(amax[t], 32);
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gt = acc[q][tt][i], up = acc[q + 2][tt][i];
+            const float v = gt / (1.0f + expf(-gt)) * up;
+            acc[q][tt][i] = v;
+            amax[tt] = fmaxf(amax[tt], fabsf(v));
+          }
+        amax[tt] = wave_max_xor(amax[tt], 16);
+        amax[tt] = wave_max_xor(amax[tt], 32);
       }
-      __syncthreads();
       if (g == 0)
 #pragma unroll
-        for (int t = 0; t < kTokTiles; ++t) L.red[w][t * 16 + m] = amax[t];
+        for (int tt = 0; tt < kTokPerWave; ++tt) red[wr * kTokCap + (2 * tt + wc) * 16 + m] = amax[tt];
       __syncthreads();
 #pragma unroll
-      for (int t = 0; t < kTokTiles; ++t) {
-        const int idx = t * 16 + m;
-        if (t >= ntt || idx >= npass) continue;
-        float am = L.red[0][idx];
+      for (int tt = 0; tt < kTokPerWave; ++tt) {
+        const int idx = (2 * tt + wc) * 16 + m;
+        if (tt >= ntw || idx >= npass) continue;
+        float am = red[idx];
 #pragma unroll
-        for (int q = 1; q < 8; ++q) am = fmaxf(am, L.red[q][idx]);
+        for (int q = 1; q < 4; ++q) am = fmaxf(am, red[q * kTokCap + idx]);
         const float mult = quant_mult(am);
         const long r = row0 + pass0 + idx;
-        uint32_t word = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) word |= enc_e4m3(acc[0][t][i] * mult) << (8 * i);
-        *reinterpret_cast<uint32_t*>(p.hq + r * I + n0 + 16 * w + 4 * g) = word;
-        if (g == 0 && w == 0) p.hs[r * (I / 128) + n0 / 128] = 1.0f / mult;
+        for (int q = 0; q < 2; ++q) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) word |= enc_e4m3(acc[q][tt][i] * mult) << (8 * i);
+          *reinterpret_cast<uint32_t*>(p.hq + r * I + n0 + 32 * wr + 16 * q + 4 * g) = word;
+        }
+        if (g == 0 && wr == 0) p.hs[r * (I / 128) + n0 / 128] = 1.0f / mult;
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < kTokTiles; ++t) {
-        const int idx = t * 16 + m;
-        if (t >= ntt || idx >= npass) continue;
+      for (int tt = 0; tt < kTokPerWave; ++tt) {
+        const int idx = (2 * tt + wc) * 16 + m;
+        if (tt >= ntw || idx >= npass) continue;
         const long r = row0 + pass0 + idx;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          *reinterpret_cast<v4f*>(p.y + r * H + n0 + 32 * w + 16 * j + 4 * g) = acc[j][t];
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<v4f*>(p.y + r * H + n0 + 64 * wr + 16 * q + 4 * g) = acc[q][tt];
       }
     }
     __syncthreads();  // LDS is reused by the next pass
@@ -308,8 +459,7 @@ static hipError_t launch_big(const Shape& s, int mode, BigParams& p, hipStream_t
   p.units = units;
   p.per_xcd = (units + 7) / 8;
   const unsigned grid = unsigned(p.per_xcd) * 8;
-  const size_t lds = sizeof(Lds);
-  static_assert(sizeof(Lds) <= 64 * 1024, "within the default dynamic LDS limit");
+  const size_t lds = 0;  // static LDS
   if (s.wfmt == 0) {
     if (mode == 0) hipLaunchKernelGGL((k_gemm_big<0, 0>), dim3(grid), dim3(kBigThreads), lds, st, p);
     else hipLaunchKernelGGL((k_gemm_big<0, 1>), dim3(grid), dim3(kBigThreads), lds, st, p);
@@ -320,7 +470,6 @@ static hipError_t launch_big(const Shape& s, int mode, BigParams& p, hipStream_t
   return hipGetLastError();
 }
 
-size_t big_lds_bytes() { return sizeof(Lds); }
 
 hipError_t launch_gemm1_big(const Shape& s, const uint8_t* xq, const float* xs, const int32_t* row_token,
                             const int32_t* offsets, WeightPtrs w1, uint8_t* hq, float* hs, int min_rows,
