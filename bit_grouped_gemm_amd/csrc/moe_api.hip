@@ -306,6 +306,20 @@ int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, co
   return hip_status(launch_combine(s, y, eidx, offsets, topk_weights, out, st));
 }
 
+int moe_tile_weights(int32_t wfmt, int32_t mats, int32_t N, int32_t K, const void* w, const void* s, void* w_tiled,
+                     void* s_tiled, void* stream) {
+  if (wfmt != MOE_WFMT_FP8_BLOCK && wfmt != MOE_WFMT_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (mats < 0 || N < 0 || K < 0 || N % 16 || K % 128) return MOE_ERR_BAD_SHAPE;
+  const bool any = int64_t(mats) * N * K > 0, mx = wfmt == MOE_WFMT_MXFP4;
+  int rc = check_ptrs({{w, any}, {w_tiled, any}, {s, any && mx}, {s_tiled, any && mx}});
+  if (rc) return rc;
+  if (!any) return MOE_OK;
+  if (w == w_tiled || (mx && s == s_tiled)) return MOE_ERR_UNSUPPORTED;  // not in place
+  return hip_status(launch_tile_weights(wfmt, mats, N, K, static_cast<const uint8_t*>(w),
+                                        static_cast<const uint8_t*>(s), static_cast<uint8_t*>(w_tiled),
+                                        static_cast<uint8_t*>(s_tiled), static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_str(int status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -105,6 +105,32 @@ __device__ __forceinline__ v8i load_e2m1_frag(const uint8_t* row_k0, int g) {
   return r;
 }
 
+// ------------------------------------------------------------ tiled weights
+// Expert weights are stored as tiles of 16 rows x 128 K in MFMA lane order,
+// tile (k step, row tile) at ((ks * N/16) + rt) * kTileBytes<WF>: lane l's
+// 16 bytes (row 16 rt + l % 16, K bytes 16 (l / 16) of the step's row chunk)
+// at l * 16; e4m3 tiles carry the K bytes 64..127 of the step in a second
+// kilobyte.  MXFP4 scales: 64 bytes per tile, byte l = e8m0 of row
+// 16 rt + l % 16 and 32-block l / 16 of the step -- the scale operand of
+// MFMA lane l.
+template <int WF> constexpr int kTileBytes = WF == 0 ? 2048 : 1024;
+constexpr int kTileScaleBytes = 64;
+
+// this lane's operand from a weight tile (tile_lane = tile base + 16 * lane)
+template <int WF>
+__device__ __forceinline__ v8i load_tile_frag(const uint8_t* tile_lane) {
+  const v4u lo = ldg16(tile_lane);
+  v8i r;
+  r[0] = int(lo[0]); r[1] = int(lo[1]); r[2] = int(lo[2]); r[3] = int(lo[3]);
+  if (WF == 0) {
+    const v4u hi = ldg16(tile_lane + 1024);
+    r[4] = int(hi[0]); r[5] = int(hi[1]); r[6] = int(hi[2]); r[7] = int(hi[3]);
+  } else {
+    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  }
+  return r;
+}
+
 // Keep only the bytes of 32-wide K block `blk` in an e4m3 fragment (used
 // when the weight scales change every 32 along K): block blk lives in lane
 // groups with (g >> 1) == (blk & 1), in byte half (blk >> 1).

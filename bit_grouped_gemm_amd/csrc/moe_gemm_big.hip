@@ -11,10 +11,11 @@
 //     stages (three for MXFP4 weights, two for e4m3 weights whose steps are
 //     twice as large), so two steps of weights and token rows are in
 //     flight while one is multiplied;
-//   * in LDS every 16-row x 128-K operand tile is stored in the lane order
-//     of the scaled-MFMA fragment (lane l's 16 bytes at l * 16 of a 1 KB
-//     block), so fragment reads are linear ds_read_b128 with no bank
-//     conflicts and the address permutation is paid on the global side;
+//   * weights come from the tiled layout (16-row x 128-K tiles in MFMA lane
+//     order, see moe_tile.hip), one contiguous kilobyte per tile and step,
+//     and land in LDS unchanged, so fragment reads are linear ds_read_b128;
+//     token rows travel as whole 128-byte lines into a chunk-swizzled layout
+//     whose fragment reads are conflict-free as well;
 //   * the 8 waves form a 4 x 2 grid: a wave owns 4 weight tiles (64 rows;
 //     in GEMM1 two gate and the two matching up tiles, so SwiGLU pairs meet
 //     in one lane) and every second token tile, which keeps up to 4 x 6
@@ -181,16 +182,19 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
   // rows, 8..15 the up rows of the same h columns; GEMM2 rows in order
   auto wtile_row = [&](int j) { return MODE == 0 ? (j < 8 ? n0 + 16 * j : I + n0 + 16 * (j - 8)) : n0 + 16 * j; };
 
-  // ---- loader side: this lane's sources for the weight tiles of wave w
-  // (tiles 2w, 2w+1; e4m3: both K halves of each) and the MXFP4 scales
+  // ---- loader side: this lane's sources in the tiled weights for the tiles
+  // of wave w (tiles 2w, 2w+1: one contiguous kilobyte each, two for e4m3)
+  // and their MXFP4 scales (the two tiles' 128 bytes are adjacent; lanes
+  // 32..63 repeat lanes 0..31)
+  const long wstep = long(NR / 16) * kTileBytes<WF>;       // bytes per K step
+  const long sstep = long(NR / 16) * kTileScaleBytes;
   const uint8_t* a_src[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) a_src[q] = wmat + long(wtile_row(2 * w + q) + m) * kb + 16 * g;
+  for (int q = 0; q < 2; ++q) a_src[q] = wmat + long(wtile_row(2 * w + q) / 16) * kTileBytes<WF> + lane * 16;
   const uint8_t* as_src = nullptr;
-  if (WF == 1) {
-    const int jt = 2 * w + (lane >> 5);
-    as_src = static_cast<const uint8_t*>(smat) + ee * long(NR) * (K / 32) + long(wtile_row(jt) + m) * (K / 32);
-  }
+  if (WF == 1)
+    as_src = static_cast<const uint8_t*>(smat) + ee * long(NR) * (K / 32) +
+             long(wtile_row(2 * w) / 16) * kTileScaleBytes + (lane & 31) * 4;
   // ---- consumer side: this wave's weight tiles
   int ja[4];
 #pragma unroll
@@ -240,16 +244,16 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
         dma4(xs_src + ks, st + Geo::kXsOff + w * 256);
         if (WF == 1) {
 #pragma unroll
-          for (int q = 0; q < 2; ++q) dma16(a_src[q] + long(ks) * 64, st + Geo::kAOff + (2 * w + q) * 1024);
+          for (int q = 0; q < 2; ++q) dma16(a_src[q] + ks * wstep, st + Geo::kAOff + (2 * w + q) * 1024);
         } else {
 #pragma unroll
           for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-              dma16(a_src[q] + long(ks) * 128 + 64 * h, st + Geo::kAOff + (2 * (2 * w + q) + h) * 1024);
+              dma16(a_src[q] + ks * wstep + 1024 * h, st + Geo::kAOff + (2 * (2 * w + q) + h) * 1024);
         }
       } else if (part == 1) {
-        if (WF == 1) dma4(as_src + ks * 4, st + Geo::kAsOff + w * 256);
+        if (WF == 1) dma4(as_src + ks * sstep, st + Geo::kAsOff + w * 256);
         dma16(b_src[0] + long(ks) * 128, st + b_dst[0]);
       } else {
         dma16(b_src[1] + long(ks) * 128, st + b_dst[1]);
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
         if (WF == 1) {
           const v4u a = *reinterpret_cast<const v4u*>(st + Geo::kAOff + ja[q] * 1024 + lane * 16);
           af[q] = v8i{int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
-          sa[q] = st[Geo::kAsOff + ((ja[q] >> 1) * 64 + (ja[q] & 1) * 32 + m) * 4 + g];
+          sa[q] = st[Geo::kAsOff + (ja[q] >> 1) * 256 + (ja[q] & 1) * kTileScaleBytes + lane];
           wsv[q] = 1.0f;
         } else {
           const v4u lo = *reinterpret_cast<const v4u*>(st + Geo::kAOff + (2 * ja[q]) * 1024 + lane * 16);

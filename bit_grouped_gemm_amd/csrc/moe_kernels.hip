@@ -232,19 +232,21 @@ struct Frag {
   float xsv[NTT];  // activation scale of this lane's token column
 };
 
+// wtile[j]: this lane's bytes in weight tile j of K step 0 (tiled layout);
+// wstep: bytes between K steps of the tiled tensor; wsb[j] / sstep: the same
+// for the MXFP4 scale tiles
 template <int WF, int NJ, int NTT, int B32>
-__device__ __forceinline__ void load_frag(Frag<WF, NJ, NTT>& f, const uint8_t* const (&wrow)[NJ],
+__device__ __forceinline__ void load_frag(Frag<WF, NJ, NTT>& f, const uint8_t* const (&wtile)[NJ],
                                           const float* const (&wsc)[NJ], const uint8_t* const (&wsb)[NJ],
                                           const uint8_t* const (&brow)[NTT], const float* const (&bsc)[NTT],
-                                          int ks, int g) {
+                                          int ks, int g, long wstep, long sstep) {
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
+    f.a[j] = load_tile_frag<WF>(wtile[j] + ks * wstep);
     if (WF == 0) {
-      f.a[j] = load_e4m3_frag(wrow[j] + ks * 128, g);
       if (!B32) f.wsc[j] = wsc[j][ks];
     } else {
-      f.a[j] = load_e2m1_frag(wrow[j] + ks * 64, g);
-      f.wsb[j] = wsb[j][ks * 4 + g];
+      f.wsb[j] = wsb[j][ks * sstep];
     }
   }
 #pragma unroll
@@ -301,20 +303,21 @@ __device__ __forceinline__ void mma_frag(v4f (&acc)[NJ][NTT], const Frag<WF, NJ,
 // hit in cache) so the compiler can count outstanding loads exactly and
 // wait only for the stage about to be used; only the MFMAs are predicated.
 template <int WF, int NJ, int NTT, int B32, int ST>
-__device__ __forceinline__ void kloop(v4f (&acc)[NJ][NTT], const uint8_t* const (&wrow)[NJ],
+__device__ __forceinline__ void kloop(v4f (&acc)[NJ][NTT], const uint8_t* const (&wtile)[NJ],
                                       const float* const (&wsc)[NJ], const uint8_t* const (&wsb)[NJ],
                                       const uint8_t* const (&brow)[NTT], const float* const (&bsc)[NTT],
-                                      int ks0, int ks1, int g) {
+                                      int ks0, int ks1, int g, long wstep, long sstep) {
   Frag<WF, NJ, NTT> f[ST];
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s) {
-    load_frag<WF, NJ, NTT, B32>(f[s], wrow, wsc, wsb, brow, bsc, min(ks0 + s, ks1 - 1), g);
+    load_frag<WF, NJ, NTT, B32>(f[s], wtile, wsc, wsb, brow, bsc, min(ks0 + s, ks1 - 1), g, wstep, sstep);
     __builtin_amdgcn_sched_barrier(0);  // keep each stage's loads together, in stage order
   }
   for (int ks = ks0; ks < ks1; ks += ST) {
 #pragma unroll
     for (int s = 0; s < ST; ++s) {
-      load_frag<WF, NJ, NTT, B32>(f[(s + ST - 1) % ST], wrow, wsc, wsb, brow, bsc, min(ks + s + ST - 1, ks1 - 1), g);
+      load_frag<WF, NJ, NTT, B32>(f[(s + ST - 1) % ST], wtile, wsc, wsb, brow, bsc, min(ks + s + ST - 1, ks1 - 1), g,
+                                  wstep, sstep);
       __builtin_amdgcn_sched_barrier(0);
       if (ks + s < ks1) mma_frag<WF, NJ, NTT, B32>(acc, f[s], wsc, bsc, ks + s, g);
       __builtin_amdgcn_sched_barrier(0);
@@ -452,13 +455,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
   const long ee = shared ? 0 : e;
   const long kbytes = WF == 0 ? H : H / 2;
   const uint8_t* wbase = (shared ? p.sw : p.w) + ee * 2L * I * kbytes;
-  const uint8_t* wrow[4];
+  const long wstep = long(2 * I / 16) * kTileBytes<WF>, sstep = long(2 * I / 16) * kTileScaleBytes;
+  const uint8_t* wtile[4];
   const float* wsc[4];
   const uint8_t* wsb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int rb = (j < 2) ? (n0 + 32 * w + 16 * j) : (I + n0 + 32 * w + 16 * (j - 2));
-    wrow[j] = wbase + long(rb + m) * kbytes;
+    wtile[j] = wbase + long(rb / 16) * kTileBytes<WF> + lane * 16;
     if (WF == 0) {
       const int b = p.wblk;
       const float* sb = static_cast<const float*>(shared ? p.sws : p.ws) + ee * long(2 * I / b) * (H / b);
@@ -466,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
       wsb[j] = nullptr;
     } else {
       const uint8_t* sb = static_cast<const uint8_t*>(shared ? p.sws : p.ws) + ee * 2L * I * (H / 32);
-      wsb[j] = sb + long(rb + m) * (H / 32);
+      wsb[j] = sb + long(rb / 16) * kTileScaleBytes + lane;
       wsc[j] = nullptr;
     }
   }
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int t = 0; t < NTT; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    kloop<WF, 4, NTT, B32, kStages>(acc, wrow, wsc, wsb, brow, bsc, ks0, ks1, g);
+    kloop<WF, 4, NTT, B32, kStages>(acc, wtile, wsc, wsb, brow, bsc, ks0, ks1, g, wstep, sstep);
     if (S == 1) {
       swiglu_requant_store<NTT>(acc, p, row0, ne, pass, n0, s_red);
     } else {
@@ -544,13 +548,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
   const long ee = shared ? 0 : e;
   const long kbytes = WF == 0 ? I : I / 2;
   const uint8_t* wbase = (shared ? p.sw : p.w) + ee * long(H) * kbytes;
-  const uint8_t* wrow[2];
+  const long wstep = long(H / 16) * kTileBytes<WF>, sstep = long(H / 16) * kTileScaleBytes;
+  const uint8_t* wtile[2];
   const float* wsc[2];
   const uint8_t* wsb[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int rb = n0 + 32 * w + 16 * j;
-    wrow[j] = wbase + long(rb + m) * kbytes;
+    wtile[j] = wbase + long(rb / 16) * kTileBytes<WF> + lane * 16;
     if (WF == 0) {
       const int b = p.wblk;
       const float* sb = static_cast<const float*>(shared ? p.sws : p.ws) + ee * long(H / b) * (I / b);
@@ -558,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
       wsb[j] = nullptr;
     } else {
       const uint8_t* sb = static_cast<const uint8_t*>(shared ? p.sws : p.ws) + ee * long(H) * (I / 32);
-      wsb[j] = sb + long(rb + m) * (I / 32);
+      wsb[j] = sb + long(rb / 16) * kTileScaleBytes + lane;
       wsc[j] = nullptr;
     }
   }
@@ -578,7 +583,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int t = 0; t < NTT; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    kloop<WF, 2, NTT, B32, kStages>(acc, wrow, wsc, wsb, brow, bsc, ks0, ks1, g);
+    kloop<WF, 2, NTT, B32, kStages>(acc, wtile, wsc, wsb, brow, bsc, ks0, ks1, g, wstep, sstep);
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
       const int idx = pass * 16 * NTT + t * 16 + m;

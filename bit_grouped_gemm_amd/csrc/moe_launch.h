@@ -65,6 +65,9 @@ hipError_t launch_gemm1_big(const Shape& s, const uint8_t* xq, const float* xs, 
 hipError_t launch_gemm2_big(const Shape& s, const uint8_t* hq, const float* hs, const int32_t* offsets,
                             WeightPtrs w2, float* y, int min_rows, hipStream_t st);
 
+hipError_t launch_tile_weights(int wfmt, int mats, int N, int K, const uint8_t* w, const uint8_t* s, uint8_t* w_tiled,
+                               uint8_t* s_tiled, hipStream_t st);
+
 hipError_t launch_combine(const Shape& s, const float* y, const int32_t* expand_idx, const int32_t* offsets,
                           const float* topk_w, uint16_t* out, hipStream_t st);
 

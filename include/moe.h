@@ -82,12 +82,15 @@ typedef struct moe_cfg {
   int32_t has_shared;
 } moe_cfg;
 
-/* Expert weights in canonical row-major layout (host struct of device
- * pointers).  FP8:   w1 uint8 [E][2I][H] (rows 0..I-1 gate, I..2I-1 up, K
- * contiguous), w1s float [E][2I/wblk][H/wblk]; w2 uint8 [E][H][I], w2s float
- * [E][H/wblk][I/wblk].  MXFP4: w1 uint8 [E][2I][H/2], w1s uint8 [E][2I][H/32];
- * w2 uint8 [E][H][I/2], w2s uint8 [E][H][I/32].  sw1..sw2s: the shared
- * expert with a leading dimension of 1 (may be NULL when has_shared == 0). */
+/* Expert weights (host struct of device pointers) as the GEMM entry points
+ * read them: codes and MXFP4 scales in the TILED layout written by
+ * moe_tile_weights from the row-major tensors below; e4m3 block scales stay
+ * row-major.  Row-major tensors -- FP8: w1 uint8 [E][2I][H] (rows 0..I-1
+ * gate, I..2I-1 up, K contiguous), w1s float [E][2I/wblk][H/wblk]; w2 uint8
+ * [E][H][I], w2s float [E][H/wblk][I/wblk].  MXFP4: w1 uint8 [E][2I][H/2],
+ * w1s uint8 [E][2I][H/32]; w2 uint8 [E][H][I/2], w2s uint8 [E][H][I/32].
+ * The tiled tensors have the same sizes.  sw1..sw2s: the shared expert with
+ * a leading dimension of 1 (may be NULL when has_shared == 0). */
 typedef struct moe_weights {
   const void *w1, *w1s, *w2, *w2s;
   const void *sw1, *sw1s, *sw2, *sw2s;
@@ -152,6 +155,28 @@ int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* expand_idx, c
  *   out bf16 [T][H]; ws of at least moe_workspace_size(cfg) bytes. */
 int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
               const moe_weights* w, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Reorders one row-major expert weight tensor of `mats` matrices [N][K]
+ * (and, for MXFP4, its e8m0 scales [mats][N][K/32]) into the tiled layout
+ * the grouped GEMMs stream: a one-time step when weights are loaded, as the
+ * FusedDeepMoE family analysis keeps its GMM weights in the matrix unit's
+ * blocked (zN) layout and hands the framework entry permuted GMM1 weights
+ * (GMM type definitions; FWK kernel entry).  Tile (k step
+ * ks, row tile rt) = rows 16 rt..16 rt+15 x K 128 ks..128 ks+127, stored at
+ * ((m * K/128 + ks) * N/16 + rt) * B with B = 2048 (e4m3) or 1024 (e2m1)
+ * bytes, in the lane order of the gfx950 scaled MFMA operand: byte l*16+i
+ * (l < 64, i < 16) is row-major byte (16 (l/16) + i) of row 16 rt + l%16 in
+ * the step's K chunk (128 bytes for e4m3, 64 for e2m1), and for e4m3 byte
+ * 1024 + l*16 + i is row-major byte 64 + 16 (l/16) + i of that chunk.
+ * MXFP4 scales: 64 bytes per tile in the same order, byte l = scale of row
+ * 16 rt + l%16 and 32-block 4 ks + l/16.  e4m3 block scales are not
+ * touched (s, s_tiled are ignored and may be NULL).
+ *   wfmt     MOE_WFMT_FP8_BLOCK or MOE_WFMT_MXFP4
+ *   mats, N, K  matrix count, rows, reduction length (N % 16 == 0, K % 128 == 0)
+ *   w, w_tiled  uint8 codes, row-major in, tiled out (distinct buffers)
+ *   s, s_tiled  MXFP4 scales, row-major in, tiled out (distinct buffers) */
+int moe_tile_weights(int32_t wfmt, int32_t mats, int32_t N, int32_t K, const void* w, const void* s,
+                     void* w_tiled, void* s_tiled, void* stream);
 
 /* Static description of an error code (host only). */
 const char* moe_status_str(int status);

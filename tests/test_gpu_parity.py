@@ -64,13 +64,18 @@ _WCACHE = {}
 
 
 def weights_for(wl, seed=0):
+    """(weights tiled on the GPU for the library, row-major weights on the CPU
+    for the oracle)."""
     key = (wl, seed)
     if key not in _WCACHE:
         if len(_WCACHE) > 3:
             _WCACHE.clear()
             torch.cuda.empty_cache()
         w = synth.gen_weights(wl, seed=seed, device=DEV)
-        _WCACHE[key] = (w, w.to("cpu"))
+        moe = M()
+        wt = moe.tile_weights(moe.Cfg.for_workload(wl, 1), w)
+        _WCACHE[key] = (wt, w.to("cpu"))
+        del w
     return _WCACHE[key]
 
 
@@ -93,6 +98,40 @@ def run_permute(wl, T, x, ids):
     outs = moe.moe_permute(cfg, x, ids)
     torch.cuda.synchronize()
     return [o.cpu().numpy() for o in outs]
+
+
+# ------------------------------------------------------------------ tiled weights
+def _tile_ref(wfmt, w, s):
+    """The tiled layout written out with numpy reshapes: tile (k step, row tile)
+    holds lane l = 16 g + m's 16 bytes (row m, K group g) at l * 16; e4m3 tiles
+    keep K 64..127 of the step in a second kilobyte; MXFP4 scale byte l is
+    (row m, 32-block g)."""
+    mats, N, KB = w.shape
+    nrt = N // 16
+    if wfmt == 0:
+        nks = KB // 128
+        wt = w.reshape(mats, nrt, 16, nks, 2, 4, 16).transpose(0, 3, 1, 4, 5, 2, 6)
+        return wt.reshape(mats, N, KB), s
+    nks = KB // 64
+    wt = w.reshape(mats, nrt, 16, nks, 4, 16).transpose(0, 3, 1, 4, 2, 5).reshape(mats, N, KB)
+    st = s.reshape(mats, nrt, 16, nks, 4).transpose(0, 3, 1, 4, 2).reshape(s.shape)
+    return wt, st
+
+
+@pytest.mark.parametrize("wfmt,mats,N,K", [(0, 2, 48, 256), (1, 2, 48, 384), (1, 1, 16, 128), (0, 3, 32, 128)])
+def test_tile_weights_bitexact(wfmt, mats, N, K):
+    moe = M()
+    _note(f"tile wfmt={wfmt} mats={mats} N={N} K={K}")
+    g = torch.Generator().manual_seed(mats * 1000 + N + K)
+    kb = K if wfmt == 0 else K // 2
+    w = torch.randint(0, 256, (mats, N, kb), generator=g, dtype=torch.uint8)
+    s = (torch.randint(0, 256, (mats, N, K // 32), generator=g, dtype=torch.uint8) if wfmt == 1
+         else torch.rand(mats, N // 32 if N % 32 == 0 else 1, K // 32, generator=g))
+    wt, st = moe.moe_tile_weights(wfmt, w.to(DEV), s.to(DEV))
+    torch.cuda.synchronize()
+    rw, rs = _tile_ref(wfmt, w.numpy(), s.numpy())
+    assert np.array_equal(wt.cpu().numpy(), rw)
+    assert np.array_equal(st.cpu().numpy(), rs)
 
 
 # ------------------------------------------------------------------ permute + quant
@@ -434,7 +473,7 @@ def test_worked_examples_on_gpu():
         wl, wc, x, ids, tw = pins._golden_case(ex)
         T = x.shape[0]
         cfg = moe.Cfg.for_workload(wl, T)
-        out = moe.moe_layer(cfg, x.to(DEV), ids.to(DEV), tw.to(DEV), wc.to(DEV))
+        out = moe.moe_layer(cfg, x.to(DEV), ids.to(DEV), tw.to(DEV), moe.tile_weights(cfg, wc.to(DEV)))
         torch.cuda.synchronize()
         got = out.float().cpu().numpy()
         for t in range(T):
