@@ -56,12 +56,18 @@ __device__ void permute_block(const RouteParams& p) {
   // each wave owns one contiguous, 64-aligned range of flat slots
   const int per = ((n + 4 * 64 - 1) / (4 * 64)) * 64;
   const int i0 = min(n, w * per), i1 = min(n, i0 + per);
-  for (int base = i0; base < i1; base += 64) {
-    const int i = base + lane;
-    if (i < i1) {
-      const int e = p.ids[i];
-      if (e >= 0 && e < E) atomicAdd(&cnt[w][e], 1);
+  // ids are read kBatch rounds of 64 at a time so the loads overlap
+  constexpr int kBatch = 8;
+  for (int base = i0; base < i1; base += 64 * kBatch) {
+    int eb[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int i = base + q * 64 + lane;
+      eb[q] = i < i1 ? p.ids[i] : -1;
     }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+      if (eb[q] >= 0 && eb[q] < E) atomicAdd(&cnt[w][eb[q]], 1);
   }
   __syncthreads();
   // totals per expert and their exclusive scan (thread tid owns a contiguous
@@ -112,9 +118,18 @@ __device__ void permute_block(const RouteParams& p) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  for (int base = i0; base < i1; base += 64) {
+  for (int base0 = i0; base0 < i1; base0 += 64 * kBatch) {
+   int eb[kBatch];
+#pragma unroll
+   for (int q = 0; q < kBatch; ++q) {
+     const int i = base0 + q * 64 + lane;
+     eb[q] = i < i1 ? p.ids[i] : -1;
+   }
+   for (int q = 0; q < kBatch; ++q) {
+    const int base = base0 + q * 64;
+    if (base >= i1) break;
     const int i = base + lane;
-    const int e = i < i1 ? p.ids[i] : -1;
+    const int e = eb[q];
     const bool valid = i < i1 && e >= 0 && e < E;
     uint64_t match = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
@@ -131,6 +146,7 @@ __device__ void permute_block(const RouteParams& p) {
       p.expand_idx[i] = row;
       if (valid) p.row_token[row] = i / p.k;
     }
+   }
   }
   if (p.shared)
     for (int t = tid; t < p.T; t += kThreads) p.row_token[R0 + t] = t;
@@ -624,29 +640,46 @@ struct CombineParams {
   int H, k, E, shared;
 };
 
+// One workgroup per (token, 1024 channels), four channels per thread.  The
+// k slot rows are loaded in unrolled batches of 8 with no branch between the
+// loads, so a thread has up to 8 loads in flight; masked slots read a valid
+// row of the token with weight 0, whose product is an exact zero and leaves
+// the ascending-order fp32 sum unchanged.
+constexpr int kCombineChunk = kThreads * 4;
+
 __global__ __launch_bounds__(kThreads) void k_combine(CombineParams p) {
-  const long t = blockIdx.x;
-  __shared__ int s_row[33];
-  __shared__ float s_w[33];
-  if (threadIdx.x < p.k) {
-    s_row[threadIdx.x] = p.expand_idx[t * p.k + threadIdx.x];
-    s_w[threadIdx.x] = p.tw[t * p.k + threadIdx.x];
-  }
-  if (threadIdx.x == 0) s_row[32] = p.shared ? p.offsets[p.E] + int(t) : -1;
-  __syncthreads();
-  for (int c = threadIdx.x * 4; c < p.H; c += kThreads * 4) {
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j = 0; j < p.k; ++j) {
-      const int r = s_row[j];
-      if (r < 0) continue;
-      acc += s_w[j] * *reinterpret_cast<const v4f*>(p.y + long(r) * p.H + c);
+  const int nchunk = (p.H + kCombineChunk - 1) / kCombineChunk;
+  const long t = blockIdx.x / nchunk;
+  const int c = (blockIdx.x % nchunk) * kCombineChunk + threadIdx.x * 4;
+  const int k = p.k;
+  const int* ids = p.expand_idx + t * k;
+  const float* tw = p.tw + t * k;
+  const int srow = p.shared ? p.offsets[p.E] + int(t) : -1;
+  int pad = srow;  // a valid row to stand in for masked slots
+  for (int j = k - 1; j >= 0; --j)
+    if (ids[j] >= 0) pad = ids[j];
+  if (c >= p.H) return;
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (pad >= 0) {
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      v4f v[8];
+      float wj[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = j0 + jj;
+        const int r = j < k ? ids[j] : -1;
+        wj[jj] = r >= 0 ? tw[j] : 0.0f;
+        v[jj] = *reinterpret_cast<const v4f*>(p.y + long(r >= 0 ? r : pad) * p.H + c);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) acc += wj[jj] * v[jj];
     }
-    if (s_row[32] >= 0) acc += *reinterpret_cast<const v4f*>(p.y + long(s_row[32]) * p.H + c);
-    uint2 o;
-    o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-    o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-    *reinterpret_cast<uint2*>(p.out + t * p.H + c) = o;
+    if (srow >= 0) acc += *reinterpret_cast<const v4f*>(p.y + long(srow) * p.H + c);
   }
+  uint2 o;
+  o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+  o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+  *reinterpret_cast<uint2*>(p.out + t * p.H + c) = o;
 }
 
 // =====================================================================
@@ -723,7 +756,8 @@ hipError_t launch_combine(const Shape& s, const float* y, const int32_t* expand_
                           const float* topk_w, uint16_t* out, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   CombineParams p{y, expand_idx, offsets, topk_w, out, s.H, s.k, s.E, s.shared};
-  hipLaunchKernelGGL(k_combine, dim3(unsigned(s.T)), dim3(kThreads), 0, st, p);
+  const long grid = long(s.T) * ((s.H + kCombineChunk - 1) / kCombineChunk);
+  hipLaunchKernelGGL(k_combine, dim3(unsigned(grid)), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
