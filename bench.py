@@ -98,7 +98,7 @@ def main():
     t0 = time.time()
     w_rowmajor = synth.gen_weights(wl, seed=0, device=dev)
     # one-time reorder into the tiled layout the GEMMs read (weight load time, not timed)
-    w = moe.tile_weights(moe.Cfg.for_workload(wl, 1), w_rowmajor)
+    w = moe.moe_prepack_weights(moe.Cfg.for_workload(wl, 1), w_rowmajor)
     cases = {}
     for T in Ts:
         x, ids, tw = synth.gen_inputs(wl, T, seed=0, device=dev)

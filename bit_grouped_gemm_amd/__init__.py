@@ -12,10 +12,11 @@ Entry points (same names as the C ABI):
     moe_grouped_gemm2(cfg, hq, hs, offsets, weights, ws) -> y
     moe_combine(cfg, y, expand_idx, offsets, topk_weights) -> out
     moe_layer(cfg, x, topk_ids, topk_weights, weights, ws=None, out=None) -> out
-    moe_tile_weights(wfmt, w, s=None) -> (w_tiled, s_tiled)
+    moe_prepack_weights(cfg, weights) -> TiledWeights
 
 The GEMM entry points read expert weights in the tiled layout: convert the
-row-major tensors once with tile_weights(cfg, weights).
+canonical row-major tensors once with moe_prepack_weights(cfg, weights)
+(a one-time step at weight load).
 """
 from __future__ import annotations
 
@@ -41,7 +42,7 @@ WFMT_FP8_BLOCK = 0
 WFMT_MXFP4 = 1
 
 EXPORTS = ("moe_workspace_size", "moe_permute", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm2",
-           "moe_combine", "moe_layer", "moe_tile_weights", "moe_status_str")
+           "moe_combine", "moe_layer", "moe_prepack_weights", "moe_status_str")
 
 
 class MoeCfg(C.Structure):
@@ -80,8 +81,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     L.moe_grouped_gemm2.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp]
     L.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
     L.moe_layer.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp]
-    i32 = C.c_int32
-    L.moe_tile_weights.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    L.moe_prepack_weights.argtypes = [cfgp, wp, wp, vp]
     L.moe_status_str.argtypes = [C.c_int]
     L.moe_status_str.restype = C.c_char_p
     for n in EXPORTS:
@@ -221,20 +221,6 @@ def moe_layer(cfg: Cfg, x, topk_ids, topk_weights, weights, ws: Optional[torch.T
     return out
 
 
-def moe_tile_weights(wfmt: int, w: torch.Tensor, s: Optional[torch.Tensor] = None):
-    """Tiled copies of a row-major expert weight tensor w ([mats][N][K] codes,
-    K halved for MXFP4) and, for MXFP4, its scales s ([mats][N][K/32]).
-    e4m3 block scales keep their layout: s is returned as given."""
-    mats, N = w.shape[0], w.shape[1]
-    K = w.shape[2] * (2 if wfmt == WFMT_MXFP4 else 1)
-    wt = torch.empty_like(w)
-    st = torch.empty_like(s) if (wfmt == WFMT_MXFP4 and s is not None) else None
-    _check("moe_tile_weights", load().moe_tile_weights(wfmt, mats, N, K, _ptr(w),
-                                                       _ptr(s) if wfmt == WFMT_MXFP4 else None, _ptr(wt),
-                                                       _ptr(st), _stream()))
-    return wt, (st if wfmt == WFMT_MXFP4 else s)
-
-
 @dataclasses.dataclass
 class TiledWeights:
     """Expert weights in the layout the GEMM entry points read."""
@@ -248,17 +234,17 @@ class TiledWeights:
     sw2s: Optional[torch.Tensor] = None
 
 
-def tile_weights(cfg: Cfg, weights) -> TiledWeights:
-    """Tile every weight tensor of a layer (row-major w1, w1s, w2, w2s and the
-    shared expert's sw1..sw2s when cfg.has_shared) once, at load time."""
-    f = cfg.wfmt
-    w1, w1s = moe_tile_weights(f, weights.w1, weights.w1s)
-    w2, w2s = moe_tile_weights(f, weights.w2, weights.w2s)
-    out = TiledWeights(w1, w1s, w2, w2s)
-    if cfg.has_shared:
-        out.sw1, out.sw1s = moe_tile_weights(f, weights.sw1, weights.sw1s)
-        out.sw2, out.sw2s = moe_tile_weights(f, weights.sw2, weights.sw2s)
+def moe_prepack_weights(cfg: Cfg, weights) -> TiledWeights:
+    """Tiled copies of a layer's canonical row-major weights (w1, w1s, w2, w2s
+    and, when cfg.has_shared, sw1..sw2s): the one-time step at weight load."""
+    names = ["w1", "w1s", "w2", "w2s"] + (["sw1", "sw1s", "sw2", "sw2s"] if cfg.has_shared else [])
+    out = TiledWeights(**{n: torch.empty_like(getattr(weights, n)) for n in names})
+    c, src, dst = cfg.c(), weights_struct(weights), weights_struct(out)
+    _check("moe_prepack_weights", load().moe_prepack_weights(C.byref(c), C.byref(src), C.byref(dst), _stream()))
     return out
+
+
+
 
 
 def raw_call(name: str, *args) -> int:

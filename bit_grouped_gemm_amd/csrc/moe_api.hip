@@ -306,18 +306,37 @@ int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, co
   return hip_status(launch_combine(s, y, eidx, offsets, topk_weights, out, st));
 }
 
-int moe_tile_weights(int32_t wfmt, int32_t mats, int32_t N, int32_t K, const void* w, const void* s, void* w_tiled,
-                     void* s_tiled, void* stream) {
-  if (wfmt != MOE_WFMT_FP8_BLOCK && wfmt != MOE_WFMT_MXFP4) return MOE_ERR_UNSUPPORTED;
-  if (mats < 0 || N < 0 || K < 0 || N % 16 || K % 128) return MOE_ERR_BAD_SHAPE;
-  const bool any = int64_t(mats) * N * K > 0, mx = wfmt == MOE_WFMT_MXFP4;
-  int rc = check_ptrs({{w, any}, {w_tiled, any}, {s, any && mx}, {s_tiled, any && mx}});
+int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_weights* packed, void* stream) {
+  int rc = check_cfg(cfg);
   if (rc) return rc;
-  if (!any) return MOE_OK;
-  if (w == w_tiled || (mx && s == s_tiled)) return MOE_ERR_UNSUPPORTED;  // not in place
-  return hip_status(launch_tile_weights(wfmt, mats, N, K, static_cast<const uint8_t*>(w),
-                                        static_cast<const uint8_t*>(s), static_cast<uint8_t*>(w_tiled),
-                                        static_cast<uint8_t*>(s_tiled), static_cast<hipStream_t>(stream)));
+  if ((rc = check_weights(cfg, canonical))) return rc;
+  if (!packed) return MOE_ERR_NULL_ARG;
+  if ((rc = check_weights(cfg, packed))) return rc;
+  const moe_cfg& c = *cfg;
+  const bool mx = c.wfmt == MOE_WFMT_MXFP4;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // (codes, scales, matrices, rows N, reduction K) of each tensor pair
+  struct Pair { const void *w, *s; void *wt, *stl; int mats, N, K; };
+  Pair pairs[4] = {
+      {canonical->w1, canonical->w1s, const_cast<void*>(packed->w1), const_cast<void*>(packed->w1s), c.E, 2 * c.I, c.H},
+      {canonical->w2, canonical->w2s, const_cast<void*>(packed->w2), const_cast<void*>(packed->w2s), c.E, c.H, c.I},
+      {canonical->sw1, canonical->sw1s, const_cast<void*>(packed->sw1), const_cast<void*>(packed->sw1s), 1, 2 * c.I, c.H},
+      {canonical->sw2, canonical->sw2s, const_cast<void*>(packed->sw2), const_cast<void*>(packed->sw2s), 1, c.H, c.I}};
+  const int np = c.has_shared ? 4 : 2;
+  for (int i = 0; i < np; ++i)  // not in place
+    if (pairs[i].w == pairs[i].wt || (mx && pairs[i].s == pairs[i].stl)) return MOE_ERR_UNSUPPORTED;
+  for (int i = 0; i < np; ++i) {
+    const Pair& q = pairs[i];
+    if ((rc = hip_status(launch_tile_weights(c.wfmt, q.mats, q.N, q.K, static_cast<const uint8_t*>(q.w),
+                                             static_cast<const uint8_t*>(q.s), static_cast<uint8_t*>(q.wt),
+                                             static_cast<uint8_t*>(q.stl), st))))
+      return rc;
+    if (!mx && q.s != q.stl) {  // e4m3 block scales keep their layout
+      const size_t sb = size_t(q.mats) * (q.N / c.wblk) * (q.K / c.wblk) * sizeof(float);
+      if ((rc = hip_status(hipMemcpyAsync(q.stl, q.s, sb, hipMemcpyDeviceToDevice, st)))) return rc;
+    }
+  }
+  return MOE_OK;
 }
 
 const char* moe_status_str(int status) {

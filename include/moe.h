@@ -84,8 +84,8 @@ typedef struct moe_cfg {
 
 /* Expert weights (host struct of device pointers) as the GEMM entry points
  * read them: codes and MXFP4 scales in the TILED layout written by
- * moe_tile_weights from the row-major tensors below; e4m3 block scales stay
- * row-major.  Row-major tensors -- FP8: w1 uint8 [E][2I][H] (rows 0..I-1
+ * moe_prepack_weights from the canonical row-major tensors below; e4m3
+ * block scales stay row-major.  Row-major tensors -- FP8: w1 uint8 [E][2I][H] (rows 0..I-1
  * gate, I..2I-1 up, K contiguous), w1s float [E][2I/wblk][H/wblk]; w2 uint8
  * [E][H][I], w2s float [E][H/wblk][I/wblk].  MXFP4: w1 uint8 [E][2I][H/2],
  * w1s uint8 [E][2I][H/32]; w2 uint8 [E][H][I/2], w2s uint8 [E][H][I/32].
@@ -156,27 +156,29 @@ int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* expand_idx, c
 int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
               const moe_weights* w, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
-/* Reorders one row-major expert weight tensor of `mats` matrices [N][K]
- * (and, for MXFP4, its e8m0 scales [mats][N][K/32]) into the tiled layout
- * the grouped GEMMs stream: a one-time step when weights are loaded, as the
- * FusedDeepMoE family analysis keeps its GMM weights in the matrix unit's
- * blocked (zN) layout and hands the framework entry permuted GMM1 weights
- * (GMM type definitions; FWK kernel entry).  Tile (k step
- * ks, row tile rt) = rows 16 rt..16 rt+15 x K 128 ks..128 ks+127, stored at
+/* One-time re-layout of a layer's expert weights (canonical row-major, as
+ * above) into the tiled layout the GEMM entry points read -- the step a
+ * caller runs when weights are loaded, as the FusedDeepMoE family analysis
+ * keeps its GMM weights in the matrix unit's blocked (zN) layout and hands
+ * the framework entry permuted GMM1 weights (GMM type definitions; FWK
+ * kernel entry).  Every tensor of `canonical` is read and the matching one
+ * of `packed` written (w1, w1s, w2, w2s, and sw1..sw2s when has_shared);
+ * `packed` holds buffers of the canonical sizes, distinct from the
+ * canonical ones (MOE_ERR_UNSUPPORTED otherwise).  Only cfg's E, H, I,
+ * wfmt, wblk and has_shared matter (the rest must still be valid).
+ *
+ * Tiled layout of a [mats][N][K] tensor: tile (k step ks, row tile rt) =
+ * rows 16 rt..16 rt+15 x K 128 ks..128 ks+127, stored at
  * ((m * K/128 + ks) * N/16 + rt) * B with B = 2048 (e4m3) or 1024 (e2m1)
- * bytes, in the lane order of the gfx950 scaled MFMA operand: byte l*16+i
- * (l < 64, i < 16) is row-major byte (16 (l/16) + i) of row 16 rt + l%16 in
+ * bytes, in the lane order of the gfx950 scaled-MFMA operand: byte l*16+i
+ * (l < 64, i < 16) is row-major byte 16 (l/16) + i of row 16 rt + l%16 in
  * the step's K chunk (128 bytes for e4m3, 64 for e2m1), and for e4m3 byte
  * 1024 + l*16 + i is row-major byte 64 + 16 (l/16) + i of that chunk.
  * MXFP4 scales: 64 bytes per tile in the same order, byte l = scale of row
- * 16 rt + l%16 and 32-block 4 ks + l/16.  e4m3 block scales are not
- * touched (s, s_tiled are ignored and may be NULL).
- *   wfmt     MOE_WFMT_FP8_BLOCK or MOE_WFMT_MXFP4
- *   mats, N, K  matrix count, rows, reduction length (N % 16 == 0, K % 128 == 0)
- *   w, w_tiled  uint8 codes, row-major in, tiled out (distinct buffers)
- *   s, s_tiled  MXFP4 scales, row-major in, tiled out (distinct buffers) */
-int moe_tile_weights(int32_t wfmt, int32_t mats, int32_t N, int32_t K, const void* w, const void* s,
-                     void* w_tiled, void* s_tiled, void* stream);
+ * 16 rt + l%16 and 32-block 4 ks + l/16.  e4m3 block scales keep their
+ * row-major layout (copied when the packed pointer differs).  Work is
+ * enqueued on `stream` like every other call. */
+int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_weights* packed, void* stream);
 
 /* Static description of an error code (host only). */
 const char* moe_status_str(int status);

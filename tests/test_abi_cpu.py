@@ -147,15 +147,17 @@ def test_product_path_does_not_touch_the_oracle():
                 assert "oracle" not in src, f
 
 
-def test_tile_weights_argument_errors(lib):
-    call = lambda wfmt, mats, N, K, w, s, wt, st: moe.raw_call("moe_tile_weights", wfmt, mats, N, K, w, s, wt, st, None)
-    assert call(7, 1, 16, 128, FAKE, FAKE, FAKE + 64, FAKE + 128) == moe.MOE_ERR_UNSUPPORTED
-    assert call(0, 1, 20, 128, FAKE, None, FAKE + 64, None) == moe.MOE_ERR_BAD_SHAPE   # N % 16
-    assert call(1, 1, 16, 96, FAKE, FAKE, FAKE + 64, FAKE + 128) == moe.MOE_ERR_BAD_SHAPE  # K % 128
-    assert call(0, -1, 16, 128, FAKE, None, FAKE + 64, None) == moe.MOE_ERR_BAD_SHAPE
-    assert call(0, 1, 16, 128, None, None, FAKE, None) == moe.MOE_ERR_NULL_ARG
-    assert call(1, 1, 16, 128, FAKE, None, FAKE + 64, FAKE + 128) == moe.MOE_ERR_NULL_ARG  # MXFP4 scales
-    assert call(0, 1, 16, 128, FAKE + 8, None, FAKE + 64, None) == moe.MOE_ERR_MISALIGNED
-    assert call(0, 1, 16, 128, FAKE, None, FAKE, None) == moe.MOE_ERR_UNSUPPORTED        # in place
-    assert call(1, 1, 16, 128, FAKE, FAKE + 32, FAKE + 64, FAKE + 32) == moe.MOE_ERR_UNSUPPORTED
-    assert call(0, 0, 16, 128, None, None, None, None) == moe.MOE_OK                    # nothing to do
+def test_prepack_argument_errors(lib):
+    c = cfg()
+    cc = c.c()
+    src, dst = _w(), _w(w1=FAKE + 256, w1s=FAKE + 512, w2=FAKE + 768, w2s=FAKE + 1024)
+    call = lambda cfgp, a, b: moe.raw_call("moe_prepack_weights", cfgp, a, b, None)
+    assert call(None, C.byref(src), C.byref(dst)) == moe.MOE_ERR_NULL_ARG
+    assert call(C.byref(cc), None, C.byref(dst)) == moe.MOE_ERR_NULL_ARG
+    assert call(C.byref(cc), C.byref(src), None) == moe.MOE_ERR_NULL_ARG
+    assert call(C.byref(cc), C.byref(src), C.byref(_w(w2=None))) == moe.MOE_ERR_NULL_ARG
+    assert call(C.byref(cc), C.byref(src), C.byref(_w(w1=FAKE + 8))) == moe.MOE_ERR_MISALIGNED
+    assert call(C.byref(cfg(topk=0).c()), C.byref(src), C.byref(dst)) == moe.MOE_ERR_BAD_SHAPE
+    assert call(C.byref(cc), C.byref(src), C.byref(src)) == moe.MOE_ERR_UNSUPPORTED   # in place
+    cs = cfg(has_shared=1).c()
+    assert call(C.byref(cs), C.byref(src), C.byref(dst)) == moe.MOE_ERR_NULL_ARG       # shared tensors

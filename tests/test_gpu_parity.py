@@ -73,7 +73,7 @@ def weights_for(wl, seed=0):
             torch.cuda.empty_cache()
         w = synth.gen_weights(wl, seed=seed, device=DEV)
         moe = M()
-        wt = moe.tile_weights(moe.Cfg.for_workload(wl, 1), w)
+        wt = moe.moe_prepack_weights(moe.Cfg.for_workload(wl, 1), w)
         _WCACHE[key] = (wt, w.to("cpu"))
         del w
     return _WCACHE[key]
@@ -118,20 +118,26 @@ def _tile_ref(wfmt, w, s):
     return wt, st
 
 
-@pytest.mark.parametrize("wfmt,mats,N,K", [(0, 2, 48, 256), (1, 2, 48, 384), (1, 1, 16, 128), (0, 3, 32, 128)])
-def test_tile_weights_bitexact(wfmt, mats, N, K):
+@pytest.mark.parametrize("name", ["tiny_fp8", "fp8_b128", "mxfp4", "mxfp4_shared"])
+def test_prepack_weights_bitexact(name):
+    """Every tensor of moe_prepack_weights against numpy reshapes of the
+    documented tiled layout (e4m3 block scales unchanged)."""
     moe = M()
-    _note(f"tile wfmt={wfmt} mats={mats} N={N} K={K}")
-    g = torch.Generator().manual_seed(mats * 1000 + N + K)
-    kb = K if wfmt == 0 else K // 2
-    w = torch.randint(0, 256, (mats, N, kb), generator=g, dtype=torch.uint8)
-    s = (torch.randint(0, 256, (mats, N, K // 32), generator=g, dtype=torch.uint8) if wfmt == 1
-         else torch.rand(mats, N // 32 if N % 32 == 0 else 1, K // 32, generator=g))
-    wt, st = moe.moe_tile_weights(wfmt, w.to(DEV), s.to(DEV))
+    wl = synth.WORKLOADS.get(name) or REDUCED[name]
+    _note(f"prepack {name}")
+    w = synth.gen_weights(wl, seed=3, device=DEV)
+    cfg = moe.Cfg.for_workload(wl, 1)
+    wt = moe.moe_prepack_weights(cfg, w)
     torch.cuda.synchronize()
-    rw, rs = _tile_ref(wfmt, w.numpy(), s.numpy())
-    assert np.array_equal(wt.cpu().numpy(), rw)
-    assert np.array_equal(st.cpu().numpy(), rs)
+    pairs = [("w1", "w1s"), ("w2", "w2s")] + ([("sw1", "sw1s"), ("sw2", "sw2s")] if wl.shared else [])
+    for wn, sn in pairs:
+        ww, ss = getattr(w, wn).cpu().numpy(), getattr(w, sn).cpu().numpy()
+        if ww.ndim == 2:
+            ww, ss = ww[None], ss[None]
+        rw, rs = _tile_ref(wl.wfmt, ww, ss)
+        got_w, got_s = getattr(wt, wn).cpu().numpy(), getattr(wt, sn).cpu().numpy()
+        assert np.array_equal(got_w.reshape(rw.shape), rw), wn
+        assert np.array_equal(got_s.reshape(rs.shape), rs), sn
 
 
 # ------------------------------------------------------------------ permute + quant
@@ -473,7 +479,7 @@ def test_worked_examples_on_gpu():
         wl, wc, x, ids, tw = pins._golden_case(ex)
         T = x.shape[0]
         cfg = moe.Cfg.for_workload(wl, T)
-        out = moe.moe_layer(cfg, x.to(DEV), ids.to(DEV), tw.to(DEV), moe.tile_weights(cfg, wc.to(DEV)))
+        out = moe.moe_layer(cfg, x.to(DEV), ids.to(DEV), tw.to(DEV), moe.moe_prepack_weights(cfg, wc.to(DEV)))
         torch.cuda.synchronize()
         got = out.float().cpu().numpy()
         for t in range(T):
