@@ -75,7 +75,9 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   // MXFP4, and H a multiple of 256.
   const double groups = std::fmin(double(E), double(T) * k);
   const double avg_rows = groups > 0 ? double(T) * k / groups : 0.0;
-  s.big = (G == 128 && (wfmt == 1 || wblk == 128) && H % 256 == 0 && avg_rows >= MOE_BIG_MIN_AVG_ROWS) ? 1 : 0;
+  // the big-tile kernels keep a pass's token scales in LDS: K <= 8192 for both GEMMs
+  s.big = (G == 128 && (wfmt == 1 || wblk == 128) && H % 256 == 0 && H <= 8192 && I <= 8192 &&
+           avg_rows >= MOE_BIG_MIN_AVG_ROWS) ? 1 : 0;
   if (s.big) s.g1_split = s.g2_split = 1;
   return s;
 }
@@ -239,7 +241,7 @@ int moe_grouped_gemm2(const moe_cfg* cfg, const uint8_t* hq, const float* hs, co
     return hip_status(launch_gemm2_big(s, hq, hs, offsets,
                                        WeightPtrs{static_cast<const uint8_t*>(w->w2), w->w2s,
                                                   static_cast<const uint8_t*>(w->sw2), w->sw2s},
-                                       y, 1, st));
+                                       y, nullptr, 1, st));
   int32_t* cnt = reinterpret_cast<int32_t*>(base + L.cnt2);
   if (s.g2_split > 1) {
     if ((rc = hip_status(launch_clear(cnt, (s.E + 1) * s.g2_tiles, st)))) return rc;
@@ -247,7 +249,7 @@ int moe_grouped_gemm2(const moe_cfg* cfg, const uint8_t* hq, const float* hs, co
   return hip_status(launch_gemm2(s, hq, hs, offsets,
                                  WeightPtrs{static_cast<const uint8_t*>(w->w2), w->w2s,
                                             static_cast<const uint8_t*>(w->sw2), w->sw2s},
-                                 y, reinterpret_cast<float*>(base + L.part2), cnt, st));
+                                 y, nullptr, reinterpret_cast<float*>(base + L.part2), cnt, st));
 }
 
 int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* expand_idx, const int32_t* offsets,
@@ -259,7 +261,8 @@ int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* expand_idx, c
                    {out, has_rows}});
   if (rc) return rc;
   const Shape s = shape_of(cfg);
-  return hip_status(launch_combine(s, y, expand_idx, offsets, topk_weights, out, static_cast<hipStream_t>(stream)));
+  return hip_status(
+      launch_combine(s, y, nullptr, expand_idx, offsets, topk_weights, out, static_cast<hipStream_t>(stream)));
 }
 
 int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
@@ -283,7 +286,9 @@ int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, co
   float* xs = reinterpret_cast<float*>(b + L.xs);
   uint8_t* hq = reinterpret_cast<uint8_t*>(b + L.hq);
   float* hs = reinterpret_cast<float*>(b + L.hs);
-  float* y = reinterpret_cast<float*>(b + L.y);
+  // GEMM2 rows stay inside the layer as bf16 (half the bytes of the fp32
+  // rows the stage export returns); the combine accumulates them in fp32
+  uint16_t* yb = reinterpret_cast<uint16_t*>(b + L.y);
   int32_t* cnt1 = reinterpret_cast<int32_t*>(b + L.cnt1);
   int32_t* cnt2 = reinterpret_cast<int32_t*>(b + L.cnt2);
   const int nclear = int((L.total - L.cnt1) / 4);
@@ -294,16 +299,16 @@ int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, co
   const WeightPtrs w2{static_cast<const uint8_t*>(w->w2), w->w2s, static_cast<const uint8_t*>(w->sw2), w->sw2s};
   if (s.big) {
     if ((rc = hip_status(launch_gemm1_big(s, xq, xs, rtok, offsets, w1, hq, hs, 1, st)))) return rc;
-    if ((rc = hip_status(launch_gemm2_big(s, hq, hs, offsets, w2, y, 1, st)))) return rc;
+    if ((rc = hip_status(launch_gemm2_big(s, hq, hs, offsets, w2, nullptr, yb, 1, st)))) return rc;
   } else {
     if ((rc = hip_status(launch_gemm1(s, xq, xs, rtok, offsets, w1, hq, hs,
                                       reinterpret_cast<float*>(b + L.part1), cnt1, st))))
       return rc;
-    if ((rc = hip_status(launch_gemm2(s, hq, hs, offsets, w2, y, reinterpret_cast<float*>(b + L.part2), cnt2,
-                                      st))))
+    if ((rc = hip_status(launch_gemm2(s, hq, hs, offsets, w2, nullptr, yb, reinterpret_cast<float*>(b + L.part2),
+                                      cnt2, st))))
       return rc;
   }
-  return hip_status(launch_combine(s, y, eidx, offsets, topk_weights, out, st));
+  return hip_status(launch_combine(s, nullptr, yb, eidx, offsets, topk_weights, out, st));
 }
 
 int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_weights* packed, void* stream) {

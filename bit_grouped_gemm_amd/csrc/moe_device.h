@@ -105,6 +105,14 @@ __device__ __forceinline__ v8i load_e2m1_frag(const uint8_t* row_k0, int g) {
   return r;
 }
 
+// four fp32 -> four bf16 (RNE), one 8-byte store
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, const v4f& v) {
+  uint2 o;
+  o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+  o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<uint2*>(dst) = o;
+}
+
 // ------------------------------------------------------------ tiled weights
 // Expert weights are stored as tiles of 16 rows x 128 K in MFMA lane order,
 // tile (k step, row tile) at ((ks * N/16) + rt) * kTileBytes<WF>: lane l's

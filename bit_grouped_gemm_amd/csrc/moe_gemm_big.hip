@@ -43,7 +43,8 @@ constexpr int kTokCap = 160;                 // token rows per pass
 constexpr int kTokTiles = kTokCap / 16;      // 10
 constexpr int kWTiles = 16;                  // 256 weight rows
 constexpr int kBBytes = kTokTiles * 2048;     // token tiles: 16 rows x 128 B, chunk-swizzled
-constexpr int kXsBytes = 8 * 64 * 4;         // token scales: one dword slot per lane of 8 waves
+constexpr int kMaxKSteps = 64;              // K <= 8192: the pass's token scales fit one LDS table
+constexpr int kXsRow = kMaxKSteps + 1;       // floats per token row of the table (odd: no bank conflicts)
 constexpr int kAsBytes = 8 * 64 * 4;         // MXFP4 scales: one dword (4 x e8m0) per lane of 8 waves
 constexpr int kTokPerWave = kTokTiles / 2;   // token tiles of one wave column
 constexpr int kSinkBytes = 1024;             // target of token loads past the pass's tiles
@@ -51,19 +52,19 @@ constexpr int kSinkBytes = 1024;             // target of token loads past the p
 template <int WF> struct BigGeo {
   static constexpr int kStages = WF == 1 ? 3 : 2;
   static constexpr int kABytes = kWTiles * 1024 * (WF == 1 ? 1 : 2);
-  static constexpr int kXsOff = kBBytes;
-  static constexpr int kAOff = kBBytes + kXsBytes;
+  static constexpr int kAOff = kBBytes;
   static constexpr int kAsOff = kAOff + kABytes;
   static constexpr int kSinkOff = kAsOff + (WF == 1 ? kAsBytes : 0);
   static constexpr int kStageBytes = kSinkOff + kSinkBytes;
-  // direct-to-LDS loads per wave per stage: token rows 3, token scales 1,
-  // weight tiles 2 (MXFP4) or 4 (e4m3 halves), MXFP4 scales 1
-  static constexpr int kLoadsPerStage = 3 + 1 + (WF == 1 ? 2 + 1 : 4);
-  static constexpr int kLdsBytes = kStages * kStageBytes;
+  // direct-to-LDS loads per wave per stage: token rows 3, weight tiles 2
+  // (MXFP4) or 4 (e4m3 halves), MXFP4 scales 1
+  static constexpr int kLoadsPerStage = 3 + (WF == 1 ? 2 + 1 : 4);
+  static constexpr int kXsTabBytes = kTokCap * kXsRow * 4;  // [token][k step] fp32
+  static constexpr int kLdsBytes = kStages * kStageBytes + kXsTabBytes;
 };
-static_assert(BigGeo<1>::kLdsBytes <= 160 * 1024, "MXFP4 ring fits the 160 KB LDS");
+static_assert(BigGeo<1>::kLdsBytes + 1024 <= 160 * 1024, "MXFP4 ring, scale table and small arrays fit the 160 KB LDS");
 static_assert(4 * kTokCap * 4 <= BigGeo<0>::kStageBytes, "epilogue maxima fit one stage");
-static_assert(BigGeo<0>::kLdsBytes <= 160 * 1024, "e4m3 ring fits the 160 KB LDS");
+static_assert(BigGeo<0>::kLdsBytes + 1024 <= 160 * 1024, "e4m3 ring, scale table and small arrays fit the 160 KB LDS");
 static_assert(kTokTiles * 2 <= 3 * 8, "at most three token-row loads per wave");
 
 struct BigParams {
@@ -78,6 +79,7 @@ struct BigParams {
   uint8_t* hq;
   float* hs;
   float* y;
+  uint16_t* yb;  // bf16 y instead when non-null (layer-internal)
   int H, I, E, G, wblk, ngroups, ntiles, units, per_xcd, min_rows;
 };
 
@@ -124,6 +126,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
   __shared__ __align__(1024) uint8_t st0[Geo::kStageBytes];
   __shared__ __align__(1024) uint8_t st1[Geo::kStageBytes];
   __shared__ __align__(1024) uint8_t st2[S == 3 ? Geo::kStageBytes : 16];
+  __shared__ __align__(16) float xs_tab[kTokCap * kXsRow];  // token scales of the pass
   __shared__ int s_wsum[8], s_res;
 
   // ---- unit: XCD-aware order (blockIdx -> XCD is round-robin over 8)
@@ -229,19 +232,22 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
       b_src[q] = p.act + arow * K + (real ? ((lane & 7) ^ (rl & 7)) << 4 : 0);
       b_dst[q] = real ? i * 1024 : Geo::kSinkOff;
     }
-    const float* xs_src;
-    {
-      const int tk = min(w * 64 + lane, npass - 1);
-      const long arow = MODE == 0 ? long(p.row_token[row0 + pass0 + tk]) : long(row0 + pass0 + tk);
-      xs_src = p.act_s + arow * (K / 128);
+    // token scales of the whole pass, read once into a [token][k step]
+    // table: one direct-to-LDS load per token (its K/128 scales are
+    // contiguous; lanes past them repeat the last one), 20 per wave.  Being
+    // direct loads into their own array, the table's reads wait only for
+    // these loads, not for the ring's.
+    for (int tk = w; tk < kTokCap; tk += 8) {
+      const int c = min(tk, npass - 1);
+      const long arow = MODE == 0 ? long(p.row_token[row0 + pass0 + c]) : long(row0 + pass0 + c);
+      dma4(p.act_s + arow * nks + min(lane, nks - 1), reinterpret_cast<uint8_t*>(xs_tab + tk * kXsRow));
     }
 
     // the direct-to-LDS loads of step ks into stage buffer st, in three
-    // parts (0: token scales and weights, 1: weight scales and the first
+    // parts (0: weight tiles, 1: weight scales and the first
     // token-row load, 2: the other two token-row loads)
     auto issue = [&](int ks, uint8_t* st, int part) __attribute__((always_inline)) {
       if (part == 0) {
-        dma4(xs_src + ks, st + Geo::kXsOff + w * 256);
         if (WF == 1) {
 #pragma unroll
           for (int q = 0; q < 2; ++q) dma16(a_src[q] + ks * wstep, st + Geo::kAOff + (2 * w + q) * 1024);
@@ -310,7 +316,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
       float xsv[kTokPerWave];
 #pragma unroll
       for (int tt = 0; tt < kTokPerWave; ++tt)
-        xsv[tt] = *reinterpret_cast<const float*>(st + Geo::kXsOff + ((2 * tt + wc) * 16 + m) * 4);
+        xsv[tt] = xs_tab[((2 * tt + wc) * 16 + m) * kXsRow + ks];
       if (WF == 1) {
         // rescale to this step's token scales
 #pragma unroll
@@ -450,7 +456,8 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
         const long r = row0 + pass0 + idx;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<v4f*>(p.y + r * H + n0 + 64 * wr + 16 * q + 4 * g) = acc[q][tt];
+          if (p.yb) store_bf16x4(p.yb + r * H + n0 + 64 * wr + 16 * q + 4 * g, acc[q][tt]);
+          else *reinterpret_cast<v4f*>(p.y + r * H + n0 + 64 * wr + 16 * q + 4 * g) = acc[q][tt];
       }
     }
     __syncthreads();  // LDS is reused by the next pass
@@ -488,11 +495,12 @@ hipError_t launch_gemm1_big(const Shape& s, const uint8_t* xq, const float* xs, 
 }
 
 hipError_t launch_gemm2_big(const Shape& s, const uint8_t* hq, const float* hs, const int32_t* offsets,
-                            WeightPtrs w2, float* y, int min_rows, hipStream_t st) {
+                            WeightPtrs w2, float* y, uint16_t* yb, int min_rows, hipStream_t st) {
   BigParams p{};
   p.act = hq; p.act_s = hs; p.offsets = offsets;
   p.w = w2.w; p.ws = w2.ws; p.sw = w2.sw; p.sws = w2.sws;
   p.y = y;
+  p.yb = yb;
   p.H = s.H; p.I = s.I; p.E = s.E; p.G = s.G; p.wblk = s.wblk; p.ngroups = s.ngroups;
   p.ntiles = s.H / 256; p.min_rows = min_rows;
   return launch_big(s, 1, p, st);

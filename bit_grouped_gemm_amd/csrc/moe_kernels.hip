@@ -352,7 +352,8 @@ struct GemmParams {
   const void* sws;
   uint8_t* hq;               // GEMM1 outputs
   float* hs;
-  float* y;                  // GEMM2 output
+  float* y;                  // GEMM2 output (fp32), or
+  uint16_t* yb;              // the same as bf16 when non-null (layer-internal)
   float* part;
   int32_t* cnt;
   int H, I, E, G, wblk, ngroups, S, ntiles, rows_cap;
@@ -608,8 +609,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int col = 32 * w + 16 * j + 4 * g;
-        if (S == 1)
-          *reinterpret_cast<v4f*>(p.y + r * H + n0 + col) = acc[j][t];
+        if (S == 1) {
+          if (p.yb) store_bf16x4(p.yb + r * H + n0 + col, acc[j][t]);
+          else *reinterpret_cast<v4f*>(p.y + r * H + n0 + col) = acc[j][t];
+        }
         else
           st_coherent(prs, ((long(split) * nt + tile) * p.rows_cap + r) * 128 + col, acc[j][t]);
       }
@@ -624,7 +627,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
     v4f s = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int sp = 0; sp < S; ++sp)
       s += ld_coherent(prs, ((long(sp) * nt + tile) * p.rows_cap + r) * 128 + col);
-    *reinterpret_cast<v4f*>(p.y + r * H + n0 + col) = s;
+    if (p.yb) store_bf16x4(p.yb + r * H + n0 + col, s);
+    else *reinterpret_cast<v4f*>(p.y + r * H + n0 + col) = s;
   }
 }
 
@@ -632,7 +636,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
 // combine: one workgroup per token, 4 channels per thread per step
 // =====================================================================
 struct CombineParams {
-  const float* y;
+  const float* y;            // fp32 rows, or
+  const uint16_t* yb;        // bf16 rows when non-null
   const int32_t* expand_idx;
   const int32_t* offsets;
   const float* tw;
@@ -646,6 +651,14 @@ struct CombineParams {
 // row of the token with weight 0, whose product is an exact zero and leaves
 // the ascending-order fp32 sum unchanged.
 constexpr int kCombineChunk = kThreads * 4;
+
+__device__ __forceinline__ v4f load_row4(const CombineParams& p, long r, int c) {
+  if (p.yb) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p.yb + r * p.H + c);
+    return v4f{bf16_to_f32(u.x & 0xFFFFu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xFFFFu), bf16_to_f32(u.y >> 16)};
+  }
+  return *reinterpret_cast<const v4f*>(p.y + r * p.H + c);
+}
 
 __global__ __launch_bounds__(kThreads) void k_combine(CombineParams p) {
   const int nchunk = (p.H + kCombineChunk - 1) / kCombineChunk;
@@ -669,12 +682,12 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineParams p) {
         const int j = j0 + jj;
         const int r = j < k ? ids[j] : -1;
         wj[jj] = r >= 0 ? tw[j] : 0.0f;
-        v[jj] = *reinterpret_cast<const v4f*>(p.y + long(r >= 0 ? r : pad) * p.H + c);
+        v[jj] = load_row4(p, r >= 0 ? r : pad, c);
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) acc += wj[jj] * v[jj];
     }
-    if (srow >= 0) acc += *reinterpret_cast<const v4f*>(p.y + long(srow) * p.H + c);
+    if (srow >= 0) acc += load_row4(p, srow, c);
   }
   uint2 o;
   o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
@@ -740,11 +753,11 @@ hipError_t launch_gemm1(const Shape& s, const uint8_t* xq, const float* xs, cons
 }
 
 hipError_t launch_gemm2(const Shape& s, const uint8_t* hq, const float* hs, const int32_t* offsets,
-                        WeightPtrs w2, float* y, float* part, int32_t* cnt, hipStream_t st) {
+                        WeightPtrs w2, float* y, uint16_t* yb, float* part, int32_t* cnt, hipStream_t st) {
   GemmParams p{};
   p.act = hq; p.act_s = hs; p.offsets = offsets;
   p.w = w2.w; p.ws = w2.ws; p.sw = w2.sw; p.sws = w2.sws;
-  p.y = y; p.part = part; p.cnt = cnt;
+  p.y = y; p.yb = yb; p.part = part; p.cnt = cnt;
   p.H = s.H; p.I = s.I; p.E = s.E; p.G = s.G; p.wblk = s.wblk; p.ngroups = s.ngroups;
   p.S = s.g2_split; p.ntiles = s.g2_tiles; p.rows_cap = s.rows_cap;
   const unsigned grid = unsigned(s.slots_max) * s.g2_tiles * s.g2_split;
@@ -752,10 +765,10 @@ hipError_t launch_gemm2(const Shape& s, const uint8_t* hq, const float* hs, cons
   return dispatch_k_gemm2(s, s.g2_ntt, grid, p, st);
 }
 
-hipError_t launch_combine(const Shape& s, const float* y, const int32_t* expand_idx, const int32_t* offsets,
+hipError_t launch_combine(const Shape& s, const float* y, const uint16_t* yb, const int32_t* expand_idx, const int32_t* offsets,
                           const float* topk_w, uint16_t* out, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
-  CombineParams p{y, expand_idx, offsets, topk_w, out, s.H, s.k, s.E, s.shared};
+  CombineParams p{y, yb, expand_idx, offsets, topk_w, out, s.H, s.k, s.E, s.shared};
   const long grid = long(s.T) * ((s.H + kCombineChunk - 1) / kCombineChunk);
   hipLaunchKernelGGL(k_combine, dim3(unsigned(grid)), dim3(kThreads), 0, st, p);
   return hipGetLastError();

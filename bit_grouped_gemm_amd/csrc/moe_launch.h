@@ -56,19 +56,20 @@ hipError_t launch_gemm1(const Shape& s, const uint8_t* xq, const float* xs, cons
                         int32_t* cnt, hipStream_t st);
 
 hipError_t launch_gemm2(const Shape& s, const uint8_t* hq, const float* hs, const int32_t* offsets,
-                        WeightPtrs w2, float* y, float* part, int32_t* cnt, hipStream_t st);
+                        WeightPtrs w2, float* y, uint16_t* yb, float* part, int32_t* cnt, hipStream_t st);
 
 hipError_t launch_gemm1_big(const Shape& s, const uint8_t* xq, const float* xs, const int32_t* row_token,
                             const int32_t* offsets, WeightPtrs w1, uint8_t* hq, float* hs, int min_rows,
                             hipStream_t st);
 
 hipError_t launch_gemm2_big(const Shape& s, const uint8_t* hq, const float* hs, const int32_t* offsets,
-                            WeightPtrs w2, float* y, int min_rows, hipStream_t st);
+                            WeightPtrs w2, float* y, uint16_t* yb, int min_rows, hipStream_t st);
 
 hipError_t launch_tile_weights(int wfmt, int mats, int N, int K, const uint8_t* w, const uint8_t* s, uint8_t* w_tiled,
                                uint8_t* s_tiled, hipStream_t st);
 
-hipError_t launch_combine(const Shape& s, const float* y, const int32_t* expand_idx, const int32_t* offsets,
+// y: GEMM2 output rows in fp32, or yb in bf16 (the layer's internal form; y unused then)
+hipError_t launch_combine(const Shape& s, const float* y, const uint16_t* yb, const int32_t* expand_idx, const int32_t* offsets,
                           const float* topk_w, uint16_t* out, hipStream_t st);
 
 }  // namespace moe

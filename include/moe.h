@@ -152,7 +152,11 @@ int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* expand_idx, c
 
 /* Steps 1-8 in one call (internally fused where it pays):
  *   x bf16 [T][H], topk_ids int32 [T][topk], topk_weights fp32 [T][topk],
- *   out bf16 [T][H]; ws of at least moe_workspace_size(cfg) bytes. */
+ *   out bf16 [T][H]; ws of at least moe_workspace_size(cfg) bytes.
+ * Between GEMM2 and the combine the rows y are kept as bf16 (round to
+ * nearest even) instead of fp32, halving that round trip through memory;
+ * every sum is still accumulated in fp32.  The result equals the stage
+ * calls chained with y rounded to bf16 before moe_combine. */
 int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
               const moe_weights* w, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 

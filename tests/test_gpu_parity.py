@@ -391,7 +391,7 @@ def test_layer_big_tiles(name, T):
     ws = moe.workspace(cfg)
     hq, hs = moe.moe_grouped_gemm1_swiglu(cfg, xq, xs, rtok, offsets, w, ws)
     y = moe.moe_grouped_gemm2(cfg, hq, hs, offsets, w, ws)
-    out2 = moe.moe_combine(cfg, y, eidx, offsets, tw)
+    out2 = moe.moe_combine(cfg, y.to(torch.bfloat16).float().contiguous(), eidx, offsets, tw)  # layer keeps y in bf16
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
     # requantised codes of a sample of rows against the oracle's
@@ -455,7 +455,9 @@ def test_poisoned_workspace_and_determinism():
 
 
 def test_layer_matches_its_stages():
-    """moe_layer equals the four stage calls chained through the C ABI."""
+    """moe_layer equals the four stage calls chained through the C ABI, with
+    the GEMM2 rows rounded to bf16 (RNE) before the combine, as the layer
+    keeps them internally."""
     moe = M()
     wl = REDUCED["fp8_zipf_shared"]
     T = 19
@@ -467,7 +469,7 @@ def test_layer_matches_its_stages():
     ws = moe.workspace(cfg)
     hq, hs = moe.moe_grouped_gemm1_swiglu(cfg, xq, xs, rtok, offsets, w, ws)
     y = moe.moe_grouped_gemm2(cfg, hq, hs, offsets, w, ws)
-    out2 = moe.moe_combine(cfg, y, eidx, offsets, tw)
+    out2 = moe.moe_combine(cfg, y.to(torch.bfloat16).float().contiguous(), eidx, offsets, tw)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
