@@ -7,7 +7,7 @@ missing, importing the entry points raises.
 
 Entry points (same names as the C ABI):
     moe_workspace_size(cfg) -> int
-    moe_permute(cfg, x, topk_ids) -> (counts, offsets, expand_idx, row_token, xq, xs)
+    moe_permute(cfg, x, topk_ids, ws=None) -> (counts, offsets, expand_idx, row_token, xq, xs)
     moe_grouped_gemm1_swiglu(cfg, xq, xs, row_token, offsets, weights, ws) -> (hq, hs)
     moe_grouped_gemm2(cfg, hq, hs, offsets, weights, ws) -> y
     moe_combine(cfg, y, expand_idx, offsets, topk_weights) -> out
@@ -161,7 +161,7 @@ def workspace(cfg: Cfg, device="cuda") -> torch.Tensor:
     return torch.empty(moe_workspace_size(cfg), dtype=torch.uint8, device=device)
 
 
-def moe_permute(cfg: Cfg, x: torch.Tensor, topk_ids: torch.Tensor):
+def moe_permute(cfg: Cfg, x: torch.Tensor, topk_ids: torch.Tensor, ws: Optional[torch.Tensor] = None):
     dev = x.device
     T, k, E, sh = cfg.T, cfg.topk, cfg.E, cfg.has_shared
     counts = torch.empty(E + sh, dtype=torch.int32, device=dev)
@@ -171,9 +171,10 @@ def moe_permute(cfg: Cfg, x: torch.Tensor, topk_ids: torch.Tensor):
     xq = torch.empty(T, cfg.H, dtype=torch.uint8, device=dev)
     xs = torch.empty(T, cfg.H // cfg.act_group, dtype=torch.float32, device=dev)
     c = cfg.c()
+    ws = workspace(cfg, dev) if ws is None else ws  # per-chunk counts when T*topk > 4096
     _check("moe_permute", load().moe_permute(C.byref(c), _ptr(_u16(x)), _ptr(topk_ids), _ptr(counts),
                                              _ptr(offsets), _ptr(eidx), _ptr(rtok), _ptr(xq), _ptr(xs),
-                                             None, 0, _stream()))
+                                             _ptr(ws), ws.numel(), _stream()))
     return counts, offsets, eidx, rtok, xq, xs
 
 

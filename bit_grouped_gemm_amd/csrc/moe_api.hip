@@ -79,6 +79,19 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   s.big = (G == 128 && (wfmt == 1 || wblk == 128) && H % 256 == 0 && H <= 8192 && I <= 8192 &&
            avg_rows >= MOE_BIG_MIN_AVG_ROWS) ? 1 : 0;
   if (s.big) s.g1_split = s.g2_split = 1;
+  // permute: one block places up to 4096 slots; beyond that the slots are
+  // split into at most 64 chunks of at least 2048, each placed by its own
+  // block after a counting pass
+  const long n = long(T) * k;
+  if (n <= 4096) {
+    s.perm_chunk = int(std::max(n, 1L));
+    s.perm_chunks = 1;
+  } else {
+    long chunk = std::max(2048L, (n + 63) / 64);
+    chunk = (chunk + 63) / 64 * 64;
+    s.perm_chunk = int(chunk);
+    s.perm_chunks = int((n + chunk - 1) / chunk);
+  }
   return s;
 }
 
@@ -104,6 +117,7 @@ WsLayout make_ws_layout(const Shape& s) {
   L.y = take(4 * R * s.H);
   L.part1 = take(s.g1_split > 1 ? 4 * size_t(s.g1_split) * R * 2 * s.I : 0);
   L.part2 = take(s.g2_split > 1 ? 4 * size_t(s.g2_split) * R * s.H : 0);
+  L.chunk_cnt = take(s.perm_chunks > 1 ? 4 * size_t(s.perm_chunks) * s.E : 0);
   // the two counter arrays are adjacent so one clear covers both
   L.cnt1 = o;
   L.cnt2 = L.cnt1 + 4 * size_t(s.E + 1) * s.g1_tiles;
@@ -179,17 +193,19 @@ int moe_workspace_size(const moe_cfg* cfg, size_t* bytes) {
 int moe_permute(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, int32_t* counts,
                 int32_t* offsets, int32_t* expand_idx, int32_t* row_token, uint8_t* xq, float* xs, void* ws,
                 size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   int rc = check_cfg(cfg);
   if (rc) return rc;
   const bool has_rows = cfg->T > 0;
-  rc = check_ptrs({{x, has_rows}, {topk_ids, has_rows}, {counts, true}, {offsets, true},
-                   {expand_idx, has_rows}, {row_token, has_rows}, {xq, has_rows}, {xs, has_rows}});
-  if (rc) return rc;
   const Shape s = shape_of(cfg);
+  const bool chunked = s.perm_chunks > 1;  // needs the workspace for per-chunk counts
+  rc = check_ptrs({{x, has_rows}, {topk_ids, has_rows}, {counts, true}, {offsets, true},
+                   {expand_idx, has_rows}, {row_token, has_rows}, {xq, has_rows}, {xs, has_rows}, {ws, chunked}});
+  if (rc) return rc;
+  const WsLayout L = make_ws_layout(s);
+  if (chunked && ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  int32_t* chunk_cnt = chunked ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.chunk_cnt) : nullptr;
   return hip_status(launch_route_quant(s, x, topk_ids, counts, offsets, expand_idx, row_token, xq, xs, nullptr,
-                                       0, static_cast<hipStream_t>(stream)));
+                                       0, chunk_cnt, static_cast<hipStream_t>(stream)));
 }
 
 int moe_grouped_gemm1_swiglu(const moe_cfg* cfg, const uint8_t* xq, const float* xs, const int32_t* row_token,
@@ -292,7 +308,9 @@ int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, co
   int32_t* cnt1 = reinterpret_cast<int32_t*>(b + L.cnt1);
   int32_t* cnt2 = reinterpret_cast<int32_t*>(b + L.cnt2);
   const int nclear = int((L.total - L.cnt1) / 4);
-  if ((rc = hip_status(launch_route_quant(s, x, topk_ids, counts, offsets, eidx, rtok, xq, xs, cnt1, nclear, st))))
+  int32_t* chunk_cnt = reinterpret_cast<int32_t*>(b + L.chunk_cnt);
+  if ((rc = hip_status(launch_route_quant(s, x, topk_ids, counts, offsets, eidx, rtok, xq, xs, cnt1, nclear,
+                                          chunk_cnt, st))))
     return rc;
   if (!has_rows) return MOE_OK;
   const WeightPtrs w1{static_cast<const uint8_t*>(w->w1), w->w1s, static_cast<const uint8_t*>(w->sw1), w->sw1s};

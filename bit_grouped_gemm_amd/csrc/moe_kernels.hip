@@ -2,7 +2,9 @@
 //
 //   k_route_quant  expert histogram, exclusive-scan offsets, stable expand
 //                  index (block 0) and per-token FP8 activation
-//                  quantisation (all other blocks), one launch.
+//                  quantisation (all other blocks), one launch; for many
+//                  slots the first blocks only count their chunk of slots
+//   k_permute_rank and one block per chunk then places that chunk's slots.
 //   k_gemm1        grouped GEMM1 over gate|up weights (e4m3 with fp32
 //                  block scales, or MXFP4 through the scaled MFMA), fp32
 //                  accumulation, fused SwiGLU and FP8 requantisation;
@@ -14,10 +16,11 @@
 // Dataflow follows the GMM1 -> SwiGLU -> GMM2 -> combine chain of the
 // FusedDeepMoE family analysis (unified execution flow figure; OpDequant,
 // OpSwiglu, OpBlockQuant) and the FP8/FP4 grouped GEMM with fused SwiGLU and
-// requantisation of the GC-MoE abstract.  At decode the weights are the
-// traffic ("weight traffic dominate[s]" in the GC-MoE abstract): weight rows
-// sit on the 16-row MFMA side and stream straight from HBM into registers,
-// while the few tokens of an expert form the 16-column side.
+// requantisation of the GC-MoE abstract.  At decode the expert weights are
+// most of the bytes moved (the GC-MoE abstract makes the same point for
+// decode), so weight rows sit on the 16-row MFMA side and stream straight
+// from HBM into registers, while the few tokens of an expert form the
+// 16-column side.
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -43,19 +46,25 @@ struct RouteParams {
   float* xs;
   int32_t* clear;
   int nclear;
+  int32_t* chunk_cnt;  // chunked mode: per-chunk expert counts [nchunks][E]
+  int chunk, nchunks;  // slots per chunk; nchunks == 1: one block places every slot
   int T, H, k, E, G, shared;
 };
 
-__device__ void permute_block(const RouteParams& p) {
+// Place slots [c0, c1) (chunk b of nb): expert histogram of the chunk, the
+// experts' row offsets (from this block's own counts when nb == 1, else
+// from every chunk's counts in p.chunk_cnt), then stable ranks.  Block 0
+// also writes counts, offsets and the layer's bookkeeping.
+__device__ void permute_chunk(const RouteParams& p, int b, int nb, int c0, int c1) {
   __shared__ int cnt[4][1024];  // per-wave expert counts, then per-wave running row bases
   __shared__ int wsum[4];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int E = p.E, n = p.T * p.k;
   for (int i = tid; i < 4 * 1024; i += kThreads) (&cnt[0][0])[i] = 0;
   __syncthreads();
-  // each wave owns one contiguous, 64-aligned range of flat slots
-  const int per = ((n + 4 * 64 - 1) / (4 * 64)) * 64;
-  const int i0 = min(n, w * per), i1 = min(n, i0 + per);
+  // each wave owns one contiguous, 64-aligned range of the chunk's slots
+  const int per = ((c1 - c0 + 4 * 64 - 1) / (4 * 64)) * 64;
+  const int i0 = min(c1, c0 + w * per), i1 = min(c1, i0 + per);
   // ids are read kBatch rounds of 64 at a time so the loads overlap
   constexpr int kBatch = 8;
   for (int base = i0; base < i1; base += 64 * kBatch) {
@@ -70,14 +79,25 @@ __device__ void permute_block(const RouteParams& p) {
       if (eb[q] >= 0 && eb[q] < E) atomicAdd(&cnt[w][eb[q]], 1);
   }
   __syncthreads();
-  // totals per expert and their exclusive scan (thread tid owns a contiguous
-  // run of at most 4 experts)
+  // totals per expert over all slots, their exclusive scan, and the rows
+  // taken by earlier chunks (thread tid owns a contiguous run of at most 4
+  // experts)
   const int ept = (E + kThreads - 1) / kThreads;
-  int tot[4] = {0, 0, 0, 0};
+  int tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
   int local = 0;
   for (int q = 0; q < ept; ++q) {
     const int e = tid * ept + q;
-    if (e < E) tot[q] = cnt[0][e] + cnt[1][e] + cnt[2][e] + cnt[3][e];
+    if (e < E) {
+      if (nb == 1) {
+        tot[q] = cnt[0][e] + cnt[1][e] + cnt[2][e] + cnt[3][e];
+      } else {
+        for (int bb = 0; bb < nb; ++bb) {
+          const int c = p.chunk_cnt[bb * E + e];
+          tot[q] += c;
+          if (bb < b) pre[q] += c;
+        }
+      }
+    }
     local += tot[q];
   }
   int incl = local;
@@ -92,19 +112,21 @@ __device__ void permute_block(const RouteParams& p) {
   for (int q = 0; q < ept; ++q) {
     const int e = tid * ept + q;
     if (e < E) {
-      p.counts[e] = tot[q];
-      p.offsets[e] = run;
-      int b = run;
+      if (b == 0) {
+        p.counts[e] = tot[q];
+        p.offsets[e] = run;
+      }
+      int bs = run + pre[q];
       for (int ww = 0; ww < 4; ++ww) {
         const int c = cnt[ww][e];
-        cnt[ww][e] = b;
-        b += c;
+        cnt[ww][e] = bs;
+        bs += c;
       }
       run += tot[q];
     }
   }
   const int R0 = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  if (tid == 0) {
+  if (b == 0 && tid == 0) {
     p.offsets[E] = R0;
     if (p.shared) {
       p.counts[E] = p.T;
@@ -119,41 +141,57 @@ __device__ void permute_block(const RouteParams& p) {
   while ((1 << nbits) < E) ++nbits;
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   for (int base0 = i0; base0 < i1; base0 += 64 * kBatch) {
-   int eb[kBatch];
+    int eb[kBatch];
 #pragma unroll
-   for (int q = 0; q < kBatch; ++q) {
-     const int i = base0 + q * 64 + lane;
-     eb[q] = i < i1 ? p.ids[i] : -1;
-   }
-   for (int q = 0; q < kBatch; ++q) {
-    const int base = base0 + q * 64;
-    if (base >= i1) break;
-    const int i = base + lane;
-    const int e = eb[q];
-    const bool valid = i < i1 && e >= 0 && e < E;
-    uint64_t match = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t bb = __ballot(bit);
-      match &= bit ? bb : ~bb;
+    for (int q = 0; q < kBatch; ++q) {
+      const int i = base0 + q * 64 + lane;
+      eb[q] = i < i1 ? p.ids[i] : -1;
     }
-    int row = -1;
-    if (valid) row = cnt[w][e] + __popcll(match & below);
-    __builtin_amdgcn_wave_barrier();
-    if (valid && (match & below) == 0) cnt[w][e] = row + __popcll(match);
-    __builtin_amdgcn_wave_barrier();
-    if (i < i1) {
-      p.expand_idx[i] = row;
-      if (valid) p.row_token[row] = i / p.k;
+    for (int q = 0; q < kBatch; ++q) {
+      const int base = base0 + q * 64;
+      if (base >= i1) break;
+      const int i = base + lane;
+      const int e = eb[q];
+      const bool valid = i < i1 && e >= 0 && e < E;
+      uint64_t match = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool on = valid && ((e >> bit) & 1);
+        const uint64_t bb = __ballot(on);
+        match &= on ? bb : ~bb;
+      }
+      int row = -1;
+      if (valid) row = cnt[w][e] + __popcll(match & below);
+      __builtin_amdgcn_wave_barrier();
+      if (valid && (match & below) == 0) cnt[w][e] = row + __popcll(match);
+      __builtin_amdgcn_wave_barrier();
+      if (i < i1) {
+        p.expand_idx[i] = row;
+        if (valid) p.row_token[row] = i / p.k;
+      }
     }
-   }
   }
+  if (b != 0) return;
   if (p.shared)
     for (int t = tid; t < p.T; t += kThreads) p.row_token[R0 + t] = t;
   const int R = R0 + (p.shared ? p.T : 0);
   const int cap = n + (p.shared ? p.T : 0);
   for (int r = R + tid; r < cap; r += kThreads) p.row_token[r] = -1;
   for (int q = tid; q < p.nclear; q += kThreads) p.clear[q] = 0;
+}
+
+// chunked mode, first pass: expert counts of chunk b into p.chunk_cnt[b][:]
+__device__ void count_chunk(const RouteParams& p, int b) {
+  __shared__ int c[1024];
+  const int tid = threadIdx.x, E = p.E, n = p.T * p.k;
+  for (int e = tid; e < E; e += kThreads) c[e] = 0;
+  __syncthreads();
+  const int c0 = b * p.chunk, c1 = min(n, c0 + p.chunk);
+  for (int i = c0 + tid; i < c1; i += kThreads) {
+    const int e = p.ids[i];
+    if (e >= 0 && e < E) atomicAdd(&c[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) p.chunk_cnt[b * E + e] = c[e];
 }
 
 // one thread = 8 consecutive channels of one token; a group of G channels
@@ -190,9 +228,19 @@ __device__ void quant_block(const RouteParams& p, int blk) {
   }
 }
 
+// blocks [0, nlead) route (the whole permute, or the chunk counts), the
+// rest quantise
 __global__ __launch_bounds__(kThreads) void k_route_quant(RouteParams p) {
-  if (blockIdx.x == 0) permute_block(p);
-  else quant_block(p, blockIdx.x - 1);
+  const int nlead = p.nchunks == 1 ? 1 : p.nchunks;
+  if (int(blockIdx.x) >= nlead) quant_block(p, blockIdx.x - nlead);
+  else if (p.nchunks == 1) permute_chunk(p, 0, 1, 0, p.T * p.k);
+  else count_chunk(p, blockIdx.x);
+}
+
+// chunked mode, second pass: block b places chunk b's slots
+__global__ __launch_bounds__(kThreads) void k_permute_rank(RouteParams p) {
+  const int b = blockIdx.x, n = p.T * p.k;
+  permute_chunk(p, b, p.nchunks, b * p.chunk, min(n, (b + 1) * p.chunk));
 }
 
 __global__ __launch_bounds__(kThreads) void k_clear(int32_t* p, int n) {
@@ -700,12 +748,14 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineParams p) {
 // =====================================================================
 hipError_t launch_route_quant(const Shape& s, const uint16_t* x, const int32_t* ids, int32_t* counts,
                               int32_t* offsets, int32_t* expand_idx, int32_t* row_token, uint8_t* xq,
-                              float* xs, int32_t* clear, int nclear, hipStream_t st) {
+                              float* xs, int32_t* clear, int nclear, int32_t* chunk_cnt, hipStream_t st) {
   RouteParams p{x, ids, counts, offsets, expand_idx, row_token, xq, xs, clear, nclear,
-                s.T, s.H, s.k, s.E, s.G, s.shared};
+                chunk_cnt, s.perm_chunk, s.perm_chunks, s.T, s.H, s.k, s.E, s.G, s.shared};
   const long items = long(s.T) * (s.H / 8);
   const long nq = (items + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(k_route_quant, dim3(unsigned(1 + nq)), dim3(kThreads), 0, st, p);
+  const int nlead = s.perm_chunks == 1 ? 1 : s.perm_chunks;
+  hipLaunchKernelGGL(k_route_quant, dim3(unsigned(nlead + nq)), dim3(kThreads), 0, st, p);
+  if (s.perm_chunks > 1) hipLaunchKernelGGL(k_permute_rank, dim3(unsigned(s.perm_chunks)), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 

@@ -24,6 +24,9 @@ struct Shape {
   int g2_ntt;
   // groups with many rows (prefill) run the 256 x 256-token LDS-staged kernels
   int big;          // 1: both GEMMs use the big-tile kernels
+  // permute: slots per chunk and chunk count; one chunk = one block places
+  // every slot, more = a counting pass then one placing block per chunk
+  int perm_chunk, perm_chunks;
 };
 
 // Workspace carve (byte offsets from the caller's ws base; 256-aligned).
@@ -32,6 +35,7 @@ struct WsLayout {
   size_t xq, xs, hq, hs, y;                       // layer-internal activations
   size_t part1, part2;                            // split-K partial sums (fp32)
   size_t cnt1, cnt2;                              // split-K arrival counters (int32)
+  size_t chunk_cnt;                               // permute per-chunk expert counts (int32)
   size_t total;
 };
 
@@ -47,7 +51,7 @@ struct WeightPtrs {
 
 hipError_t launch_route_quant(const Shape& s, const uint16_t* x, const int32_t* ids, int32_t* counts,
                               int32_t* offsets, int32_t* expand_idx, int32_t* row_token, uint8_t* xq,
-                              float* xs, int32_t* clear, int nclear, hipStream_t st);
+                              float* xs, int32_t* clear, int nclear, int32_t* chunk_cnt, hipStream_t st);
 
 hipError_t launch_clear(int32_t* p, int n, hipStream_t st);
 

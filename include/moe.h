@@ -115,7 +115,10 @@ int moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
  *   row_token  int32 [T*topk + T*has_shared]: token of each row, -1 after
  *              the last row; shared rows are offsets[E] + t
  *   xq, xs     e4m3 codes uint8 [T][H] and fp32 scales [T][H/act_group]
- * ws / ws_bytes are unused (may be NULL / 0). */
+ * ws / ws_bytes: needed only when T*topk > 4096 (the slots are then placed
+ * in chunks whose counts live in the workspace): at least
+ * moe_workspace_size(cfg) bytes, else MOE_ERR_WORKSPACE / MOE_ERR_NULL_ARG;
+ * otherwise unused (may be NULL / 0). */
 int moe_permute(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, int32_t* counts,
                 int32_t* offsets, int32_t* expand_idx, int32_t* row_token, uint8_t* xq, float* xs,
                 void* ws, size_t ws_bytes, void* stream);

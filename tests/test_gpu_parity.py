@@ -144,6 +144,8 @@ def test_prepack_weights_bitexact(name):
 PERMUTE_CASES = [
     ("tiny_fp8", 16), ("decode_fp8", 1), ("decode_fp8", 8), ("decode_fp8", 256),
     ("decode_fp8_zipf_shared", 256), ("prefill_mxfp4", 4096), ("fp8_b32", 37), ("mxfp4_shared", 5),
+    # more than 4096 slots: counted and placed in chunks (the last one ragged)
+    ("mxfp4_shared", 3000), ("decode_fp8_zipf_shared", 700),
 ]
 
 
@@ -164,7 +166,7 @@ def test_permute_and_quant_bitexact(name, T):
 def test_permute_masked_duplicate_and_odd_expert_counts():
     moe = M()
     rng = np.random.default_rng(3)
-    for E, k, T in ((5, 3, 300), (64, 8, 1000), (1000, 4, 700), (1, 1, 129)):
+    for E, k, T in ((5, 3, 300), (64, 8, 1000), (1000, 4, 700), (1, 1, 129), (9, 8, 1100), (1000, 16, 600)):
         ids = rng.integers(0, E, size=(T, k)).astype(np.int32)     # duplicates allowed
         ids[rng.random((T, k)) < 0.15] = -1
         ids[0, 0] = E + 7
