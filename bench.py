@@ -11,7 +11,10 @@ weights; a warm call right after is timed too, as a diagnostic.  Inputs are synt
 seeded, and resident in HBM before timing starts.
 
 Output: one JSON line.  value = aggregate effective weight bandwidth over
-the sweep (touched-expert weight bytes / HIP-event layer time).
+the sweep (touched-expert weight bytes / HIP-event layer time).  After the
+timed decode steps, a "prefill" section measures the MXFP4 layer at T=4096
+(H=7168, E=256, top-8, I=2048): layer latency and TFLOP/s, per-stage times,
+and GEMM1's rate against the MFMA peak of its operand formats.
 """
 from __future__ import annotations
 
@@ -29,6 +32,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# dense MFMA peak for an e2m1 x e4m3 contraction: the scaled MFMA takes the
+# FP8 rate when either operand is FP8 (MI355X dense FP8: 5.0 PFLOP/s)
+MFMA_PEAK_TFLOPS = 5000.0
 FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm1_decode_fp8_T64.json")
 KERNEL_SRC = os.path.join(ROOT, "bit_grouped_gemm_amd", "csrc", "moe_kernels.hip")
@@ -43,6 +49,8 @@ def parse():
     ap.add_argument("--tokens", default=None, help="comma-separated T values (default: the workload's sweep)")
     ap.add_argument("--roofline-T", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the T=4096 MXFP4 prefill section")
+    ap.add_argument("--prefill-reps", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times): the known-size "
@@ -218,7 +226,70 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, w_rowmajor, cases[RT], RT, args.cpu_seconds)
+    if not args.no_prefill:
+        del cases, w, w_rowmajor, flush
+        torch.cuda.empty_cache()
+        line["prefill"] = prefill(moe, synth, torch, dev, args.prefill_reps)
     print(json.dumps(line), flush=True)
+
+
+def prefill(moe, synth, torch, dev, reps):
+    """The MXFP4 layer at T=4096: its 6 GB of weights exceed every cache, so
+    each call streams them from HBM."""
+    wl = synth.WORKLOADS["prefill_mxfp4"]
+    T = wl.tokens[0]
+    w_rm = synth.gen_weights(wl, seed=0, device=dev)
+    w = moe.moe_prepack_weights(moe.Cfg.for_workload(wl, 1), w_rm)
+    wbytes_all = w_rm.nbytes_expert() * wl.E
+    del w_rm
+    x, ids, tw = synth.gen_inputs(wl, T, seed=0, device=dev)
+    cfg = moe.Cfg.for_workload(wl, T)
+    ws = moe.workspace(cfg, dev)
+    out = torch.empty(T, wl.H, dtype=torch.bfloat16, device=dev)
+    flops = synth.layer_flops(wl, T, ids)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        moe.moe_layer(cfg, x, ids, tw, w, ws=ws, out=out)
+    lat, st = [], []
+    for _ in range(reps):
+        a, b = ev(), ev()
+        a.record()
+        moe.moe_layer(cfg, x, ids, tw, w, ws=ws, out=out)
+        b.record()
+        lat.append((a, b))
+        e = [ev() for _ in range(5)]
+        e[0].record()
+        _, offsets, eidx, rtok, xq, xs = moe.moe_permute(cfg, x, ids, ws)
+        e[1].record()
+        hq, hs = moe.moe_grouped_gemm1_swiglu(cfg, xq, xs, rtok, offsets, w, ws)
+        e[2].record()
+        y = moe.moe_grouped_gemm2(cfg, hq, hs, offsets, w, ws)
+        e[3].record()
+        moe.moe_combine(cfg, y, eidx, offsets, tw)
+        e[4].record()
+        st.append(e)
+        del y
+    torch.cuda.synchronize()
+    lat_us = np.array([a.elapsed_time(b) for a, b in lat]) * 1e3
+    stg = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in st]) * 1e3
+    med = float(np.median(lat_us))
+    stages = {n: round(float(np.median(stg[:, i])), 1) for i, n in
+              enumerate(["permute_quant", "gemm1_swiglu", "gemm2_fp32y", "combine_fp32y"])}
+    R = T * wl.topk
+    g1_flops = 2.0 * R * (2 * wl.I) * wl.H
+    g1_tf = g1_flops / (stages["gemm1_swiglu"] * 1e-6) / 1e12
+    tf = flops / (med * 1e-6) / 1e12
+    return {
+        "workload": f"{wl.name}: H={wl.H} E={wl.E} top-{wl.topk} I={wl.I} MXFP4 weights, T={T}",
+        "layer_us_median": round(med, 1), "layer_us_p10": round(float(np.percentile(lat_us, 10)), 1),
+        "layer_us_p90": round(float(np.percentile(lat_us, 90)), 1),
+        "TFLOPs": round(tf, 1), "mfma_peak_TFLOPs": MFMA_PEAK_TFLOPS, "mfma_frac": round(tf / MFMA_PEAK_TFLOPS, 4),
+        "weight_GBps": round(wbytes_all / (med * 1e-6) / 1e9, 1),
+        "stages_us_median": stages,
+        "gemm1_TFLOPs": round(g1_tf, 1), "gemm1_mfma_frac": round(g1_tf / MFMA_PEAK_TFLOPS, 4),
+        "reps": reps,
+        "note": "stage times use the stage exports (fp32 y); moe_layer keeps y in bf16",
+    }
 
 
 def cpu_baseline(wl, w, c, T, budget_s):
