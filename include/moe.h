@@ -5,12 +5,12 @@
  * per-token FP8 activation quantisation -> grouped GEMM1 (gate|up) over FP8
  * e4m3 or MXFP4 block-scaled expert weights with fused SwiGLU and
  * requantisation -> grouped GEMM2 -> top-k weighted combine back to token
- * order.  This is the local compute of the FP8/FP4 MoE operator in the
- * GC-MoE abstract ("grouped GEMMs, and a combine step"; "fused SwiGLU,
- * requantization, and optional shared experts") and the GMM1 -> SwiGLU ->
- * GMM2 -> combine chain of the FusedDeepMoE family analysis (unified
- * execution flow figure); the cross-GPU dispatch / all-to-all is not part
- * of it.
+ * order.  This is the local compute of the FP8/FP4 MoE operator of the
+ * GC-MoE abstract (its grouped GEMMs with SwiGLU and requantisation fused
+ * in, its combine step, and shared experts as an option) and the GMM1 ->
+ * SwiGLU -> GMM2 -> combine chain of the FusedDeepMoE family analysis
+ * (unified execution flow figure); the cross-GPU dispatch / all-to-all is
+ * not part of it.
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns
@@ -70,8 +70,8 @@ enum { MOE_WFMT_FP8_BLOCK = 0, MOE_WFMT_MXFP4 = 1 };
  *          the low nibble) with one e8m0 scale per 32 along K (wblk = 32);
  *          act_group must be 128.
  *   has_shared = 1 adds one always-on shared expert (same format and I) to
- *   every token with weight 1 (GC-MoE abstract, "optional shared experts";
- *   FusedDeepMoE shared-expert path: all tokens in one group).
+ *   every token with weight 1 (GC-MoE abstract: shared experts as an
+ *   option; FusedDeepMoE shared-expert path: all tokens in one group).
  * Limits: 1 <= E <= 1024, topk <= 32, H and I multiples of 128,
  *   T * topk < 2^24. */
 typedef struct moe_cfg {

@@ -8,25 +8,25 @@
 // What it computes (the plain definition; grouping, tiling and fusion on the
 // GPU only reorder floating-point sums):
 //   1. per-token activation quantisation to FP8 e4m3, one fp32 scale per
-//      group of G channels (FusedDeepMoE family analysis, "QuantToken"
+//      group of G channels (FusedDeepMoE family analysis, QuantToken
 //      snippet: multiplier = max-code / row max, code = round(x * multiplier),
 //      stored scale = 1 / multiplier; here e4m3 with max 448, per group);
 //   2. the local token permute: expert histogram, exclusive prefix-scan
 //      offsets (the group list) and a stable expand index (same page,
-//      "gmGroupList" / "gmExpandIdx" workspace objects and
-//      "CalAndSendTokenCount");
+//      gmGroupList / gmExpandIdx workspace objects and the
+//      CalAndSendTokenCount step);
 //   3. grouped GEMM1 over the gate|up weights with per-token / per-block
-//      dequantisation ("OpDequant": value = integer dot * weight scale *
-//      per-token scale), SwiGLU ("OpSwiglu": left half through SiLU times
-//      right half) and requantisation ("OpBlockQuant" / "BlockQuant"), as in
-//      the GC-MoE abstract's "fused SwiGLU, requantization";
+//      dequantisation (OpDequant: value = integer dot * weight scale *
+//      per-token scale), SwiGLU (OpSwiglu: left half through SiLU times
+//      right half) and requantisation (OpBlockQuant / BlockQuant), the
+//      fusion the GC-MoE abstract describes for its grouped GEMM;
 //   4. grouped GEMM2 with the same dequantisation;
-//   5. the top-k weighted combine back to token order ("ReducePermute":
+//   5. the top-k weighted combine back to token order (ReducePermute:
 //      accumulate each token's expert outputs), plus an always-on shared
-//      expert with weight 1 (GC-MoE abstract, "optional shared experts";
+//      expert with weight 1 (GC-MoE abstract: shared experts as an option;
 //      FusedDeepMoE shared-expert path: all tokens, one group).
 //
-// Number formats (the pages name "FP8/FP4" and MXFP4 but print no bit
+// Number formats (the pages name FP8, FP4 and MXFP4 but print no bit
 // layouts; these are the OCP 8-bit float E4M3FN and Microscaling e2m1 /
 // e8m0 definitions, rebuilt from sign / exponent / mantissa fields):
 //   e4m3: bias 7, no infinities, S.1111.111 is NaN, max 448, subnormal step 2^-9
