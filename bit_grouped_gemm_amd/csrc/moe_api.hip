@@ -15,8 +15,12 @@ namespace moe {
 #ifndef MOE_SPLIT_TARGET_WG
 #define MOE_SPLIT_TARGET_WG 256
 #endif
-#ifndef MOE_BIG_MIN_AVG_ROWS
-#define MOE_BIG_MIN_AVG_ROWS 48
+// average rows per touched group from which the big-tile kernels take over
+#ifndef MOE_BIG_MIN_AVG_ROWS_FP8
+#define MOE_BIG_MIN_AVG_ROWS_FP8 24
+#endif
+#ifndef MOE_BIG_MIN_AVG_ROWS_FP4
+#define MOE_BIG_MIN_AVG_ROWS_FP4 16
 #endif
 #ifndef MOE_SPLIT_MIN_KSTEPS
 #define MOE_SPLIT_MIN_KSTEPS 4
@@ -76,8 +80,12 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   const double groups = std::fmin(double(E), double(T) * k);
   const double avg_rows = groups > 0 ? double(T) * k / groups : 0.0;
   // the big-tile kernels keep a pass's token scales in LDS: K <= 8192 for both GEMMs
+  const double min_rows = wfmt == 1 ? MOE_BIG_MIN_AVG_ROWS_FP4 : MOE_BIG_MIN_AVG_ROWS_FP8;
   s.big = (G == 128 && (wfmt == 1 || wblk == 128) && H % 256 == 0 && H <= 8192 && I <= 8192 &&
-           avg_rows >= MOE_BIG_MIN_AVG_ROWS) ? 1 : 0;
+           avg_rows >= min_rows) ? 1 : 0;
+  // 64 rows per pass while nearly every group fits (mean + 3 sd of a
+  // Poisson count), which leaves LDS for a deeper ring; 160 beyond
+  s.big_cap = avg_rows + 3.0 * std::sqrt(avg_rows) + 1.0 <= 64.0 ? 64 : 160;
   if (s.big) s.g1_split = s.g2_split = 1;
   // permute: one block places up to 4096 slots; beyond that the slots are
   // split into at most 64 chunks of at least 2048, each placed by its own

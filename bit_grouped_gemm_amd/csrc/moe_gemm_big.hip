@@ -39,33 +39,37 @@ namespace moe {
 namespace {
 
 constexpr int kBigThreads = 512;
-constexpr int kTokCap = 160;                 // token rows per pass
-constexpr int kTokTiles = kTokCap / 16;      // 10
 constexpr int kWTiles = 16;                  // 256 weight rows
-constexpr int kBBytes = kTokTiles * 2048;     // token tiles: 16 rows x 128 B, chunk-swizzled
+constexpr int kAsBytes = 8 * 64 * 4;         // MXFP4 scales: one dword (4 x e8m0) per lane of 8 waves
 constexpr int kMaxKSteps = 64;              // K <= 8192: the pass's token scales fit one LDS table
 constexpr int kXsRow = kMaxKSteps + 1;       // floats per token row of the table (odd: no bank conflicts)
-constexpr int kAsBytes = 8 * 64 * 4;         // MXFP4 scales: one dword (4 x e8m0) per lane of 8 waves
-constexpr int kTokPerWave = kTokTiles / 2;   // token tiles of one wave column
 constexpr int kSinkBytes = 1024;             // target of token loads past the pass's tiles
 
-template <int WF> struct BigGeo {
-  static constexpr int kStages = WF == 1 ? 3 : 2;
+// Geometry of one instantiation: weight format WF and token rows per pass
+// CAP (160 for prefill-sized groups; 64 when groups are smaller, which
+// leaves LDS for a three-stage ring with e4m3 weights too).
+template <int WF, int CAP> struct BigGeo {
+  static constexpr int kTokCap = CAP;
+  static constexpr int kTokTiles = CAP / 16;
+  static constexpr int kTokPerWave = kTokTiles / 2;       // token tiles of one wave column
+  static constexpr int kTokLoads = (2 * kTokTiles + 7) / 8;  // token-row loads per wave per step
+  static constexpr int kBBytes = kTokTiles * 2048;        // token tiles: 16 rows x 128 B, chunk-swizzled
+  static constexpr int kStages = (WF == 1 || CAP <= 64) ? 3 : 2;
   static constexpr int kABytes = kWTiles * 1024 * (WF == 1 ? 1 : 2);
   static constexpr int kAOff = kBBytes;
   static constexpr int kAsOff = kAOff + kABytes;
   static constexpr int kSinkOff = kAsOff + (WF == 1 ? kAsBytes : 0);
   static constexpr int kStageBytes = kSinkOff + kSinkBytes;
-  // direct-to-LDS loads per wave per stage: token rows 3, weight tiles 2
+  // direct-to-LDS loads per wave per stage: token rows, weight tiles 2
   // (MXFP4) or 4 (e4m3 halves), MXFP4 scales 1
-  static constexpr int kLoadsPerStage = 3 + (WF == 1 ? 2 + 1 : 4);
-  static constexpr int kXsTabBytes = kTokCap * kXsRow * 4;  // [token][k step] fp32
+  static constexpr int kLoadsPerStage = kTokLoads + (WF == 1 ? 2 + 1 : 4);
+  static constexpr int kXsTabBytes = CAP * kXsRow * 4;    // [token][k step] fp32
   static constexpr int kLdsBytes = kStages * kStageBytes + kXsTabBytes;
+  static_assert(kTokPerWave <= 6, "three pairs of token tiles, one load part after each");
+  static_assert(kTokLoads <= 3, "token-row loads fit the three load parts");
+  static_assert(4 * CAP * 4 <= kStageBytes, "epilogue maxima fit one stage");
+  static_assert(kLdsBytes + 1024 <= 160 * 1024, "ring, scale table and small arrays fit the 160 KB LDS");
 };
-static_assert(BigGeo<1>::kLdsBytes + 1024 <= 160 * 1024, "MXFP4 ring, scale table and small arrays fit the 160 KB LDS");
-static_assert(4 * kTokCap * 4 <= BigGeo<0>::kStageBytes, "epilogue maxima fit one stage");
-static_assert(BigGeo<0>::kLdsBytes + 1024 <= 160 * 1024, "e4m3 ring, scale table and small arrays fit the 160 KB LDS");
-static_assert(kTokTiles * 2 <= 3 * 8, "at most three token-row loads per wave");
 
 struct BigParams {
   const uint8_t* act;        // GEMM1: xq [T][H] by token; GEMM2: hq [rows][I] by row
@@ -117,9 +121,10 @@ __device__ __forceinline__ void ring_barrier() {
 
 }  // namespace
 
-template <int WF, int MODE>
+template <int WF, int MODE, int CAP>
 __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
-  using Geo = BigGeo<WF>;
+  using Geo = BigGeo<WF, CAP>;
+  constexpr int kTokCap = Geo::kTokCap, kTokPerWave = Geo::kTokPerWave, kTokLoads = Geo::kTokLoads;
   constexpr int S = Geo::kStages;
   // one array per ring stage: the compiler's alias analysis then tells the
   // stages apart and waits for a stage's own direct-to-LDS loads only
@@ -217,13 +222,13 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
     // 128 B (load i: tile i / 2, rows 8 (i % 2) .. + 7), dealt round-robin to
     // the waves (load q of wave w is i = w + 8 q).  Lane l fills LDS chunk
     // l % 8 of row l / 8, i.e. global chunk (l % 8) ^ (row & 7).  Rows past
-    // the group repeat its last row.  Every wave issues three such loads per
-    // step; the ones past the pass's tiles read one 16-byte chunk with all
-    // lanes into the stage's sink, so every step has the same load count.
-    const uint8_t* b_src[3];
-    int b_dst[3];
+    // the group repeat its last row.  Every wave issues kTokLoads such loads
+    // per step; the ones past the pass's tiles read one 16-byte chunk with
+    // all lanes into the stage's sink, so every step has the same load count.
+    const uint8_t* b_src[kTokLoads];
+    int b_dst[kTokLoads];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
+    for (int q = 0; q < kTokLoads; ++q) {
       const int i = w + 8 * q;
       const int rl = (i & 1) * 8 + (lane >> 3);
       const bool real = i < 2 * ntt;
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
     }
     // token scales of the whole pass, read once into a [token][k step]
     // table: one direct-to-LDS load per token (its K/128 scales are
-    // contiguous; lanes past them repeat the last one), 20 per wave.  Being
+    // contiguous; lanes past them repeat the last one), CAP / 8 per wave.  Being
     // direct loads into their own array, the table's reads wait only for
     // these loads, not for the ring's.
     for (int tk = w; tk < kTokCap; tk += 8) {
@@ -262,8 +267,8 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
         if (WF == 1) dma4(as_src + ks * sstep, st + Geo::kAsOff + w * 256);
         dma16(b_src[0] + long(ks) * 128, st + b_dst[0]);
       } else {
-        dma16(b_src[1] + long(ks) * 128, st + b_dst[1]);
-        dma16(b_src[2] + long(ks) * 128, st + b_dst[2]);
+#pragma unroll
+        for (int q = 1; q < kTokLoads; ++q) dma16(b_src[q] + long(ks) * 128, st + b_dst[q]);
       }
     };
     // pinned in place among the MFMAs: the load pipeline drains while the
@@ -329,7 +334,6 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
           xsp[tt] = xsv[tt];
         }
       }
-      static_assert(kTokPerWave <= 6, "three pairs of token tiles, one load part after each");
 #pragma unroll
       for (int t0 = 0; t0 < 6; t0 += 2) {
         issue_part(ksn, nxt, t0 / 2);
@@ -471,13 +475,19 @@ static hipError_t launch_big(const Shape& s, int mode, BigParams& p, hipStream_t
   p.per_xcd = (units + 7) / 8;
   const unsigned grid = unsigned(p.per_xcd) * 8;
   const size_t lds = 0;  // static LDS
+#define MOE_BIG_LAUNCH(WF, CAP)                                                                   \
+  do {                                                                                            \
+    if (mode == 0) hipLaunchKernelGGL((k_gemm_big<WF, 0, CAP>), dim3(grid), dim3(kBigThreads), lds, st, p); \
+    else hipLaunchKernelGGL((k_gemm_big<WF, 1, CAP>), dim3(grid), dim3(kBigThreads), lds, st, p);           \
+  } while (0)
   if (s.wfmt == 0) {
-    if (mode == 0) hipLaunchKernelGGL((k_gemm_big<0, 0>), dim3(grid), dim3(kBigThreads), lds, st, p);
-    else hipLaunchKernelGGL((k_gemm_big<0, 1>), dim3(grid), dim3(kBigThreads), lds, st, p);
+    if (s.big_cap == 64) MOE_BIG_LAUNCH(0, 64);
+    else MOE_BIG_LAUNCH(0, 160);
   } else {
-    if (mode == 0) hipLaunchKernelGGL((k_gemm_big<1, 0>), dim3(grid), dim3(kBigThreads), lds, st, p);
-    else hipLaunchKernelGGL((k_gemm_big<1, 1>), dim3(grid), dim3(kBigThreads), lds, st, p);
+    if (s.big_cap == 64) MOE_BIG_LAUNCH(1, 64);
+    else MOE_BIG_LAUNCH(1, 160);
   }
+#undef MOE_BIG_LAUNCH
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ struct Shape {
   int g2_ntt;
   // groups with many rows (prefill) run the 256 x 256-token LDS-staged kernels
   int big;          // 1: both GEMMs use the big-tile kernels
+  int big_cap;      // their token rows per pass: 64 or 160
   // permute: slots per chunk and chunk count; one chunk = one block places
   // every slot, more = a counting pass then one placing block per chunk
   int perm_chunk, perm_chunks;

@@ -374,7 +374,7 @@ BIG = {
 
 
 @pytest.mark.parametrize("name", list(BIG))
-@pytest.mark.parametrize("T", [200, 700])
+@pytest.mark.parametrize("T", [80, 200, 700])  # 80: 64-row passes (the shared group takes two)
 def test_layer_big_tiles(name, T):
     moe = M()
     wl = BIG[name]
