@@ -47,6 +47,18 @@ __device__ __forceinline__ uint32_t enc_e4m3(float v) {
   return code | sign;
 }
 
+// Four fp32 -> four e4m3 codes (byte i = value i) with the same rounding as
+// enc_e4m3, by the hardware conversion: the values are clamped to +-448 (the
+// saturation) and converted two at a time with round-to-nearest-even.  This
+// was checked against enc_e4m3 on every finite fp32 bit pattern (all 2^32
+// minus inf/NaN, on an MI355X): identical codes, signed zeros included.
+__device__ __forceinline__ uint32_t enc_e4m3x4(float a, float b, float c, float d) {
+  const auto sat = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+  return uint32_t(w);
+}
+
 // Quantisation multiplier and dequant scale of a group with absolute max a.
 __device__ __forceinline__ float quant_mult(float amax) { return 448.0f / fmaxf(amax, 0x1p-64f); }
 

@@ -111,6 +111,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // while a direct-to-LDS load still covers 8 whole rows (full cache lines)
 __device__ __forceinline__ int tok_swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
 
+// instruction classes the scheduler may move across a load-issue point (the
+// sched_barrier mask): ALU, VALU, SALU, MFMA, LDS reads, transcendentals --
+// not the vector-memory loads themselves
+constexpr int kSchedMayCross = 0x0001 | 0x0002 | 0x0004 | 0x0008 | 0x0100 | 0x0400;
+
 // workgroup barrier that the compiler may not move memory operations across;
 // the waits for the ring's direct-to-LDS loads are explicit (wait_vmcnt)
 __device__ __forceinline__ void ring_barrier() {
@@ -273,10 +278,11 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
     };
     // pinned in place among the MFMAs: the load pipeline drains while the
     // matrix cores work instead of taking every wave's loads in one burst
+    // (ALU, MFMA and LDS reads may still be scheduled across the point)
     auto issue_part = [&](int ks, uint8_t* st, int part) __attribute__((always_inline)) {
-      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(kSchedMayCross);
       issue(ks, st, part);
-      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(kSchedMayCross);
     };
 
     // accumulators: e4m3 weights promote each step's MFMA result with a VALU
@@ -445,9 +451,8 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
         const long r = row0 + pass0 + idx;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) word |= enc_e4m3(acc[q][tt][i] * mult) << (8 * i);
+          const v4f& hv = acc[q][tt];
+          const uint32_t word = enc_e4m3x4(hv[0] * mult, hv[1] * mult, hv[2] * mult, hv[3] * mult);
           *reinterpret_cast<uint32_t*>(p.hq + r * I + n0 + 32 * wr + 16 * q + 4 * g) = word;
         }
         if (g == 0 && wr == 0) p.hs[r * (I / 128) + n0 / 128] = 1.0f / mult;

@@ -217,9 +217,8 @@ __device__ void quant_block(const RouteParams& p, int blk) {
   for (int msk = 1; msk < lanes; msk <<= 1) amax = wave_max_xor(amax, msk);
   if (item < items) {
     const float mult = quant_mult(amax);
-    uint32_t lo = 0, hi = 0;
-    for (int q = 0; q < 4; ++q) lo |= enc_e4m3(f[q] * mult) << (8 * q);
-    for (int q = 0; q < 4; ++q) hi |= enc_e4m3(f[4 + q] * mult) << (8 * q);
+    const uint32_t lo = enc_e4m3x4(f[0] * mult, f[1] * mult, f[2] * mult, f[3] * mult);
+    const uint32_t hi = enc_e4m3x4(f[4] * mult, f[5] * mult, f[6] * mult, f[7] * mult);
     uint2 o;
     o.x = lo;
     o.y = hi;
@@ -488,9 +487,8 @@ __device__ __forceinline__ void swiglu_requant_store(const v4f (&acc)[4][NTT], c
     const float mult = quant_mult(amax[t]);
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) word |= enc_e4m3(h[t][jt * 4 + i] * mult) << (8 * i);
+      const float* hv = h[t] + jt * 4;
+      const uint32_t word = enc_e4m3x4(hv[0] * mult, hv[1] * mult, hv[2] * mult, hv[3] * mult);
       *reinterpret_cast<uint32_t*>(p.hq + r * p.I + n0 + 32 * w + 16 * jt + 4 * g) = word;
     }
     if (g == 0) {
