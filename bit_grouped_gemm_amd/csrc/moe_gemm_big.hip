@@ -3,14 +3,14 @@
 // When an expert holds ~100+ token rows (prefill: T = 4096, top-8 over 256
 // experts gives ~128 rows per expert) a workgroup must cover all of them
 // per pass, or each weight byte is read from HBM once per pass.  Here a
-// workgroup of 8 waves owns 256 weight rows and up to 192 token rows, and
-// walks K in steps of 128:
+// workgroup of 8 waves owns 256 weight rows (a "unit") and up to CAP token
+// rows (a "pass"), and walks K in steps of 128:
 //   * both operands of a step travel HBM/L2 -> LDS by direct-to-LDS loads
-//     (global_load_lds_dwordx4: 64 lanes x 16 B into 1 KB of LDS per
-//     instruction, no registers held while in flight) through a ring of
-//     stages (three for MXFP4 weights, two for e4m3 weights whose steps are
-//     twice as large), so two steps of weights and token rows are in
-//     flight while one is multiplied;
+//     (global_load_lds: 64 lanes x 16 B into 1 KB of LDS per instruction,
+//     no registers held while in flight) through a ring of up to four
+//     stages; a stage holds the step's token rows, weight tiles, MXFP4
+//     scales (or the two e4m3 block scales) and the pass's token scales of
+//     that step, so nothing else is read from memory in the K loop;
 //   * weights come from the tiled layout (16-row x 128-K tiles in MFMA lane
 //     order, see moe_tile.hip), one contiguous kilobyte per tile and step,
 //     and land in LDS unchanged, so fragment reads are linear ds_read_b128;
@@ -18,19 +18,26 @@
 //     whose fragment reads are conflict-free as well;
 //   * the 8 waves form a 4 x 2 grid: a wave owns 4 weight tiles (64 rows;
 //     in GEMM1 two gate and the two matching up tiles, so SwiGLU pairs meet
-//     in one lane) and every second token tile, which keeps up to 4 x 6
-//     fp32 accumulator tiles in registers and reads each token fragment
-//     once per 4 MFMAs;
-//   * one vmcnt wait and one barrier per step: each wave waits for its own
-//     loads of the step, the barrier makes every wave's loads visible, and
-//     the loads two steps ahead are issued after the barrier, into the
-//     stage every wave has finished reading;
-//   * all tiles of one expert are dispatched to the same XCD (workgroup
-//     ids are dealt round-robin over the 8 XCDs), so the expert's token rows
-//     are fetched into that XCD's L2 once and re-read from there.
+//     in one lane) and every second token tile, which keeps up to 4 x 5
+//     fp32 accumulator tiles in registers;
+//   * ping-pong: the two wave columns (one wave of each per SIMD) take turns
+//     -- while column 0 reads step k's fragments out of LDS and rescales its
+//     accumulators, column 1 multiplies step k - 1 from registers, and the
+//     other way round in the next half step -- so each SIMD's matrix core
+//     is fed by one wave while the other waits on LDS, instead of all eight
+//     waves waiting on the same read burst after each barrier;
+//   * the kernel is persistent (one workgroup per CU) and all tiles of one
+//     expert run on one XCD (workgroup ids are dealt round-robin over the 8
+//     XCDs), so the expert's token rows are fetched into that XCD's L2 once;
+//     each workgroup finds its units' groups once (a table in LDS), loads
+//     the next pass's token-row indices while the current pass runs, and
+//     issues the next pass's first ring stages before its epilogue.
 // GEMM1 mode: weight rows are 128 gate + 128 up rows (128 h columns = one
 // requantisation group of 128), epilogue SwiGLU + FP8 requantisation.
 // GEMM2 mode: 256 output rows, epilogue writes y.
+#include <algorithm>
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -39,41 +46,48 @@ namespace moe {
 namespace {
 
 constexpr int kBigThreads = 512;
-constexpr int kWTiles = 16;                  // 256 weight rows
-constexpr int kAsBytes = 8 * 64 * 4;         // MXFP4 scales: one dword (4 x e8m0) per lane of 8 waves
-constexpr int kMaxKSteps = 64;              // K <= 8192: the pass's token scales fit one LDS table
-constexpr int kXsRow = kMaxKSteps + 1;       // floats per token row of the table (odd: no bank conflicts)
-constexpr int kSinkBytes = 1024;             // target of token loads past the pass's tiles
+constexpr int kWTiles = 16;           // 256 weight rows per unit
+constexpr int kTabCap = 96;           // units of one workgroup described by one table build
+constexpr int kLdsLimit = 160 * 1024;
+constexpr int kMaxKSteps = 64;        // K <= 8192: a pass's token scales fit one table
+constexpr int kXsRow = kMaxKSteps + 1;  // floats per table row (odd: conflict-free column reads)
 
 // Geometry of one instantiation: weight format WF and token rows per pass
-// CAP (160 for prefill-sized groups; 64 when groups are smaller, which
-// leaves LDS for a three-stage ring with e4m3 weights too).
+// CAP (160 for prefill-sized groups, 64 when groups are smaller).  Every
+// wave issues the same kL direct-to-LDS loads of 16 bytes per lane per step
+// (token rows, weight tiles, MXFP4 scales; spare slots load one hot line
+// into the stage's sink).  A pass's token scales, [token][k step], and the
+// unit's two e4m3 block-scale rows are read once per pass into tables.
 template <int WF, int CAP> struct BigGeo {
-  static constexpr int kTokCap = CAP;
   static constexpr int kTokTiles = CAP / 16;
-  static constexpr int kTokPerWave = kTokTiles / 2;       // token tiles of one wave column
-  static constexpr int kTokLoads = (2 * kTokTiles + 7) / 8;  // token-row loads per wave per step
-  static constexpr int kBBytes = kTokTiles * 2048;        // token tiles: 16 rows x 128 B, chunk-swizzled
-  static constexpr int kStages = (WF == 1 || CAP <= 64) ? 3 : 2;
-  static constexpr int kABytes = kWTiles * 1024 * (WF == 1 ? 1 : 2);
-  static constexpr int kAOff = kBBytes;
-  static constexpr int kAsOff = kAOff + kABytes;
-  static constexpr int kSinkOff = kAsOff + (WF == 1 ? kAsBytes : 0);
-  static constexpr int kStageBytes = kSinkOff + kSinkBytes;
-  // direct-to-LDS loads per wave per stage: token rows, weight tiles 2
-  // (MXFP4) or 4 (e4m3 halves), MXFP4 scales 1
-  static constexpr int kLoadsPerStage = kTokLoads + (WF == 1 ? 2 + 1 : 4);
-  static constexpr int kXsTabBytes = CAP * kXsRow * 4;    // [token][k step] fp32
-  static constexpr int kLdsBytes = kStages * kStageBytes + kXsTabBytes;
-  static_assert(kTokPerWave <= 6, "three pairs of token tiles, one load part after each");
-  static_assert(kTokLoads <= 3, "token-row loads fit the three load parts");
-  static_assert(4 * CAP * 4 <= kStageBytes, "epilogue maxima fit one stage");
-  static_assert(kLdsBytes + 1024 <= 160 * 1024, "ring, scale table and small arrays fit the 160 KB LDS");
+  static constexpr int kTokPerWave = kTokTiles / 2;          // token tiles of one wave column
+  static constexpr int kTokLoads = 2 * kTokTiles;            // 8 rows x 128 B each
+  static constexpr int kTokSlots = (kTokLoads + 7) / 8;      // token-row loads of one wave
+  static constexpr int kWLoads = WF == 1 ? kWTiles : 2 * kWTiles;  // 1 KB each
+  static constexpr int kScLoads = WF == 1 ? 1 : 0;           // 16 tiles x 64 B of e8m0 scales
+  static constexpr int kL = (kTokLoads + kWLoads + kScLoads + 7) / 8;
+  static constexpr int kWOff = kTokTiles * 2048;             // token tiles: 16 rows x 128 B, chunk-swizzled
+  static constexpr int kScOff = kWOff + kWLoads * 1024;
+  static constexpr int kSinkOff = kScOff + kScLoads * 1024;
+  static constexpr int kStageBytes = kSinkOff + 1024;
+  static constexpr int kXsTabFloats = CAP * kXsRow;           // token scales of the pass
+  static constexpr int kWsTabFloats = WF == 0 ? 2 * kXsRow : 1;  // e4m3 block scales of the unit
+  static constexpr int kTabLoads = (CAP + 7) / 8;            // token-scale rows per wave
+  static constexpr int kRedFloats = 4 * CAP;                 // epilogue maxima: per wave row, per token
+  static constexpr int kFixedBytes = (kXsTabFloats + kWsTabFloats + kRedFloats) * 4 + kTabCap * 16 + 64;
+  static constexpr int kStagesFit = (kLdsLimit - kFixedBytes) / kStageBytes;
+  static constexpr int kStages = kStagesFit < 4 ? kStagesFit : 4;
+  static_assert(kStageBytes % 256 == 0, "stage alignment");
+  static_assert(kStages >= 2, "a ring of two stages at least");
+  static_assert(kTabLoads <= 64, "token-scale rows of a wave fit one register");
+  static_assert(kTokPerWave <= 5, "token tiles per wave");
+  static_assert(kTokSlots <= 3, "token-row loads per wave");
+  static_assert((kStages - 2) * kL < 64, "vmcnt range");
 };
 
 struct BigParams {
   const uint8_t* act;        // GEMM1: xq [T][H] by token; GEMM2: hq [rows][I] by row
-  const float* act_s;
+  const float* act_s;        // its per-128 scales
   const int32_t* row_token;  // GEMM1 only (null in GEMM2 mode)
   const int32_t* offsets;
   const uint8_t* w;
@@ -116,10 +130,13 @@ __device__ __forceinline__ int tok_swz(int r, int c) { return r * 128 + ((c ^ (r
 // not the vector-memory loads themselves
 constexpr int kSchedMayCross = 0x0001 | 0x0002 | 0x0004 | 0x0008 | 0x0100 | 0x0400;
 
-// workgroup barrier that the compiler may not move memory operations across;
-// the waits for the ring's direct-to-LDS loads are explicit (wait_vmcnt)
-__device__ __forceinline__ void ring_barrier() {
+// workgroup barrier after this wave's LDS reads and writes have completed;
+// outstanding vector-memory loads stay in flight (unlike __syncthreads,
+// whose release fence waits for them): the waits for the ring's
+// direct-to-LDS loads are explicit (wait_vmcnt)
+__device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), other counters at their maxima
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -129,24 +146,53 @@ __device__ __forceinline__ void ring_barrier() {
 template <int WF, int MODE, int CAP>
 __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
   using Geo = BigGeo<WF, CAP>;
-  constexpr int kTokCap = Geo::kTokCap, kTokPerWave = Geo::kTokPerWave, kTokLoads = Geo::kTokLoads;
-  constexpr int S = Geo::kStages;
+  constexpr int S = Geo::kStages, L = Geo::kL, NTMAX = Geo::kTokPerWave;
   // one array per ring stage: the compiler's alias analysis then tells the
   // stages apart and waits for a stage's own direct-to-LDS loads only
-  __shared__ __align__(1024) uint8_t st0[Geo::kStageBytes];
-  __shared__ __align__(1024) uint8_t st1[Geo::kStageBytes];
-  __shared__ __align__(1024) uint8_t st2[S == 3 ? Geo::kStageBytes : 16];
-  __shared__ __align__(16) float xs_tab[kTokCap * kXsRow];  // token scales of the pass
-  __shared__ int s_wsum[8], s_res;
+  __shared__ __align__(256) uint8_t st0[Geo::kStageBytes];
+  __shared__ __align__(256) uint8_t st1[Geo::kStageBytes];
+  __shared__ __align__(256) uint8_t st2[S >= 3 ? Geo::kStageBytes : 256];
+  __shared__ __align__(256) uint8_t st3[S >= 4 ? Geo::kStageBytes : 256];
+  __shared__ __align__(16) float xs_tab[Geo::kXsTabFloats];
+  __shared__ __align__(16) float ws_tab[Geo::kWsTabFloats];
+  __shared__ __align__(16) float red[Geo::kRedFloats];
+  __shared__ int4 tab[kTabCap];  // per unit of this workgroup: group, first row, rows, tile in group
+  __shared__ int s_wsum[8];
 
-  // ---- unit: XCD-aware order (blockIdx -> XCD is round-robin over 8)
-  const int xcd = blockIdx.x & 7, k_in = blockIdx.x >> 3;
-  const int u = xcd * p.per_xcd + k_in;
-  if (k_in >= p.per_xcd || u >= p.units) return;
-  const int slot = u / p.ntiles, tile = u % p.ntiles;
   const int tid = threadIdx.x;
-  // slot-th group with at least min_rows rows
-  {
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 15, g = lane >> 4;
+  const int wr = w & 3, wc = w >> 2;     // wave row (weight tiles), wave column (token tiles, ping-pong side)
+  const int H = p.H, I = p.I;
+  const int K = MODE == 0 ? H : I;       // reduction length
+  const int NR = MODE == 0 ? 2 * I : H;  // weight rows of the matrix
+  const int kb = WF == 0 ? K : K / 2;    // bytes per weight row
+  const int nks = K / 128;
+  const long wstep = long(NR / 16) * kTileBytes<WF>;  // tiled weights: bytes per K step
+  const long sstep = long(NR / 16) * kTileScaleBytes;
+  // this wave's weight tiles among the unit's 16 (GEMM1: tiles 0..7 are gate
+  // rows, 8..15 the up rows of the same h columns; GEMM2 rows in order)
+  int ja[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ja[q] = MODE == 0 ? (q < 2 ? 2 * wr + q : 8 + 2 * wr + (q - 2)) : 4 * wr + q;
+
+  // ---- the units of this workgroup: workgroup ids are dealt round-robin
+  // over the 8 XCDs, and XCD x works through units [x per_xcd, (x + 1)
+  // per_xcd) with its nwx workgroups, unit i of this one being
+  // x per_xcd + j0 + i nwx, so all tiles of one group run on one XCD and
+  // share its L2
+  const int xcd = blockIdx.x & 7, j0 = blockIdx.x >> 3, nwx = gridDim.x >> 3;
+  const int ubase = xcd * p.per_xcd;
+  const int kmax = min(p.per_xcd, p.units - ubase);
+  const int nunits = kmax > j0 ? (kmax - j0 + nwx - 1) / nwx : 0;
+  if (nunits <= 0) return;
+
+  // table of units i0 .. i0 + kTabCap - 1: unit u belongs to slot u / ntiles,
+  // slot r being the r-th group with at least min_rows rows; units past the
+  // last such group keep group -1.  Every wave takes part (two barriers).
+  int tab0 = 0;
+  auto build_table = [&](int i0) __attribute__((always_inline)) {
+    tab0 = i0;
+    for (int idx = tid; idx < kTabCap; idx += kBigThreads) tab[idx] = make_int4(-1, 0, 0, 0);
     const int gpt = (p.ngroups + kBigThreads - 1) / kBigThreads;
     int local = 0;
     for (int q = 0; q < gpt; ++q) {
@@ -154,322 +200,470 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
       if (gg < p.ngroups && p.offsets[gg + 1] - p.offsets[gg] >= p.min_rows) ++local;
     }
     int incl = local;
-    const int ln = tid & 63, wv = tid >> 6;
     for (int d = 1; d < 64; d <<= 1) {
       const int v = __shfl_up(incl, d, 64);
-      if (ln >= d) incl += v;
+      if (lane >= d) incl += v;
     }
-    if (tid == 0) s_res = -1;
-    if (ln == 63) s_wsum[wv] = incl;
-    __syncthreads();
-    int run = incl - local;
-    for (int q = 0; q < wv; ++q) run += s_wsum[q];
-    if (slot >= run && slot < run + local) {
-      int c = run;
-      for (int q = 0; q < gpt; ++q) {
-        const int gg = tid * gpt + q;
-        if (gg < p.ngroups && p.offsets[gg + 1] - p.offsets[gg] >= p.min_rows) {
-          if (c == slot) s_res = gg;
-          ++c;
-        }
+    if (lane == 63) s_wsum[w] = incl;
+    lds_barrier();
+    int r = incl - local;
+    for (int q = 0; q < w; ++q) r += s_wsum[q];
+    for (int q = 0; q < gpt; ++q) {
+      const int gg = tid * gpt + q;
+      if (gg >= p.ngroups) break;
+      const int o0 = p.offsets[gg], cnt = p.offsets[gg + 1] - o0;
+      if (cnt < p.min_rows) continue;
+      // this workgroup's units of slot r
+      const int ulo = max(r * p.ntiles, ubase + j0), uhi = min((r + 1) * p.ntiles, ubase + kmax);
+      for (int u = ulo + (nwx - (ulo - ubase - j0) % nwx) % nwx; u < uhi; u += nwx) {
+        const int ii = (u - ubase - j0) / nwx - i0;
+        if (ii >= 0 && ii < kTabCap) tab[ii] = make_int4(gg, o0, cnt, u - r * p.ntiles);
+      }
+      ++r;
+    }
+    lds_barrier();
+  };
+
+  // ---- per-lane token index of this wave's token-row load slot j (load
+  // i = w + 8 j < kTokLoads: tile i / 2, rows 8 (i % 2) .. + 7, lane l on
+  // row 8 (i % 2) + l / 8); the wave's token-scale table rows are tokens
+  // w + 8 i (lane i holds the row of the i-th); rows past the pass repeat
+  // its last row
+  auto tok_of_slot = [&](int j) __attribute__((always_inline)) { const int i = w + 8 * j; return (i >> 1) * 16 + (i & 1) * 8 + (lane >> 3); };
+  int pf_row[Geo::kTokSlots], pf_tab = 0;  // rows of the next pass to load (GEMM1: token ids)
+  bool pf_ok = false;
+  auto prefetch = [&](int4 ent, int pass) __attribute__((always_inline)) {
+    const int npass = min(CAP, ent.z - pass * CAP);
+    const int base = ent.y + pass * CAP;
+#pragma unroll
+    for (int j = 0; j < Geo::kTokSlots; ++j) {
+      pf_row[j] = 0;
+      if (w + 8 * j < Geo::kTokLoads) {
+        const int r = base + min(tok_of_slot(j), npass - 1);
+        pf_row[j] = MODE == 0 ? p.row_token[r] : r;
       }
     }
-    __syncthreads();
-  }
-  const int e = s_res;
-  if (e < 0) return;
-  const int row0 = p.offsets[e], ne = p.offsets[e + 1] - row0;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 15, g = lane >> 4;
-  const int wr = w & 3, wc = w >> 2;     // wave row (weight tiles), wave column (token tiles)
-  const int H = p.H, I = p.I;
-  const int K = MODE == 0 ? H : I;       // reduction length
-  const int NR = MODE == 0 ? 2 * I : H;  // weight rows of the matrix
-  const int n0 = tile * (MODE == 0 ? 128 : 256);
-  const bool shared = e == p.E;
-  const long ee = shared ? 0 : e;
-  const int kb = WF == 0 ? K : K / 2;    // bytes per weight row
-  const uint8_t* wmat = (shared ? p.sw : p.w) + ee * long(NR) * kb;
-  const void* smat = shared ? p.sws : p.ws;
-  const int nks = K / 128;
-  // first matrix row of weight tile j (0..15): GEMM1 tiles 0..7 are gate
-  // rows, 8..15 the up rows of the same h columns; GEMM2 rows in order
-  auto wtile_row = [&](int j) { return MODE == 0 ? (j < 8 ? n0 + 16 * j : I + n0 + 16 * (j - 8)) : n0 + 16 * j; };
-
-  // ---- loader side: this lane's sources in the tiled weights for the tiles
-  // of wave w (tiles 2w, 2w+1: one contiguous kilobyte each, two for e4m3)
-  // and their MXFP4 scales (the two tiles' 128 bytes are adjacent; lanes
-  // 32..63 repeat lanes 0..31)
-  const long wstep = long(NR / 16) * kTileBytes<WF>;       // bytes per K step
-  const long sstep = long(NR / 16) * kTileScaleBytes;
-  const uint8_t* a_src[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) a_src[q] = wmat + long(wtile_row(2 * w + q) / 16) * kTileBytes<WF> + lane * 16;
-  const uint8_t* as_src = nullptr;
-  if (WF == 1)
-    as_src = static_cast<const uint8_t*>(smat) + ee * long(NR) * (K / 32) +
-             long(wtile_row(2 * w) / 16) * kTileScaleBytes + (lane & 31) * 4;
-  // ---- consumer side: this wave's weight tiles
-  int ja[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) ja[q] = MODE == 0 ? (q < 2 ? 2 * wr + q : 8 + 2 * wr + (q - 2)) : 4 * wr + q;
-  const float* wsc[4];  // e4m3: scale row of each tile's 128 x 128 block (one scale per K step)
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    wsc[q] = WF == 0 ? static_cast<const float*>(smat) + ee * long(NR / 128) * (K / 128) +
-                           long(wtile_row(ja[q]) / 128) * (K / 128)
-                     : nullptr;
-
-  for (int pass0 = 0; pass0 < ne; pass0 += kTokCap) {
-    const int npass = min(kTokCap, ne - pass0);
-    const int ntt = (npass + 15) / 16;
-    const int ntw = (ntt + 1 - wc) / 2;  // token tiles of this wave: t = 2 * tt + wc
-    // token-row sources: the pass's ntt tiles take 2 * ntt loads of 8 rows x
-    // 128 B (load i: tile i / 2, rows 8 (i % 2) .. + 7), dealt round-robin to
-    // the waves (load q of wave w is i = w + 8 q).  Lane l fills LDS chunk
-    // l % 8 of row l / 8, i.e. global chunk (l % 8) ^ (row & 7).  Rows past
-    // the group repeat its last row.  Every wave issues kTokLoads such loads
-    // per step; the ones past the pass's tiles read one 16-byte chunk with
-    // all lanes into the stage's sink, so every step has the same load count.
-    const uint8_t* b_src[kTokLoads];
-    int b_dst[kTokLoads];
-#pragma unroll
-    for (int q = 0; q < kTokLoads; ++q) {
-      const int i = w + 8 * q;
-      const int rl = (i & 1) * 8 + (lane >> 3);
-      const bool real = i < 2 * ntt;
-      const int tk = real ? min((i >> 1) * 16 + rl, npass - 1) : npass - 1;
-      const long arow = MODE == 0 ? long(p.row_token[row0 + pass0 + tk]) : long(row0 + pass0 + tk);
-      b_src[q] = p.act + arow * K + (real ? ((lane & 7) ^ (rl & 7)) << 4 : 0);
-      b_dst[q] = real ? i * 1024 : Geo::kSinkOff;
+    pf_tab = 0;
+    if (lane < Geo::kTabLoads) {
+      const int r = base + min(w + 8 * lane, npass - 1);
+      pf_tab = MODE == 0 ? p.row_token[r] : r;
     }
-    // token scales of the whole pass, read once into a [token][k step]
-    // table: one direct-to-LDS load per token (its K/128 scales are
-    // contiguous; lanes past them repeat the last one), CAP / 8 per wave.  Being
-    // direct loads into their own array, the table's reads wait only for
-    // these loads, not for the ring's.
-    for (int tk = w; tk < kTokCap; tk += 8) {
-      const int c = min(tk, npass - 1);
-      const long arow = MODE == 0 ? long(p.row_token[row0 + pass0 + c]) : long(row0 + pass0 + c);
-      dma4(p.act_s + arow * nks + min(lane, nks - 1), reinterpret_cast<uint8_t*>(xs_tab + tk * kXsRow));
-    }
+    pf_ok = true;
+  };
 
-    // the direct-to-LDS loads of step ks into stage buffer st, in three
-    // parts (0: weight tiles, 1: weight scales and the first
-    // token-row load, 2: the other two token-row loads)
-    auto issue = [&](int ks, uint8_t* st, int part) __attribute__((always_inline)) {
-      if (part == 0) {
-        if (WF == 1) {
+  // ---- loader state of the pass being loaded: per load slot the per-lane
+  // source of the next step to issue (steps are issued in order, each slot
+  // once per step, so the source just advances by the slot's stride), and
+  // a destination offset in the stage
+  const uint8_t* src16[L];
+  long stride16[L];
+  int dst16[L];
+  int tab_row = 0;          // this wave's token-scale rows of the pass (lane i: token w + 8 i)
+  const float* ws_src = nullptr;  // e4m3: the block-scale row this wave loads (waves 0, 1)
+  int ld_row = 0, ld_npass = 0, ld_n0 = 0, ld_ntw = 0;  // first row of the pass, its rows, unit column, tiles
+  auto setup = [&](int4 ent, int pass) __attribute__((always_inline)) {
+    if (!pf_ok) prefetch(ent, pass);
+    pf_ok = false;
+    const int e = ent.x;
+    ld_n0 = ent.w * (MODE == 0 ? 128 : 256);
+    ld_row = ent.y + pass * CAP;
+    ld_npass = min(CAP, ent.z - pass * CAP);
+    const int ntt = (ld_npass + 15) / 16;
+    ld_ntw = (ntt + 1 - wc) / 2;  // token tiles of this wave: t = 2 tt + wc
+    const bool shared = e == p.E;
+    const long ee = shared ? 0 : e;
+    const uint8_t* wmat = (shared ? p.sw : p.w) + ee * long(NR) * kb;
+    const void* smat = shared ? p.sws : p.ws;
+    const int n0 = ld_n0;
+    // first matrix row of unit weight tile t (0..15)
+    auto wtile_row = [&](int t) __attribute__((always_inline)) { return MODE == 0 ? (t < 8 ? n0 + 16 * t : I + n0 + 16 * (t - 8)) : n0 + 16 * t; };
 #pragma unroll
-          for (int q = 0; q < 2; ++q) dma16(a_src[q] + ks * wstep, st + Geo::kAOff + (2 * w + q) * 1024);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-              dma16(a_src[q] + ks * wstep + 1024 * h, st + Geo::kAOff + (2 * (2 * w + q) + h) * 1024);
-        }
-      } else if (part == 1) {
-        if (WF == 1) dma4(as_src + ks * sstep, st + Geo::kAsOff + w * 256);
-        dma16(b_src[0] + long(ks) * 128, st + b_dst[0]);
-      } else {
-#pragma unroll
-        for (int q = 1; q < kTokLoads; ++q) dma16(b_src[q] + long(ks) * 128, st + b_dst[q]);
+    for (int j = 0; j < L; ++j) {
+      const int i = w + 8 * j;
+      if (i < Geo::kTokLoads) {
+        // lane l fills LDS chunk l % 8 of its row, i.e. global chunk (l % 8) ^ (row & 7)
+        const int rl = (i & 1) * 8 + (lane >> 3);
+        src16[j] = p.act + long(pf_row[j < Geo::kTokSlots ? j : 0]) * K + (((lane & 7) ^ (rl & 7)) << 4);
+        stride16[j] = 128;
+        dst16[j] = i * 1024;
+      } else if (i < Geo::kTokLoads + Geo::kWLoads) {
+        const int wi = i - Geo::kTokLoads;
+        const int t = WF == 1 ? wi : wi >> 1, half = WF == 1 ? 0 : wi & 1;
+        src16[j] = wmat + long(wtile_row(t) / 16) * kTileBytes<WF> + half * 1024 + lane * 16;
+        stride16[j] = wstep;
+        dst16[j] = Geo::kWOff + wi * 1024;
+      } else if (i < Geo::kTokLoads + Geo::kWLoads + Geo::kScLoads) {
+        // the 16 tiles' e8m0 scales: lanes 0..31 the 8 tiles from unit tile 0
+        // (512 adjacent bytes), lanes 32..63 those from unit tile 8
+        const uint8_t* sb = static_cast<const uint8_t*>(smat) + ee * long(NR) * (K / 32);
+        src16[j] = sb + long(wtile_row(lane < 32 ? 0 : 8) / 16) * kTileScaleBytes + (lane & 31) * 16;
+        stride16[j] = sstep;
+        dst16[j] = Geo::kScOff;
+      } else {  // spare slot: one hot line into the sink
+        src16[j] = wmat;
+        stride16[j] = 0;
+        dst16[j] = Geo::kSinkOff;
       }
-    };
-    // pinned in place among the MFMAs: the load pipeline drains while the
-    // matrix cores work instead of taking every wave's loads in one burst
-    // (ALU, MFMA and LDS reads may still be scheduled across the point)
-    auto issue_part = [&](int ks, uint8_t* st, int part) __attribute__((always_inline)) {
-      __builtin_amdgcn_sched_barrier(kSchedMayCross);
-      issue(ks, st, part);
-      __builtin_amdgcn_sched_barrier(kSchedMayCross);
-    };
+    }
+    tab_row = pf_tab;
+    if (WF == 0 && w < 2) {
+      // e4m3 128 x 128 block scales of the unit's row block w (GEMM1: gate, up)
+      const int brow = MODE == 0 ? (w ? I + n0 : n0) / 128 : n0 / 128 + w;
+      ws_src = static_cast<const float*>(smat) + ee * long(NR / 128) * nks + long(brow) * nks;
+    }
+  };
 
-    // accumulators: e4m3 weights promote each step's MFMA result with a VALU
-    // FMA (acc += d * ws * xs).  MXFP4 weights carry their scales inside
-    // the MFMA, and the accumulator is kept in units of the current step's
-    // token scale: before a step it is multiplied by xs_prev / xs_cur (a
-    // multiply that depends only on the previous step), then the MFMA adds
-    // the step's product in place; after the last step it is multiplied by
-    // that step's xs.  Token scales are positive (at least 2^-64 / 448), so
-    // the ratio is always defined.
-    v4f acc[4][kTokPerWave];
-    float xsp[kTokPerWave];  // MXFP4: the token scales of the previous step
+  // this wave's direct-to-LDS loads [j0, j1) of its kL for the next step
+  // (ks, the step they belong to, is implied by the order) into stage st
+  auto issue_range = [&](int ks, uint8_t* st, int ja0, int ja1) __attribute__((always_inline)) {
+    (void)ks;
+#pragma unroll
+    for (int j = 0; j < L; ++j)
+      if (j >= ja0 && j < ja1) {
+        dma16(src16[j], st + dst16[j]);
+        src16[j] += stride16[j];
+      }
+  };
+  auto stage_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* { return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3; };
+  // first loads of a pass: the token-scale table (one load per token: its
+  // nks scales are contiguous; lanes past them repeat the last), the e4m3
+  // block-scale rows, then steps 0 .. S - 2 into stages 0 .. S - 2.  The
+  // tables are older than every stage load, so the wait for step 0 covers
+  // them.
+  auto prologue = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < Geo::kTabLoads; ++i) {
+      const int arow = __builtin_amdgcn_readlane(tab_row, i);
+      dma4(p.act_s + long(arow) * nks + min(lane, nks - 1), reinterpret_cast<uint8_t*>(xs_tab + (w + 8 * i) * kXsRow));
+    }
+    if (WF == 0 && w < 2) dma4(ws_src + min(lane, nks - 1), reinterpret_cast<uint8_t*>(ws_tab + w * kXsRow));
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nks) issue_range(s, stage_ptr(s), 0, L);
+  };
+  // before step k's first read: this wave's loads of steps k + 1 ..
+  // min(k + S - 2, nks - 1) may stay in flight (rem = nks - 1 - k)
+  auto wait_ring = [&](int rem) __attribute__((always_inline)) {
+    if (rem >= S - 2) wait_vmcnt<(S - 2) * L>();
+    else if (rem == 1) wait_vmcnt<L>();
+    else wait_vmcnt<0>();
+  };
+
+  // ---- accumulators: e4m3 weights promote each step's MFMA result with a
+  // VALU FMA (acc += d * ws * xs).  MXFP4 weights carry their scales inside
+  // the MFMA, and the accumulator is kept in units of the current step's
+  // token scale: when a step's fragments are read it is multiplied by
+  // xs_prev / xs_cur, then the MFMA adds the step's product in place; the
+  // epilogue multiplies by the last step's xs.  Token scales are positive
+  // (at least 2^-64 / 448), so the ratio is always defined.
+  v4f acc[4][NTMAX];
+  float xsp[NTMAX];  // MXFP4: the token scales of the previous step
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int t = 0; t < kTokPerWave; ++t) acc[q][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int t = 0; t < NTMAX; ++t) acc[q][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int t = 0; t < kTokPerWave; ++t) xsp[t] = 0.0f;
+    for (int t = 0; t < NTMAX; ++t) xsp[t] = 0.0f;
+  };
+  zero_acc();
 
-    // multiply one stage: A fragments of the wave's 4 weight tiles, then its
-    // token tiles two at a time, with the next stage's loads issued in
-    // between
-    auto compute = [&](int ks, const uint8_t* st, int ksn, uint8_t* nxt) __attribute__((always_inline)) {
-      v8i af[4];
-      int sa[4];
-      float wsv[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (WF == 1) {
-          const v4u a = *reinterpret_cast<const v4u*>(st + Geo::kAOff + ja[q] * 1024 + lane * 16);
-          af[q] = v8i{int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
-          sa[q] = st[Geo::kAsOff + (ja[q] >> 1) * 256 + (ja[q] & 1) * kTileScaleBytes + lane];
-          wsv[q] = 1.0f;
-        } else {
-          const v4u lo = *reinterpret_cast<const v4u*>(st + Geo::kAOff + (2 * ja[q]) * 1024 + lane * 16);
-          const v4u hi = *reinterpret_cast<const v4u*>(st + Geo::kAOff + (2 * ja[q] + 1) * 1024 + lane * 16);
-          af[q] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
-          sa[q] = kUnitScale;
-          wsv[q] = wsc[q][ks];
-        }
-      }
-      float xsv[kTokPerWave];
-#pragma unroll
-      for (int tt = 0; tt < kTokPerWave; ++tt)
-        xsv[tt] = xs_tab[((2 * tt + wc) * 16 + m) * kXsRow + ks];
-      if (WF == 1) {
-        // rescale to this step's token scales
-#pragma unroll
-        for (int tt = 0; tt < kTokPerWave; ++tt) {
-          if (tt < ntw) {
-            const float r = xsp[tt] * __builtin_amdgcn_rcpf(xsv[tt]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[q][tt] *= r;
-          }
-          xsp[tt] = xsv[tt];
-        }
-      }
-#pragma unroll
-      for (int t0 = 0; t0 < 6; t0 += 2) {
-        issue_part(ksn, nxt, t0 / 2);
-        if (t0 < kTokPerWave && t0 < ntw) {
-          // a pair of token tiles (the last one alone when the count is odd)
-          v8i bf[2];
-#pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            if (t0 + r >= kTokPerWave) continue;
-            const int t = 2 * (t0 + r) + wc;
-            const v4u lo = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, g));
-            const v4u hi = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, 4 + g));
-            bf[r] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
-          }
-          if (WF == 1) {
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if (t0 + r < kTokPerWave)
-                  acc[q][t0 + r] = mfma_scaled_acc<kFmtE2M1, kFmtE4M3>(af[q], bf[r], acc[q][t0 + r], sa[q], kUnitScale);
-          } else {
-            v4f d[2][4];
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if (t0 + r < kTokPerWave) d[r][q] = mfma_scaled<kFmtE4M3, kFmtE4M3>(af[q], bf[r], kUnitScale, kUnitScale);
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if (t0 + r < kTokPerWave) acc[q][t0 + r] += d[r][q] * (wsv[q] * xsv[t0 + r]);
-          }
-        }
-      }
-    };
-
-    // ---- the K loop over the ring, unrolled by the ring depth so that each
-    // step's stage buffers are fixed arrays.  Every step issues the loads of
-    // the step S - 1 ahead, clamped to the last step (past the end they
-    // re-load it into a stage that is not read again), so every step has
-    // the same count of loads in flight and waits for the same count.
-    auto step = [&](int ks, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
-      wait_vmcnt<(S - 2) * Geo::kLoadsPerStage>();
-      ring_barrier();
-      compute(ks, cur, min(ks + S - 1, nks - 1), nxt);
-    };
-    for (int part = 0; part < 3; ++part) issue(0, st0, part);
-    int ks = 0;
-    if (S == 3) {
-      for (int part = 0; part < 3; ++part) issue(min(1, nks - 1), st1, part);
-      for (; ks + 3 <= nks; ks += 3) {
-        step(ks, st0, st2);
-        step(ks + 1, st1, st0);
-        step(ks + 2, st2, st1);
-      }
-      if (ks < nks) step(ks, st0, st2);
-      if (ks + 1 < nks) step(ks + 1, st1, st0);
-    } else {
-      for (; ks + 2 <= nks; ks += 2) {
-        step(ks, st0, st1);
-        step(ks + 1, st1, st0);
-      }
-      if (ks < nks) step(ks, st0, st1);
-    }
-
-    if (WF == 1)  // back from units of the last step's token scale
-#pragma unroll
-      for (int tt = 0; tt < kTokPerWave; ++tt)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q][tt] *= xsp[tt];
-
-    // ---- epilogue
-    wait_vmcnt<0>();  // the clamped loads past the last step land in the ring too
-    __syncthreads();  // all waves are done reading the ring
+  // ---- epilogue of a finished pass (c_*: its first row, rows, unit column
+  // and this wave's tile count).  GEMM1: part 1 forms h = silu(gate) * up in
+  // place of the gate accumulators (h column n0 + 32 wr + 16 q + 4 g + i,
+  // token 16 t + m with t = 2 tt + wc) and posts each token's partial
+  // maximum to LDS; part 2, after a barrier, requantises with the maximum
+  // over the four wave rows.  GEMM2: part 1 stores y.  Outputs go through
+  // LDS so that the global stores write whole 128-byte lines: the last ring
+  // stage holds them (the next pass's first loads go to stages 0 .. S - 2,
+  // and stage S - 1 is not written before the next A(0) barrier, which every
+  // wave reaches after its epilogue).
+  constexpr int kEPitch = 144;  // bytes per buffered row: 128 of data + 16 (rows 36 banks apart)
+  static_assert(CAP * kEPitch <= Geo::kStageBytes && 8 * 16 * kEPitch <= Geo::kStageBytes,
+                "epilogue buffers fit one stage");
+  uint8_t* const ebuf = stage_ptr(S - 1);
+  int c_row = 0, c_npass = 0, c_n0 = 0, c_ntw = 0;
+  auto epi1 = [&]() __attribute__((always_inline)) {
     if (MODE == 0) {
-      // h = silu(gate) * up in place of the gate accumulators: h column
-      // n0 + 32 wr + 16 q + 4 g + i, token 16 t + m with t = 2 tt + wc
-      float* red = reinterpret_cast<float*>(st0);  // [4 wave rows][kTokCap]
-      float amax[kTokPerWave];
 #pragma unroll
-      for (int tt = 0; tt < kTokPerWave; ++tt) {
-        amax[tt] = 0.0f;
+      for (int tt = 0; tt < NTMAX; ++tt) {
+        if (WF == 1)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q][tt] *= xsp[tt];
+        float amax = 0.0f;
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float gt = acc[q][tt][i], up = acc[q + 2][tt][i];
-            const float v = gt / (1.0f + expf(-gt)) * up;
+            const float v = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
             acc[q][tt][i] = v;
-            amax[tt] = fmaxf(amax[tt], fabsf(v));
+            amax = fmaxf(amax, fabsf(v));
           }
-        amax[tt] = wave_max_xor(amax[tt], 16);
-        amax[tt] = wave_max_xor(amax[tt], 32);
-      }
-      if (g == 0)
-#pragma unroll
-        for (int tt = 0; tt < kTokPerWave; ++tt) red[wr * kTokCap + (2 * tt + wc) * 16 + m] = amax[tt];
-      __syncthreads();
-#pragma unroll
-      for (int tt = 0; tt < kTokPerWave; ++tt) {
-        const int idx = (2 * tt + wc) * 16 + m;
-        if (tt >= ntw || idx >= npass) continue;
-        float am = red[idx];
-#pragma unroll
-        for (int q = 1; q < 4; ++q) am = fmaxf(am, red[q * kTokCap + idx]);
-        const float mult = quant_mult(am);
-        const long r = row0 + pass0 + idx;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const v4f& hv = acc[q][tt];
-          const uint32_t word = enc_e4m3x4(hv[0] * mult, hv[1] * mult, hv[2] * mult, hv[3] * mult);
-          *reinterpret_cast<uint32_t*>(p.hq + r * I + n0 + 32 * wr + 16 * q + 4 * g) = word;
-        }
-        if (g == 0 && wr == 0) p.hs[r * (I / 128) + n0 / 128] = 1.0f / mult;
+        amax = wave_max_xor(amax, 16);
+        amax = wave_max_xor(amax, 32);
+        if (g == 0 && tt < c_ntw) red[wr * CAP + (2 * tt + wc) * 16 + m] = amax;
       }
     } else {
+      // this wave's 16 x 64 block of a token tile, row by row through its
+      // own slice of the buffer: 128 bytes per row (bf16: 64 columns; fp32:
+      // 32 columns, two halves)
+      uint8_t* const wb = ebuf + w * (16 * kEPitch);
+      const int rr = lane >> 3, ch = lane & 7;  // read-back: rows rr, rr + 8, 16-byte chunk ch
 #pragma unroll
-      for (int tt = 0; tt < kTokPerWave; ++tt) {
-        const int idx = (2 * tt + wc) * 16 + m;
-        if (tt >= ntw || idx >= npass) continue;
-        const long r = row0 + pass0 + idx;
+      for (int tt = 0; tt < NTMAX; ++tt) {
+        if (tt >= c_ntw) continue;
+        const int t0 = (2 * tt + wc) * 16;
+        v4f v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (p.yb) store_bf16x4(p.yb + r * H + n0 + 64 * wr + 16 * q + 4 * g, acc[q][tt]);
-          else *reinterpret_cast<v4f*>(p.y + r * H + n0 + 64 * wr + 16 * q + 4 * g) = acc[q][tt];
+        for (int q = 0; q < 4; ++q) v[q] = WF == 1 ? acc[q][tt] * xsp[tt] : acc[q][tt];
+        if (p.yb) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint2 o;
+            o.x = f32_to_bf16(v[q][0]) | (f32_to_bf16(v[q][1]) << 16);
+            o.y = f32_to_bf16(v[q][2]) | (f32_to_bf16(v[q][3]) << 16);
+            *reinterpret_cast<uint2*>(wb + m * kEPitch + (16 * q + 4 * g) * 2) = o;
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int row = 8 * h + rr;
+            const v4u d = *reinterpret_cast<const v4u*>(wb + row * kEPitch + ch * 16);
+            if (t0 + row < c_npass)
+              *reinterpret_cast<v4u*>(p.yb + long(c_row + t0 + row) * H + c_n0 + 64 * wr + ch * 8) = d;
+          }
+        } else {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+              *reinterpret_cast<v4f*>(wb + m * kEPitch + (16 * q + 4 * g) * 4) = v[2 * half + q];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int row = 8 * h + rr;
+              const v4u d = *reinterpret_cast<const v4u*>(wb + row * kEPitch + ch * 16);
+              if (t0 + row < c_npass)
+                *reinterpret_cast<v4u*>(p.y + long(c_row + t0 + row) * H + c_n0 + 64 * wr + 32 * half + ch * 4) = d;
+            }
+          }
+        }
       }
     }
-    __syncthreads();  // LDS is reused by the next pass
+  };
+  auto epi2 = [&]() __attribute__((always_inline)) {
+    if (MODE != 0) return;
+    // codes of the pass's tokens: [token][128 h columns] in the buffer
+#pragma unroll
+    for (int tt = 0; tt < NTMAX; ++tt) {
+      if (tt >= c_ntw) continue;
+      const int idx = (2 * tt + wc) * 16 + m;
+      float am = red[idx];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) am = fmaxf(am, red[q * CAP + idx]);
+      const float mult = quant_mult(am);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const v4f& hv = acc[q][tt];
+        const uint32_t word = enc_e4m3x4(hv[0] * mult, hv[1] * mult, hv[2] * mult, hv[3] * mult);
+        *reinterpret_cast<uint32_t*>(ebuf + idx * kEPitch + 32 * wr + 16 * q + 4 * g) = word;
+      }
+      if (g == 0 && wr == 0 && idx < c_npass) p.hs[long(c_row + idx) * (I / 128) + c_n0 / 128] = 1.0f / mult;
+    }
+    lds_barrier();
+    for (int c = tid; c < c_npass * 8; c += kBigThreads) {
+      const int row = c >> 3, part = c & 7;
+      *reinterpret_cast<v4u*>(p.hq + long(c_row + row) * I + c_n0 + part * 16) =
+          *reinterpret_cast<const v4u*>(ebuf + row * kEPitch + part * 16);
+    }
+  };
+
+  // ---- work items: (unit i, pass) in order
+  auto entry_of = [&](int i) __attribute__((always_inline)) -> int4 {
+    if (i >= nunits) return make_int4(-1, 0, 0, 0);
+    return tab[i - tab0];
+  };
+  auto next_of = [&](int i, int pass, int4 e, int& ni, int& np) __attribute__((always_inline)) {
+    if ((pass + 1) * CAP < e.z) { ni = i; np = pass + 1; }
+    else { ni = i + 1; np = 0; }
+  };
+
+  int ui = 0, upass = 0;
+  build_table(0);
+  int4 ent = entry_of(0);
+  if (ent.x < 0) return;
+  setup(ent, 0);
+  {
+    int ni, np;
+    next_of(ui, upass, ent, ni, np);
+    if (ni < nunits && ni < tab0 + kTabCap) {
+      const int4 e2 = entry_of(ni);
+      if (e2.x >= 0) prefetch(e2, np);
+    }
+  }
+  prologue();
+
+  // ---- one pass: half steps A(0), B(0), ..., A(nks), the same barriers in
+  // every wave whatever its tile count NT
+  auto run_pass = [&](auto ntc) __attribute__((always_inline)) {
+    constexpr int NT = decltype(ntc)::value;
+    constexpr int NA = NT > 0 ? NT : 1;  // array extent (no zero-length arrays)
+    v8i af[4];
+    int sa[4];
+    float wsv[4];
+    float xsv[NA];
+    v8i bf[NA];
+    // the fragments of step k in stage st; MXFP4: rescale to its token scales
+    auto READ = [&](const uint8_t* st, int k) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (WF == 1) {
+          const v4u a = *reinterpret_cast<const v4u*>(st + Geo::kWOff + ja[q] * 1024 + lane * 16);
+          af[q] = v8i{int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
+          sa[q] = st[Geo::kScOff + ja[q] * kTileScaleBytes + lane];
+          wsv[q] = 1.0f;
+        } else {
+          const v4u lo = *reinterpret_cast<const v4u*>(st + Geo::kWOff + (2 * ja[q]) * 1024 + lane * 16);
+          const v4u hi = *reinterpret_cast<const v4u*>(st + Geo::kWOff + (2 * ja[q] + 1) * 1024 + lane * 16);
+          af[q] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+          sa[q] = kUnitScale;
+          // unit tiles 0..7 lie in the first 128-row block, 8..15 in the second
+          wsv[q] = ws_tab[(ja[q] >> 3) * kXsRow + k];
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        const int t = 2 * tt + wc;
+        xsv[tt] = xs_tab[(t * 16 + m) * kXsRow + k];
+        const v4u lo = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, g));
+        const v4u hi = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, 4 + g));
+        bf[tt] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+      }
+      if (WF == 1) {
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          const float rr = xsp[tt] * __builtin_amdgcn_rcpf(xsv[tt]);
+          xsp[tt] = xsv[tt];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q][tt] *= rr;
+        }
+      }
+    };
+    // multiply the fragments in registers; the loads of step kn (when there
+    // is one) go out into stage iss between the token tiles
+    auto MMA = [&](int kn, uint8_t* iss) __attribute__((always_inline)) {
+      const bool go = kn < nks;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        if (WF == 1) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[q][tt] = mfma_scaled_acc<kFmtE2M1, kFmtE4M3>(af[q], bf[tt], acc[q][tt], sa[q], kUnitScale);
+        } else {
+          v4f d[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) d[q] = mfma_scaled<kFmtE4M3, kFmtE4M3>(af[q], bf[tt], kUnitScale, kUnitScale);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q][tt] += d[q] * (wsv[q] * xsv[tt]);
+        }
+        __builtin_amdgcn_sched_barrier(kSchedMayCross);
+        if (go) issue_range(kn, iss, tt * L / NA, (tt + 1) * L / NA);
+        __builtin_amdgcn_sched_barrier(kSchedMayCross);
+      }
+      if (NT == 0 && go) issue_range(kn, iss, 0, L);
+    };
+    // half steps: in A(k) column 0 reads step k while column 1 multiplies
+    // step k - 1, in B(k) column 0 multiplies step k while column 1 reads
+    // it; each side issues its loads of step k + S - 1 while it multiplies,
+    // into the stage step k - 1 used.  The two columns run separate loops
+    // with the same barriers (one straight-line order each).
+    if (wc == 0) {
+      wait_ring(nks - 1);
+      lds_barrier();  // A(0)
+      READ(st0, 0);
+      lds_barrier();  // B(0)
+      MMA(S - 1, stage_ptr(S - 1));
+      auto half_pair = [&](int k, const uint8_t* cur, uint8_t* iss) __attribute__((always_inline)) {
+        wait_ring(nks - 1 - k);
+        lds_barrier();  // A(k)
+        READ(cur, k);
+        lds_barrier();  // B(k)
+        MMA(k + S - 1, iss);
+      };
+      for (int k = 1; k < nks; k += S) {
+        half_pair(k, stage_ptr(1 % S), stage_ptr(0));
+        if (k + 1 < nks) half_pair(k + 1, stage_ptr(2 % S), stage_ptr(1 % S));
+        if (S >= 3 && k + 2 < nks) half_pair(k + 2, stage_ptr(3 % S), stage_ptr(2 % S));
+        if (S >= 4 && k + 3 < nks) half_pair(k + 3, stage_ptr(4 % S), stage_ptr(3 % S));
+      }
+      lds_barrier();  // A(nks)
+    } else {
+      wait_ring(nks - 1);
+      lds_barrier();  // A(0)
+      if (S - 1 < nks) issue_range(S - 1, stage_ptr(S - 1), 0, L);
+      lds_barrier();  // B(0)
+      READ(st0, 0);
+      auto half_pair = [&](int k, const uint8_t* cur, uint8_t* iss) __attribute__((always_inline)) {
+        wait_ring(nks - 1 - k);
+        lds_barrier();  // A(k)
+        MMA(k + S - 1, iss);
+        lds_barrier();  // B(k)
+        READ(cur, k);
+      };
+      for (int k = 1; k < nks; k += S) {
+        half_pair(k, stage_ptr(1 % S), stage_ptr(0));
+        if (k + 1 < nks) half_pair(k + 1, stage_ptr(2 % S), stage_ptr(1 % S));
+        if (S >= 3 && k + 2 < nks) half_pair(k + 2, stage_ptr(3 % S), stage_ptr(2 % S));
+        if (S >= 4 && k + 3 < nks) half_pair(k + 3, stage_ptr(4 % S), stage_ptr(3 % S));
+      }
+      lds_barrier();  // A(nks): multiply the last step
+      MMA(nks, st0);
+    }
+  };
+  // compiled tile counts: NTMAX and the two below it (at least 1); a wave
+  // with fewer tiles runs the smallest and multiplies tiles the epilogue
+  // ignores (their token rows repeat the pass's last row)
+  constexpr int NT1 = NTMAX > 1 ? NTMAX - 1 : 1, NT2 = NTMAX > 2 ? NTMAX - 2 : 1;
+  auto run_pass_any = [&](int nt) __attribute__((always_inline)) {
+    if (nt >= NTMAX) run_pass(std::integral_constant<int, NTMAX>{});
+    else if (NT1 < NTMAX && nt >= NT1) run_pass(std::integral_constant<int, NT1>{});
+    else if (NT2 < NT1) run_pass(std::integral_constant<int, NT2>{});
+    else run_pass(std::integral_constant<int, NT1>{});
+  };
+
+  while (true) {
+    run_pass_any(ld_ntw);
+    // nothing is in flight here (the last step waited for every load), and
+    // saying so lets the compiler use the prefetched rows without a wait
+    // behind the epilogue's stores
+    wait_vmcnt<0>();
+    // ---- the pass's epilogue first (the accumulators die with it, which
+    // leaves the registers to the next pass's set-up), then the next pass's
+    // first loads: every stage is free (the last reads were in B(nks - 1))
+    c_row = ld_row; c_npass = ld_npass; c_n0 = ld_n0; c_ntw = ld_ntw;
+    epi1();
+    lds_barrier();
+    epi2();
+    zero_acc();
+    int ni, np;
+    next_of(ui, upass, ent, ni, np);
+    if (ni >= nunits) ni = -1;
+    if (ni >= 0 && ni >= tab0 + kTabCap) {
+      build_table(ni);
+      pf_ok = false;
+    }
+    const int4 nent = ni >= 0 ? entry_of(ni) : make_int4(-1, 0, 0, 0);
+    if (nent.x < 0) break;
+    ui = ni; upass = np; ent = nent;
+    setup(ent, upass);
+    // the prefetch's own waits (and any reloads) come before the pass's
+    // first loads are in flight, not behind them
+    int ni2, np2;
+    next_of(ui, upass, ent, ni2, np2);
+    if (ni2 < nunits && ni2 < tab0 + kTabCap) {
+      const int4 e2 = entry_of(ni2);
+      if (e2.x >= 0) prefetch(e2, np2);
+    }
+    prologue();
   }
 }
 
@@ -478,7 +672,14 @@ static hipError_t launch_big(const Shape& s, int mode, BigParams& p, hipStream_t
   if (units == 0) return hipSuccess;
   p.units = units;
   p.per_xcd = (units + 7) / 8;
-  const unsigned grid = unsigned(p.per_xcd) * 8;
+  // persistent: one workgroup per CU (the kernel's LDS allows one), the
+  // same number on each of the 8 XCDs
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    ncu = 256;
+  const int nwx = std::max(1, std::min(ncu / 8, p.per_xcd));
+  const unsigned grid = unsigned(nwx) * 8;
   const size_t lds = 0;  // static LDS
 #define MOE_BIG_LAUNCH(WF, CAP)                                                                   \
   do {                                                                                            \
