@@ -63,15 +63,16 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(bytes_per_launch_alg: float):
+def load_traffic(workload: str, T: int):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+    if it was taken on the current kernel source and on this workload and T;
+    else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_src_sha") != kernel_sha():
+    if t.get("kernel_src_sha") != kernel_sha() or t.get("workload") != f"{workload} T={T}":
         return None
     return float(t["hbm_bytes_per_launch"])
 
@@ -196,7 +197,7 @@ def main():
     g1_bytes = c["touched"] * e1 + T * wl.H + T * (wl.H // wl.act_group) * 4 + R * wl.I + R * (wl.I // wl.act_group) * 4
     g1_us = stage_us["gemm1_swiglu"]
     achieved = g1_bytes / g1_us / 1e3
-    traffic = load_traffic(g1_bytes)
+    traffic = load_traffic(wl.name, RT)
 
     line = {
         "metric": "MoE layer latency (us) + weight GB/s vs HBM peak at T=1..256; TFLOP/s at T=4096",
