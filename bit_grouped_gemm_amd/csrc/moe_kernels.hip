@@ -679,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
 }
 
 // =====================================================================
-// combine: one workgroup per token, 4 channels per thread per step
+// combine: one workgroup per (token, channel chunk)
 // =====================================================================
 struct CombineParams {
   const float* y;            // fp32 rows, or
@@ -691,25 +691,35 @@ struct CombineParams {
   int H, k, E, shared;
 };
 
-// One workgroup per (token, 1024 channels), four channels per thread.  The
-// k slot rows are loaded in unrolled batches of 8 with no branch between the
-// loads, so a thread has up to 8 loads in flight; masked slots read a valid
-// row of the token with weight 0, whose product is an exact zero and leaves
-// the ascending-order fp32 sum unchanged.
-constexpr int kCombineChunk = kThreads * 4;
+// One workgroup per (token, 256 NV channels), NV consecutive channels per
+// thread: one 16-byte load per row (NV = 4 for fp32 rows, 8 for bf16 rows).
+// The k slot rows are loaded in unrolled batches of 8 with no branch between
+// the loads, so a thread has up to 8 loads in flight; masked slots read a
+// valid row of the token with weight 0, whose product is an exact zero and
+// leaves the ascending-order fp32 sum unchanged.
+template <int NV> struct Row { v4f h[NV / 4]; };
 
-__device__ __forceinline__ v4f load_row4(const CombineParams& p, long r, int c) {
-  if (p.yb) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p.yb + r * p.H + c);
-    return v4f{bf16_to_f32(u.x & 0xFFFFu), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xFFFFu), bf16_to_f32(u.y >> 16)};
+template <int NV>
+__device__ __forceinline__ Row<NV> load_row(const CombineParams& p, long r, int c) {
+  Row<NV> v;
+  if (NV == 8) {
+    const v4u u = *reinterpret_cast<const v4u*>(p.yb + r * p.H + c);
+#pragma unroll
+    for (int h = 0; h < NV / 4; ++h)
+      v.h[h] = v4f{bf16_to_f32(u[2 * h] & 0xFFFFu), bf16_to_f32(u[2 * h] >> 16), bf16_to_f32(u[2 * h + 1] & 0xFFFFu),
+                   bf16_to_f32(u[2 * h + 1] >> 16)};
+  } else {
+    v.h[0] = *reinterpret_cast<const v4f*>(p.y + r * p.H + c);
   }
-  return *reinterpret_cast<const v4f*>(p.y + r * p.H + c);
+  return v;
 }
 
+template <int NV>
 __global__ __launch_bounds__(kThreads) void k_combine(CombineParams p) {
-  const int nchunk = (p.H + kCombineChunk - 1) / kCombineChunk;
+  constexpr int kChunk = kThreads * NV;
+  const int nchunk = (p.H + kChunk - 1) / kChunk;
   const long t = blockIdx.x / nchunk;
-  const int c = (blockIdx.x % nchunk) * kCombineChunk + threadIdx.x * 4;
+  const int c = (blockIdx.x % nchunk) * kChunk + threadIdx.x * NV;
   const int k = p.k;
   const int* ids = p.expand_idx + t * k;
   const float* tw = p.tw + t * k;
@@ -718,27 +728,39 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineParams p) {
   for (int j = k - 1; j >= 0; --j)
     if (ids[j] >= 0) pad = ids[j];
   if (c >= p.H) return;
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  Row<NV> acc;
+#pragma unroll
+  for (int h = 0; h < NV / 4; ++h) acc.h[h] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   if (pad >= 0) {
     for (int j0 = 0; j0 < k; j0 += 8) {
-      v4f v[8];
+      Row<NV> v[8];
       float wj[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int j = j0 + jj;
         const int r = j < k ? ids[j] : -1;
         wj[jj] = r >= 0 ? tw[j] : 0.0f;
-        v[jj] = load_row4(p, r >= 0 ? r : pad, c);
+        v[jj] = load_row<NV>(p, r >= 0 ? r : pad, c);
       }
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) acc += wj[jj] * v[jj];
+      for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+        for (int h = 0; h < NV / 4; ++h) acc.h[h] += wj[jj] * v[jj].h[h];
     }
-    if (srow >= 0) acc += load_row4(p, srow, c);
+    if (srow >= 0) {
+      const Row<NV> v = load_row<NV>(p, srow, c);
+#pragma unroll
+      for (int h = 0; h < NV / 4; ++h) acc.h[h] += v.h[h];
+    }
   }
-  uint2 o;
-  o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
-  o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
-  *reinterpret_cast<uint2*>(p.out + t * p.H + c) = o;
+  uint32_t o[NV / 2];
+#pragma unroll
+  for (int h = 0; h < NV / 4; ++h) {
+    o[2 * h] = f32_to_bf16(acc.h[h][0]) | (f32_to_bf16(acc.h[h][1]) << 16);
+    o[2 * h + 1] = f32_to_bf16(acc.h[h][2]) | (f32_to_bf16(acc.h[h][3]) << 16);
+  }
+  if (NV == 8) *reinterpret_cast<v4u*>(p.out + t * p.H + c) = v4u{o[0], o[1], o[2], o[3]};
+  else *reinterpret_cast<uint2*>(p.out + t * p.H + c) = uint2{o[0], o[1]};
 }
 
 // =====================================================================
@@ -817,8 +839,10 @@ hipError_t launch_combine(const Shape& s, const float* y, const uint16_t* yb, co
                           const float* topk_w, uint16_t* out, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   CombineParams p{y, yb, expand_idx, offsets, topk_w, out, s.H, s.k, s.E, s.shared};
-  const long grid = long(s.T) * ((s.H + kCombineChunk - 1) / kCombineChunk);
-  hipLaunchKernelGGL(k_combine, dim3(unsigned(grid)), dim3(kThreads), 0, st, p);
+  const int nv = yb ? 8 : 4;
+  const long grid = long(s.T) * ((s.H + kThreads * nv - 1) / (kThreads * nv));
+  if (yb) hipLaunchKernelGGL(k_combine<8>, dim3(unsigned(grid)), dim3(kThreads), 0, st, p);
+  else hipLaunchKernelGGL(k_combine<4>, dim3(unsigned(grid)), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
