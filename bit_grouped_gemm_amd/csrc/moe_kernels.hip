@@ -592,10 +592,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------
-// GEMM2: unit = (group, 128 output rows, K split); wave w owns output rows
-// n0+32w+16j+(0..15), j = 0,1.
+// GEMM2: unit = (group, 64 NJ output rows, K split); wave w owns output rows
+// n0 + 16 NJ w + 16 j + (0..15), j < NJ (NJ = 4 when H allows 256-row
+// units: twice the weight bytes in flight per wave).
 // ---------------------------------------------------------------------
-template <int WF, int NTT, int B32>
+template <int WF, int NTT, int B32, int NJ>
 __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
   __shared__ int s_wsum[4], s_res, s_flag;
   const int S = p.S, nt = p.ntiles;
@@ -605,19 +606,20 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
   if (e < 0) return;
   const int row0 = p.offsets[e], ne = p.offsets[e + 1] - row0;
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 15, g = lane >> 4;
-  const int H = p.H, I = p.I, n0 = tile * 128;
+  constexpr int kRows = 64 * NJ;  // output rows of a unit
+  const int H = p.H, I = p.I, n0 = tile * kRows;
   const __amdgpu_buffer_rsrc_t prs = coherent_rsrc(p.part);
   const bool shared = e == p.E;
   const long ee = shared ? 0 : e;
   const long kbytes = WF == 0 ? I : I / 2;
   const uint8_t* wbase = (shared ? p.sw : p.w) + ee * long(H) * kbytes;
   const long wstep = long(H / 16) * kTileBytes<WF>, sstep = long(H / 16) * kTileScaleBytes;
-  const uint8_t* wtile[2];
-  const float* wsc[2];
-  const uint8_t* wsb[2];
+  const uint8_t* wtile[NJ];
+  const float* wsc[NJ];
+  const uint8_t* wsb[NJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int rb = n0 + 32 * w + 16 * j;
+  for (int j = 0; j < NJ; ++j) {
+    const int rb = n0 + 16 * NJ * w + 16 * j;
     wtile[j] = wbase + long(rb / 16) * kTileBytes<WF> + lane * 16;
     if (WF == 0) {
       const int b = p.wblk;
@@ -641,38 +643,39 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
       brow[t] = p.act + r * I;
       bsc[t] = p.act_s + r * (I / p.G);
     }
-    v4f acc[2][NTT];
+    v4f acc[NJ][NTT];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int t = 0; t < NTT; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    kloop<WF, 2, NTT, B32, kStages>(acc, wtile, wsc, wsb, brow, bsc, ks0, ks1, g, wstep, sstep);
+    kloop<WF, NJ, NTT, B32, kStages>(acc, wtile, wsc, wsb, brow, bsc, ks0, ks1, g, wstep, sstep);
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
       const int idx = pass * 16 * NTT + t * 16 + m;
       if (idx >= ne) continue;
       const long r = row0 + idx;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = 32 * w + 16 * j + 4 * g;
+      for (int j = 0; j < NJ; ++j) {
+        const int col = 16 * NJ * w + 16 * j + 4 * g;
         if (S == 1) {
           if (p.yb) store_bf16x4(p.yb + r * H + n0 + col, acc[j][t]);
           else *reinterpret_cast<v4f*>(p.y + r * H + n0 + col) = acc[j][t];
         }
         else
-          st_coherent(prs, ((long(split) * nt + tile) * p.rows_cap + r) * 128 + col, acc[j][t]);
+          st_coherent(prs, ((long(split) * nt + tile) * p.rows_cap + r) * kRows + col, acc[j][t]);
       }
     }
   }
   if (S == 1) return;
   if (!arrive_last(p.cnt + e * nt + tile, S, &s_flag)) return;
-  // reduce the S partial sums in split order: 128 columns x ne rows
-  for (int q = tid; q < ne * 32; q += kThreads) {
-    const long r = row0 + q / 32;
-    const int col = (q % 32) * 4;
+  // reduce the S partial sums in split order: kRows columns x ne rows
+  constexpr int kQ = kRows / 4;  // 4-column pieces per row
+  for (int q = tid; q < ne * kQ; q += kThreads) {
+    const long r = row0 + q / kQ;
+    const int col = (q % kQ) * 4;
     v4f s = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int sp = 0; sp < S; ++sp)
-      s += ld_coherent(prs, ((long(sp) * nt + tile) * p.rows_cap + r) * 128 + col);
+      s += ld_coherent(prs, ((long(sp) * nt + tile) * p.rows_cap + r) * kRows + col);
     if (p.yb) store_bf16x4(p.yb + r * H + n0 + col, s);
     else *reinterpret_cast<v4f*>(p.y + r * H + n0 + col) = s;
   }
@@ -806,7 +809,24 @@ hipError_t launch_clear(int32_t* ptr, int n, hipStream_t st) {
   }
 
 MOE_GEMM_DISPATCH(k_gemm1)
-MOE_GEMM_DISPATCH(k_gemm2)
+
+// GEMM2 also picks its weight tiles per wave (NJ = 2 or 4)
+template <int NJ>
+static hipError_t dispatch_gemm2_nj(const Shape& s, int ntt, unsigned grid, const GemmParams& p, hipStream_t st) {
+  const bool b32 = s.wfmt == 0 && s.wblk == 32;
+  const int wf = s.wfmt == 0 ? 0 : 1;
+#define MOE_G2(WF, B32)                                                                                \
+  do {                                                                                                 \
+    if (ntt == 1) hipLaunchKernelGGL((k_gemm2<WF, 1, B32, NJ>), dim3(grid), dim3(kThreads), 0, st, p);  \
+    else if (ntt == 2) hipLaunchKernelGGL((k_gemm2<WF, 2, B32, NJ>), dim3(grid), dim3(kThreads), 0, st, p); \
+    else hipLaunchKernelGGL((k_gemm2<WF, 4, B32, NJ>), dim3(grid), dim3(kThreads), 0, st, p);          \
+  } while (0)
+  if (wf == 0 && !b32) MOE_G2(0, 0);
+  else if (b32) MOE_G2(0, 1);
+  else MOE_G2(1, 0);
+#undef MOE_G2
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm1(const Shape& s, const uint8_t* xq, const float* xs, const int32_t* row_token,
                         const int32_t* offsets, WeightPtrs w1, uint8_t* hq, float* hs, float* part,
@@ -832,7 +852,8 @@ hipError_t launch_gemm2(const Shape& s, const uint8_t* hq, const float* hs, cons
   p.S = s.g2_split; p.ntiles = s.g2_tiles; p.rows_cap = s.rows_cap;
   const unsigned grid = unsigned(s.slots_max) * s.g2_tiles * s.g2_split;
   if (grid == 0) return hipSuccess;
-  return dispatch_k_gemm2(s, s.g2_ntt, grid, p, st);
+  return s.g2_nj == 4 ? dispatch_gemm2_nj<4>(s, s.g2_ntt, grid, p, st)
+                      : dispatch_gemm2_nj<2>(s, s.g2_ntt, grid, p, st);
 }
 
 hipError_t launch_combine(const Shape& s, const float* y, const uint16_t* yb, const int32_t* expand_idx, const int32_t* offsets,

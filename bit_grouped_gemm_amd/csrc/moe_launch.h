@@ -18,8 +18,9 @@ struct Shape {
   int g1_tiles;     // I / 128
   int g1_split;     // K splits over H/128 steps
   int g1_ntt;       // 16-token tiles per pass (1, 2 or 4)
-  // GEMM2: unit = 128 output rows of one group
-  int g2_tiles;     // H / 128
+  // GEMM2: unit = 64 g2_nj output rows of one group
+  int g2_nj;        // weight tiles per wave: 4 (256-row units) when H % 256 == 0, else 2
+  int g2_tiles;     // H / (64 g2_nj)
   int g2_split;     // K splits over I/128 steps
   int g2_ntt;
   // groups with many rows (prefill) run the 256 x 256-token LDS-staged kernels
