@@ -456,13 +456,18 @@ def test_poisoned_workspace_and_determinism():
         assert torch.equal(b.view(torch.int16), c.view(torch.int16))
 
 
-def test_layer_matches_its_stages():
+@pytest.mark.parametrize("name,T", [
+    ("fp8_zipf_shared", 19),   # one token tile per pass: 128-row GEMM2 units
+    ("fp8_b128", 37),          # two token tiles: 256-row GEMM2 units
+    ("mxfp4_shared", 37),      # MXFP4 with the shared expert
+])
+def test_layer_matches_its_stages(name, T):
     """moe_layer equals the four stage calls chained through the C ABI, with
     the GEMM2 rows rounded to bf16 (RNE) before the combine, as the layer
     keeps them internally."""
     moe = M()
-    wl = REDUCED["fp8_zipf_shared"]
-    T = 19
+    wl = REDUCED[name]
+    _note(f"layer == stages {name} T={T}")
     w, _ = weights_for(wl)
     x, ids, tw = inputs_for(wl, T, seed=10)
     cfg = moe.Cfg.for_workload(wl, T)
