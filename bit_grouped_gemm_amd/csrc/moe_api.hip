@@ -157,6 +157,9 @@ int check_cfg(const moe_cfg* c) {
   if (c->topk > 32 || c->E > 1024) return MOE_ERR_BAD_SHAPE;
   if (c->H % 128 || c->I % 128) return MOE_ERR_BAD_SHAPE;
   if (int64_t(c->T) * c->topk >= (int64_t(1) << 24)) return MOE_ERR_BAD_SHAPE;
+  // activation codes are addressed with 32-bit byte offsets inside the GEMMs
+  const int64_t rows = int64_t(c->T) * (c->topk + (c->has_shared ? 1 : 0));
+  if (int64_t(c->T) * c->H >= (int64_t(1) << 31) || rows * c->I >= (int64_t(1) << 31)) return MOE_ERR_BAD_SHAPE;
   if (c->has_shared != 0 && c->has_shared != 1) return MOE_ERR_BAD_SHAPE;
   if (c->wfmt == MOE_WFMT_FP8_BLOCK) {
     if (c->wblk != 32 && c->wblk != 128) return MOE_ERR_UNSUPPORTED;

@@ -295,27 +295,47 @@ struct Frag {
   float xsv[NTT];  // activation scale of this lane's token column
 };
 
-// wtile[j]: this lane's bytes in weight tile j of K step 0 (tiled layout);
-// wstep: bytes between K steps of the tiled tensor; wsb[j] / sstep: the same
-// for the MXFP4 scale tiles
+// Operand sources of the K loop: buffer resources over the group's weight
+// matrix (tiled layout) and MXFP4 scale tiles, the activation codes and the
+// activation scales, with this lane's byte offsets at K step 0.  A K step
+// adds a wave-uniform stride through the scalar offset, so the per-lane
+// offsets stay fixed over the loop and no 64-bit addresses are formed.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+
+template <int NJ, int NTT>
+struct KSrc {
+  __amdgpu_buffer_rsrc_t wr, sr, ar, xr;
+  int wo[NJ];   // weight tile j: the tile's offset + 16 lane
+  int so[NJ];   // MXFP4: scale byte of tile j (the tile's 64 bytes + lane)
+  int bo[NTT];  // token column t: its code row + 16 g
+  int xo[NTT];  // token column t: its scale row, in bytes
+  int wstep, sstep, astep;  // bytes per K step: weight tiles, scale tiles, activation scales
+};
+
 template <int WF, int NJ, int NTT, int B32>
-__device__ __forceinline__ void load_frag(Frag<WF, NJ, NTT>& f, const uint8_t* const (&wtile)[NJ],
-                                          const float* const (&wsc)[NJ], const uint8_t* const (&wsb)[NJ],
-                                          const uint8_t* const (&brow)[NTT], const float* const (&bsc)[NTT],
-                                          int ks, int g, long wstep, long sstep) {
+__device__ __forceinline__ void load_frag(Frag<WF, NJ, NTT>& f, const KSrc<NJ, NTT>& src,
+                                          const float* const (&wsc)[NJ], int ks) {
+  const int kw = ks * src.wstep, ksc = ks * src.sstep, ka = ks * 128, kx = ks * src.astep;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    f.a[j] = load_tile_frag<WF>(wtile[j] + ks * wstep);
+    const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(src.wr, src.wo[j], kw, 0);
     if (WF == 0) {
+      const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(src.wr, src.wo[j] + 1024, kw, 0);
+      f.a[j] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
       if (!B32) f.wsc[j] = wsc[j][ks];
     } else {
-      f.wsb[j] = wsb[j][ks * sstep];
+      f.a[j] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), 0, 0, 0, 0};
+      f.wsb[j] = __builtin_amdgcn_raw_buffer_load_b8(src.sr, src.so[j], ksc, 0);
     }
   }
 #pragma unroll
   for (int t = 0; t < NTT; ++t) {
-    f.b[t] = load_e4m3_frag(brow[t] + ks * 128, g);
-    if (!B32) f.xsv[t] = bsc[t][ks];
+    const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(src.ar, src.bo[t], ka, 0);
+    const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(src.ar, src.bo[t] + 64, ka, 0);
+    f.b[t] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+    if (!B32) f.xsv[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(src.xr, src.xo[t], kx, 0));
   }
 }
 
@@ -366,21 +386,18 @@ __device__ __forceinline__ void mma_frag(v4f (&acc)[NJ][NTT], const Frag<WF, NJ,
 // hit in cache) so the compiler can count outstanding loads exactly and
 // wait only for the stage about to be used; only the MFMAs are predicated.
 template <int WF, int NJ, int NTT, int B32, int ST>
-__device__ __forceinline__ void kloop(v4f (&acc)[NJ][NTT], const uint8_t* const (&wtile)[NJ],
-                                      const float* const (&wsc)[NJ], const uint8_t* const (&wsb)[NJ],
-                                      const uint8_t* const (&brow)[NTT], const float* const (&bsc)[NTT],
-                                      int ks0, int ks1, int g, long wstep, long sstep) {
+__device__ __forceinline__ void kloop(v4f (&acc)[NJ][NTT], const KSrc<NJ, NTT>& src, const float* const (&wsc)[NJ],
+                                      const float* const (&bsc)[NTT], int ks0, int ks1, int g) {
   Frag<WF, NJ, NTT> f[ST];
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s) {
-    load_frag<WF, NJ, NTT, B32>(f[s], wtile, wsc, wsb, brow, bsc, min(ks0 + s, ks1 - 1), g, wstep, sstep);
+    load_frag<WF, NJ, NTT, B32>(f[s], src, wsc, min(ks0 + s, ks1 - 1));
     __builtin_amdgcn_sched_barrier(0);  // keep each stage's loads together, in stage order
   }
   for (int ks = ks0; ks < ks1; ks += ST) {
 #pragma unroll
     for (int s = 0; s < ST; ++s) {
-      load_frag<WF, NJ, NTT, B32>(f[(s + ST - 1) % ST], wtile, wsc, wsb, brow, bsc, min(ks + s + ST - 1, ks1 - 1), g,
-                                  wstep, sstep);
+      load_frag<WF, NJ, NTT, B32>(f[(s + ST - 1) % ST], src, wsc, min(ks + s + ST - 1, ks1 - 1));
       __builtin_amdgcn_sched_barrier(0);
       if (ks + s < ks1) mma_frag<WF, NJ, NTT, B32>(acc, f[s], wsc, bsc, ks + s, g);
       __builtin_amdgcn_sched_barrier(0);
@@ -517,44 +534,48 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
   const bool shared = e == p.E;
   const long ee = shared ? 0 : e;
   const long kbytes = WF == 0 ? H : H / 2;
-  const uint8_t* wbase = (shared ? p.sw : p.w) + ee * 2L * I * kbytes;
-  const long wstep = long(2 * I / 16) * kTileBytes<WF>, sstep = long(2 * I / 16) * kTileScaleBytes;
-  const uint8_t* wtile[4];
+  KSrc<4, NTT> src;
+  src.wr = buf_rsrc((shared ? p.sw : p.w) + ee * 2L * I * kbytes);
+  src.sr = buf_rsrc(static_cast<const uint8_t*>(shared ? p.sws : p.ws) + (WF == 1 ? ee * 2L * I * (H / 32) : 0));
+  src.ar = buf_rsrc(p.act);
+  src.xr = buf_rsrc(p.act_s);
+  src.wstep = (2 * I / 16) * kTileBytes<WF>;
+  src.sstep = (2 * I / 16) * kTileScaleBytes;
+  src.astep = 4;
   const float* wsc[4];
-  const uint8_t* wsb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int rb = (j < 2) ? (n0 + 32 * w + 16 * j) : (I + n0 + 32 * w + 16 * (j - 2));
-    wtile[j] = wbase + long(rb / 16) * kTileBytes<WF> + lane * 16;
+    src.wo[j] = (rb / 16) * kTileBytes<WF> + lane * 16;
+    src.so[j] = (rb / 16) * kTileScaleBytes + lane;
+    wsc[j] = nullptr;
     if (WF == 0) {
       const int b = p.wblk;
       const float* sb = static_cast<const float*>(shared ? p.sws : p.ws) + ee * long(2 * I / b) * (H / b);
-      wsc[j] = sb + long(rb / b) * (H / b);
-      wsb[j] = nullptr;
-    } else {
-      const uint8_t* sb = static_cast<const uint8_t*>(shared ? p.sws : p.ws) + ee * 2L * I * (H / 32);
-      wsb[j] = sb + long(rb / 16) * kTileScaleBytes + lane;
-      wsc[j] = nullptr;
+      // 128-row blocks: a wave's two gate tiles (and its two up tiles) lie in
+      // one block, so they share one scale pointer (and one load per step)
+      const int brow = B32 ? rb / b : ((j < 2) ? n0 : I + n0) / 128;
+      wsc[j] = sb + long(brow) * (H / b);
     }
   }
   const int nks = H / 128, kps = nks / S, ks0 = split * kps, ks1 = ks0 + kps;
   const int npass = (ne + 16 * NTT - 1) / (16 * NTT);
   for (int pass = 0; pass < npass; ++pass) {
-    const uint8_t* brow[NTT];
     const float* bsc[NTT];
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
       const int idx = min(pass * 16 * NTT + t * 16 + m, ne - 1);
-      const long tok = p.row_token[row0 + idx];
-      brow[t] = p.act + tok * H;
-      bsc[t] = p.act_s + tok * (H / p.G);
+      const int tok = p.row_token[row0 + idx];
+      src.bo[t] = tok * H + 16 * g;
+      src.xo[t] = tok * (H / p.G) * 4;
+      bsc[t] = p.act_s + long(tok) * (H / p.G);
     }
     v4f acc[4][NTT];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int t = 0; t < NTT; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    kloop<WF, 4, NTT, B32, kStages>(acc, wtile, wsc, wsb, brow, bsc, ks0, ks1, g, wstep, sstep);
+    kloop<WF, 4, NTT, B32, kStages>(acc, src, wsc, bsc, ks0, ks1, g);
     if (S == 1) {
       swiglu_requant_store<NTT>(acc, p, row0, ne, pass, n0, s_red);
     } else {
@@ -612,43 +633,46 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
   const bool shared = e == p.E;
   const long ee = shared ? 0 : e;
   const long kbytes = WF == 0 ? I : I / 2;
-  const uint8_t* wbase = (shared ? p.sw : p.w) + ee * long(H) * kbytes;
-  const long wstep = long(H / 16) * kTileBytes<WF>, sstep = long(H / 16) * kTileScaleBytes;
-  const uint8_t* wtile[NJ];
+  KSrc<NJ, NTT> src;
+  src.wr = buf_rsrc((shared ? p.sw : p.w) + ee * long(H) * kbytes);
+  src.sr = buf_rsrc(static_cast<const uint8_t*>(shared ? p.sws : p.ws) + (WF == 1 ? ee * long(H) * (I / 32) : 0));
+  src.ar = buf_rsrc(p.act);
+  src.xr = buf_rsrc(p.act_s);
+  src.wstep = (H / 16) * kTileBytes<WF>;
+  src.sstep = (H / 16) * kTileScaleBytes;
+  src.astep = 4;
   const float* wsc[NJ];
-  const uint8_t* wsb[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int rb = n0 + 16 * NJ * w + 16 * j;
-    wtile[j] = wbase + long(rb / 16) * kTileBytes<WF> + lane * 16;
+    src.wo[j] = (rb / 16) * kTileBytes<WF> + lane * 16;
+    src.so[j] = (rb / 16) * kTileScaleBytes + lane;
+    wsc[j] = nullptr;
     if (WF == 0) {
       const int b = p.wblk;
       const float* sb = static_cast<const float*>(shared ? p.sws : p.ws) + ee * long(H / b) * (I / b);
-      wsc[j] = sb + long(rb / b) * (I / b);
-      wsb[j] = nullptr;
-    } else {
-      const uint8_t* sb = static_cast<const uint8_t*>(shared ? p.sws : p.ws) + ee * long(H) * (I / 32);
-      wsb[j] = sb + long(rb / 16) * kTileScaleBytes + lane;
-      wsc[j] = nullptr;
+      // 128-row blocks: the wave's NJ tiles lie in one block and share its scale
+      const int brow = B32 ? rb / b : (n0 + 16 * NJ * w) / 128;
+      wsc[j] = sb + long(brow) * (I / b);
     }
   }
   const int nks = I / 128, kps = nks / S, ks0 = split * kps, ks1 = ks0 + kps;
   const int npass = (ne + 16 * NTT - 1) / (16 * NTT);
   for (int pass = 0; pass < npass; ++pass) {
-    const uint8_t* brow[NTT];
     const float* bsc[NTT];
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
-      const long r = row0 + min(pass * 16 * NTT + t * 16 + m, ne - 1);
-      brow[t] = p.act + r * I;
-      bsc[t] = p.act_s + r * (I / p.G);
+      const int r = row0 + min(pass * 16 * NTT + t * 16 + m, ne - 1);
+      src.bo[t] = r * I + 16 * g;
+      src.xo[t] = r * (I / p.G) * 4;
+      bsc[t] = p.act_s + long(r) * (I / p.G);
     }
     v4f acc[NJ][NTT];
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int t = 0; t < NTT; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    kloop<WF, NJ, NTT, B32, kStages>(acc, wtile, wsc, wsb, brow, bsc, ks0, ks1, g, wstep, sstep);
+    kloop<WF, NJ, NTT, B32, kStages>(acc, src, wsc, bsc, ks0, ks1, g);
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
       const int idx = pass * 16 * NTT + t * 16 + m;

@@ -73,7 +73,7 @@ enum { MOE_WFMT_FP8_BLOCK = 0, MOE_WFMT_MXFP4 = 1 };
  *   every token with weight 1 (GC-MoE abstract: shared experts as an
  *   option; FusedDeepMoE shared-expert path: all tokens in one group).
  * Limits: 1 <= E <= 1024, topk <= 32, H and I multiples of 128,
- *   T * topk < 2^24. */
+ *   T * topk < 2^24, T * H < 2^31 and (T * topk + T * has_shared) * I < 2^31. */
 typedef struct moe_cfg {
   int32_t T, H, I, E, topk;
   int32_t wfmt;

@@ -62,6 +62,10 @@ def test_workspace_size_and_shape_errors(lib):
     assert ws_size(cfg(T=-1))[0] == moe.MOE_ERR_BAD_SHAPE
     assert ws_size(cfg(H=200))[0] == moe.MOE_ERR_BAD_SHAPE         # not a multiple of 128
     assert ws_size(cfg(E=2000, topk=2))[0] == moe.MOE_ERR_BAD_SHAPE
+    # activation bytes beyond 32-bit offsets: T * H, and rows * I
+    assert ws_size(cfg(T=1 << 18, H=8192))[0] == moe.MOE_ERR_BAD_SHAPE
+    assert ws_size(cfg(T=(1 << 18) - 1, H=8192))[0] == moe.MOE_OK
+    assert ws_size(cfg(T=1 << 16, topk=4, I=8192))[0] == moe.MOE_ERR_BAD_SHAPE
     assert ws_size(cfg(wblk=64, act_group=64))[0] == moe.MOE_ERR_UNSUPPORTED
     assert ws_size(cfg(act_group=128))[0] == moe.MOE_ERR_BAD_SHAPE  # FP8 group != block
     assert ws_size(cfg(wfmt=1, wblk=32, act_group=128))[0] == moe.MOE_OK
