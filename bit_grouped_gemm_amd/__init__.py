@@ -42,7 +42,7 @@ WFMT_FP8_BLOCK = 0
 WFMT_MXFP4 = 1
 
 EXPORTS = ("moe_workspace_size", "moe_permute", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm2",
-           "moe_combine", "moe_layer", "moe_prepack_weights", "moe_status_str")
+           "moe_combine", "moe_layer", "moe_prepack_weights", "moe_stream_read", "moe_status_str")
 
 
 class MoeCfg(C.Structure):
@@ -82,6 +82,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     L.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
     L.moe_layer.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp]
     L.moe_prepack_weights.argtypes = [cfgp, wp, wp, vp]
+    L.moe_stream_read.argtypes = [vp, sz, vp, sz, vp]
     L.moe_status_str.argtypes = [C.c_int]
     L.moe_status_str.restype = C.c_char_p
     for n in EXPORTS:
@@ -246,6 +247,16 @@ def moe_prepack_weights(cfg: Cfg, weights) -> TiledWeights:
 
 
 
+
+
+def moe_stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Read every byte of a device buffer once (a plain HBM read stream);
+    returns the sink (one folded word per workgroup, one workgroup per CU)."""
+    if sink is None:
+        sink = torch.empty(8192, dtype=torch.int32, device=buf.device)
+    _check("moe_stream_read", load().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                                      sink.numel() * sink.element_size(), _stream()))
+    return sink
 
 
 def raw_call(name: str, *args) -> int:

@@ -382,6 +382,14 @@ int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_we
   return MOE_OK;
 }
 
+int moe_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes, void* stream) {
+  if (!buf || !sink) return MOE_ERR_NULL_ARG;
+  if (misaligned(buf) || misaligned(sink)) return MOE_ERR_MISALIGNED;
+  if (bytes % 16) return MOE_ERR_BAD_SHAPE;
+  if (sink_bytes < 4 * size_t(stream_read_grid())) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_stream_read(buf, bytes, static_cast<uint32_t*>(sink), static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_str(int status) {
   switch (status) {
     case MOE_OK: return "ok";

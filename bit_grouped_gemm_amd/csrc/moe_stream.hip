@@ -1,0 +1,73 @@
+// moe_stream.hip -- a plain HBM read stream, the achievable-bandwidth
+// reference the weight-streaming GEMMs are compared with.
+//
+// The buffer is cut into one contiguous region per wave (a multiple of the
+// 4 KiB a wave reads per step); a wave reads its region front to back with
+// four 1 KiB loads in flight (16 bytes a lane, consecutive lanes on
+// consecutive chunks).  One workgroup of four waves per CU.  Each workgroup
+// folds what it read into one word of the sink, so the loads cannot be
+// dropped.
+#include "moe_device.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kStreamThreads = 256;
+constexpr int kStreamLoads = 4;                      // 1 KiB loads per wave per step
+constexpr long kStreamStep = long(kWave) * kStreamLoads;  // 16-byte chunks per wave per step
+
+__global__ __launch_bounds__(kStreamThreads) void k_stream_read(const v4u* __restrict__ src, long n16, long per_wave,
+                                                               uint32_t* __restrict__ sink) {
+  __shared__ uint32_t s_acc[kStreamThreads / kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const long wave = long(blockIdx.x) * (kStreamThreads / kWave) + threadIdx.x / kWave;
+  const long beg = wave * per_wave;
+  const long end = beg + per_wave < n16 ? beg + per_wave : n16;
+  uint32_t acc = 0;
+  long s = beg;
+  for (; s + kStreamStep <= end; s += kStreamStep) {
+    v4u v[kStreamLoads];
+#pragma unroll
+    for (int u = 0; u < kStreamLoads; ++u) v[u] = src[s + u * kWave + lane];
+#pragma unroll
+    for (int u = 0; u < kStreamLoads; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (long j = s + lane; j < end; j += kWave) {
+    const v4u v = src[j];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  for (int o = kWave / 2; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, kWave);
+  if (lane == 0) s_acc[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t a = 0;
+    for (int w = 0; w < kStreamThreads / kWave; ++w) a ^= s_acc[w];
+    sink[blockIdx.x] = a;
+  }
+}
+
+}  // namespace
+
+int stream_read_grid() {
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    ncu = 256;
+  return ncu;
+}
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st) {
+  const long n16 = long(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int grid = stream_read_grid();
+  const long waves = long(grid) * (kStreamThreads / kWave);
+  long per = (n16 + waves - 1) / waves;
+  per = (per + kStreamStep - 1) / kStreamStep * kStreamStep;
+  hipLaunchKernelGGL(k_stream_read, dim3(unsigned(grid)), dim3(kStreamThreads), 0, st, static_cast<const v4u*>(buf),
+                     n16, per, sink);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -165,3 +165,13 @@ def test_prepack_argument_errors(lib):
     assert call(C.byref(cc), C.byref(src), C.byref(src)) == moe.MOE_ERR_UNSUPPORTED   # in place
     cs = cfg(has_shared=1).c()
     assert call(C.byref(cs), C.byref(src), C.byref(dst)) == moe.MOE_ERR_NULL_ARG       # shared tensors
+
+
+def test_stream_read_argument_errors(lib):
+    call = lambda buf, n, sink, sn: moe.raw_call("moe_stream_read", buf, C.c_size_t(n), sink, C.c_size_t(sn), None)
+    assert call(None, 64, FAKE, 1 << 15) == moe.MOE_ERR_NULL_ARG
+    assert call(FAKE, 64, None, 1 << 15) == moe.MOE_ERR_NULL_ARG
+    assert call(FAKE + 4, 64, FAKE, 1 << 15) == moe.MOE_ERR_MISALIGNED
+    assert call(FAKE, 64, FAKE + 8, 1 << 15) == moe.MOE_ERR_MISALIGNED
+    assert call(FAKE, 65, FAKE, 1 << 15) == moe.MOE_ERR_BAD_SHAPE
+    assert call(FAKE, 64, FAKE, 4) == moe.MOE_ERR_WORKSPACE

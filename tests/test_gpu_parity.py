@@ -496,3 +496,20 @@ def test_worked_examples_on_gpu():
             for i, v in ex["expect_out"][str(t)]:
                 want[i] = v
             assert np.array_equal(got[t], want), (ex["name"], t, got[t][:4])
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (1 << 24) + 16 * 37])
+def test_stream_read_reads_every_word(nbytes):
+    """The plain read stream folds every 32-bit word of the buffer exactly
+    once: the XOR of its sink equals the XOR of the buffer (ragged sizes
+    exercise the strided tail)."""
+    moe = M()
+    _note(f"stream_read nbytes={nbytes}")
+    g = torch.Generator().manual_seed(nbytes)
+    host = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, generator=g)
+    sink = torch.zeros(8192, dtype=torch.int32, device=DEV)
+    moe.moe_stream_read(host.to(DEV), sink)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want
