@@ -56,6 +56,14 @@ static int choose_ntt(int T, int k, int E) {
   return est <= 16 ? 1 : (est <= 32 ? 2 : 4);
 }
 
+// Upper bound on the decode GEMMs' work items, sum over non-empty groups of
+// ceil(n_g / R): with N rows in at most Gn groups each group adds at most
+// (n_g + R - 1) / R, and every item holds a row.
+static int items_bound(long N, long Gn, int R) {
+  if (N <= 0 || Gn <= 0) return 0;
+  return int(std::min(N, (N + Gn * (R - 1)) / R));
+}
+
 Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, int shared) {
   Shape s{};
   s.T = T; s.H = H; s.I = I; s.E = E; s.k = k; s.wfmt = wfmt; s.wblk = wblk; s.G = G; s.shared = shared;
@@ -69,6 +77,8 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   // (measured cold-cache: T = 64 layers 2-8 % faster, T <= 32 1-3 % slower)
   s.g2_nj = (MOE_G2_NJ == 4 && H % 256 == 0 && s.g2_ntt >= 2) ? 4 : 2;
   s.g2_tiles = H / (64 * s.g2_nj);
+  s.g1_items = items_bound(s.rows_cap, s.slots_max, 16 * s.g1_ntt);
+  s.g2_items = items_bound(s.rows_cap, s.slots_max, 16 * s.g2_ntt);
   s.g1_split = choose_split(long(s.slots_max) * s.g1_tiles, H / 128);
   s.g2_split = choose_split(long(s.slots_max) * s.g2_tiles, I / 128);
   // partial sums are addressed with 32-bit byte offsets: keep them under 2 GiB
@@ -137,8 +147,8 @@ WsLayout make_ws_layout(const Shape& s) {
   L.chunk_cnt = take(s.perm_chunks > 1 ? 4 * size_t(s.perm_chunks) * s.E : 0);
   // the two counter arrays are adjacent so one clear covers both
   L.cnt1 = o;
-  L.cnt2 = L.cnt1 + 4 * size_t(s.E + 1) * s.g1_tiles;
-  o = align256(L.cnt2 + 4 * size_t(s.E + 1) * s.g2_tiles);
+  L.cnt2 = L.cnt1 + 4 * size_t(s.g1_items) * s.g1_tiles;
+  o = align256(L.cnt2 + 4 * size_t(s.g2_items) * s.g2_tiles);
   L.total = o;
   return L;
 }
@@ -251,7 +261,7 @@ int moe_grouped_gemm1_swiglu(const moe_cfg* cfg, const uint8_t* xq, const float*
                                        hq, hs, 1, st));
   int32_t* cnt = reinterpret_cast<int32_t*>(base + L.cnt1);
   if (s.g1_split > 1) {
-    if ((rc = hip_status(launch_clear(cnt, (s.E + 1) * s.g1_tiles, st)))) return rc;
+    if ((rc = hip_status(launch_clear(cnt, s.g1_items * s.g1_tiles, st)))) return rc;
   }
   return hip_status(launch_gemm1(s, xq, xs, row_token, offsets,
                                  WeightPtrs{static_cast<const uint8_t*>(w->w1), w->w1s,
@@ -280,7 +290,7 @@ int moe_grouped_gemm2(const moe_cfg* cfg, const uint8_t* hq, const float* hs, co
                                        y, nullptr, 1, st));
   int32_t* cnt = reinterpret_cast<int32_t*>(base + L.cnt2);
   if (s.g2_split > 1) {
-    if ((rc = hip_status(launch_clear(cnt, (s.E + 1) * s.g2_tiles, st)))) return rc;
+    if ((rc = hip_status(launch_clear(cnt, s.g2_items * s.g2_tiles, st)))) return rc;
   }
   return hip_status(launch_gemm2(s, hq, hs, offsets,
                                  WeightPtrs{static_cast<const uint8_t*>(w->w2), w->w2s,

@@ -102,9 +102,14 @@ struct BigParams {
 };
 
 // one 16-byte-per-lane direct load into LDS: lane l's bytes land at
-// lds_base + 16 * l (lds_base wave-uniform)
+// lds_base + 16 * l (lds_base wave-uniform).  Token rows are re-read by the
+// group's other units and keep the default policy; weights and their scales
+// are read once per pass and go non-temporal (cache-policy operand nt).
 __device__ __forceinline__ void dma16(const void* src, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma16nt(const void* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 2);
 }
 __device__ __forceinline__ void dma4(const void* src, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(src, lds_base, 4, 0, 0);
@@ -320,7 +325,11 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
 #pragma unroll
     for (int j = 0; j < L; ++j)
       if (j >= ja0 && j < ja1) {
-        dma16(src16[j], st + dst16[j]);
+        // slot j is a token-row load in wave w when w + 8 j < kTokLoads
+        if (8 * j + 7 < Geo::kTokLoads) dma16(src16[j], st + dst16[j]);
+        else if (8 * j >= Geo::kTokLoads) dma16nt(src16[j], st + dst16[j]);
+        else if (w + 8 * j < Geo::kTokLoads) dma16(src16[j], st + dst16[j]);
+        else dma16nt(src16[j], st + dst16[j]);
         src16[j] += stride16[j];
       }
   };

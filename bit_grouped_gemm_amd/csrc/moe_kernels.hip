@@ -250,38 +250,50 @@ __global__ __launch_bounds__(kThreads) void k_clear(int32_t* p, int n) {
 // =====================================================================
 // grouped GEMM machinery
 // =====================================================================
-// Group id of the slot-th non-empty group (offsets[g+1] > offsets[g]), or -1.
-// Block-wide; every thread gets the same answer.
-__device__ int nth_nonempty_group(const int32_t* offsets, int ngroups, int slot, int* s_wsum, int* s_res) {
+// Work items of the decode GEMMs: a group with n rows holds ceil(n / R)
+// items of R rows each (one pass of the kernel), so the passes of a heavy
+// group run side by side on different workgroups rather than one after the
+// other on one.  Returns the group of the item-th item (groups in order) and
+// sets *pass to that item's index within its group, or returns -1 when there
+// are fewer items.  Block-wide; every thread gets the same answer.
+__device__ int nth_item(const int32_t* offsets, int ngroups, int item, int R, int* pass, int* s_wsum, int* s_res) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int gpt = (ngroups + kThreads - 1) / kThreads;  // <= 5
   int local = 0;
   for (int q = 0; q < gpt; ++q) {
     const int g = tid * gpt + q;
-    if (g < ngroups && offsets[g + 1] > offsets[g]) ++local;
+    if (g < ngroups) local += (offsets[g + 1] - offsets[g] + R - 1) / R;
   }
   int incl = local;
   for (int d = 1; d < 64; d <<= 1) {
     const int v = __shfl_up(incl, d, 64);
     if (lane >= d) incl += v;
   }
-  if (tid == 0) *s_res = -1;
+  if (tid == 0) {
+    s_res[0] = -1;
+    s_res[1] = 0;
+  }
   if (lane == 63) s_wsum[w] = incl;
   __syncthreads();
   int run = incl - local;
   for (int q = 0; q < w; ++q) run += s_wsum[q];
-  if (slot >= run && slot < run + local) {
+  if (item >= run && item < run + local) {
     int c = run;
     for (int q = 0; q < gpt; ++q) {
       const int g = tid * gpt + q;
-      if (g < ngroups && offsets[g + 1] > offsets[g]) {
-        if (c == slot) *s_res = g;
-        ++c;
+      if (g >= ngroups) break;
+      const int n = (offsets[g + 1] - offsets[g] + R - 1) / R;
+      if (item < c + n) {
+        s_res[0] = g;
+        s_res[1] = item - c;
+        break;
       }
+      c += n;
     }
   }
   __syncthreads();
-  return *s_res;
+  *pass = s_res[1];
+  return s_res[0];
 }
 
 // Operands of one 128-K step for a wave: NJ weight tiles of 16 rows and NTT
@@ -304,6 +316,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
 }
 
+// cache-policy operand of the buffer intrinsics for the weight and weight
+// scale loads: nt (non-temporal: each weight byte is read once per layer, so
+// its lines are not kept in the caches)
+constexpr int kNt = 2;
+
 template <int NJ, int NTT>
 struct KSrc {
   __amdgpu_buffer_rsrc_t wr, sr, ar, xr;
@@ -320,14 +337,14 @@ __device__ __forceinline__ void load_frag(Frag<WF, NJ, NTT>& f, const KSrc<NJ, N
   const int kw = ks * src.wstep, ksc = ks * src.sstep, ka = ks * 128, kx = ks * src.astep;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(src.wr, src.wo[j], kw, 0);
+    const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(src.wr, src.wo[j], kw, kNt);
     if (WF == 0) {
-      const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(src.wr, src.wo[j] + 1024, kw, 0);
+      const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(src.wr, src.wo[j] + 1024, kw, kNt);
       f.a[j] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
       if (!B32) f.wsc[j] = wsc[j][ks];
     } else {
       f.a[j] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), 0, 0, 0, 0};
-      f.wsb[j] = __builtin_amdgcn_raw_buffer_load_b8(src.sr, src.so[j], ksc, 0);
+      f.wsb[j] = __builtin_amdgcn_raw_buffer_load_b8(src.sr, src.so[j], ksc, kNt);
     }
   }
 #pragma unroll
@@ -520,12 +537,13 @@ __device__ __forceinline__ void swiglu_requant_store(const v4f (&acc)[4][NTT], c
 
 template <int WF, int NTT, int B32>
 __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
-  __shared__ int s_wsum[4], s_res, s_flag;
+  __shared__ int s_wsum[4], s_res[2], s_flag;
   __shared__ float s_red[NTT][4][16];
   const int S = p.S, nt = p.ntiles;
   const int u = blockIdx.x;
-  const int split = u % S, tile = (u / S) % nt, slot = u / (S * nt);
-  const int e = nth_nonempty_group(p.offsets, p.ngroups, slot, s_wsum, &s_res);
+  const int split = u % S, tile = (u / S) % nt, item = u / (S * nt);
+  int pass0 = 0;
+  const int e = nth_item(p.offsets, p.ngroups, item, 16 * NTT, &pass0, s_wsum, s_res);
   if (e < 0) return;
   const int row0 = p.offsets[e], ne = p.offsets[e + 1] - row0;
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 15, g = lane >> 4;
@@ -559,8 +577,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
     }
   }
   const int nks = H / 128, kps = nks / S, ks0 = split * kps, ks1 = ks0 + kps;
-  const int npass = (ne + 16 * NTT - 1) / (16 * NTT);
-  for (int pass = 0; pass < npass; ++pass) {
+  // this workgroup's one pass (work item) of the group's rows
+  for (int pass = pass0; pass < pass0 + 1; ++pass) {
     const float* bsc[NTT];
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
@@ -593,8 +611,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
     }
   }
   if (S == 1) return;
-  if (!arrive_last(p.cnt + e * nt + tile, S, &s_flag)) return;
-  for (int pass = 0; pass < npass; ++pass) {
+  if (!arrive_last(p.cnt + item * nt + tile, S, &s_flag)) return;
+  for (int pass = pass0; pass < pass0 + 1; ++pass) {
     v4f acc[4][NTT];
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
@@ -619,11 +637,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
 // ---------------------------------------------------------------------
 template <int WF, int NTT, int B32, int NJ>
 __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
-  __shared__ int s_wsum[4], s_res, s_flag;
+  __shared__ int s_wsum[4], s_res[2], s_flag;
   const int S = p.S, nt = p.ntiles;
   const int u = blockIdx.x;
-  const int split = u % S, tile = (u / S) % nt, slot = u / (S * nt);
-  const int e = nth_nonempty_group(p.offsets, p.ngroups, slot, s_wsum, &s_res);
+  const int split = u % S, tile = (u / S) % nt, item = u / (S * nt);
+  int pass0 = 0;
+  const int e = nth_item(p.offsets, p.ngroups, item, 16 * NTT, &pass0, s_wsum, s_res);
   if (e < 0) return;
   const int row0 = p.offsets[e], ne = p.offsets[e + 1] - row0;
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 15, g = lane >> 4;
@@ -657,8 +676,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
     }
   }
   const int nks = I / 128, kps = nks / S, ks0 = split * kps, ks1 = ks0 + kps;
-  const int npass = (ne + 16 * NTT - 1) / (16 * NTT);
-  for (int pass = 0; pass < npass; ++pass) {
+  // this workgroup's one pass (work item) of the group's rows
+  for (int pass = pass0; pass < pass0 + 1; ++pass) {
     const float* bsc[NTT];
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
@@ -691,11 +710,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
     }
   }
   if (S == 1) return;
-  if (!arrive_last(p.cnt + e * nt + tile, S, &s_flag)) return;
-  // reduce the S partial sums in split order: kRows columns x ne rows
+  if (!arrive_last(p.cnt + item * nt + tile, S, &s_flag)) return;
+  // reduce the S partial sums in split order: kRows columns x the pass's rows
   constexpr int kQ = kRows / 4;  // 4-column pieces per row
-  for (int q = tid; q < ne * kQ; q += kThreads) {
-    const long r = row0 + q / kQ;
+  const int r0 = pass0 * 16 * NTT, nr = min(ne - r0, 16 * NTT);
+  for (int q = tid; q < nr * kQ; q += kThreads) {
+    const long r = row0 + r0 + q / kQ;
     const int col = (q % kQ) * 4;
     v4f s = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int sp = 0; sp < S; ++sp)
@@ -861,7 +881,7 @@ hipError_t launch_gemm1(const Shape& s, const uint8_t* xq, const float* xs, cons
   p.hq = hq; p.hs = hs; p.part = part; p.cnt = cnt;
   p.H = s.H; p.I = s.I; p.E = s.E; p.G = s.G; p.wblk = s.wblk; p.ngroups = s.ngroups;
   p.S = s.g1_split; p.ntiles = s.g1_tiles; p.rows_cap = s.rows_cap;
-  const unsigned grid = unsigned(s.slots_max) * s.g1_tiles * s.g1_split;
+  const unsigned grid = unsigned(s.g1_items) * s.g1_tiles * s.g1_split;
   if (grid == 0) return hipSuccess;
   return dispatch_k_gemm1(s, s.g1_ntt, grid, p, st);
 }
@@ -874,7 +894,7 @@ hipError_t launch_gemm2(const Shape& s, const uint8_t* hq, const float* hs, cons
   p.y = y; p.yb = yb; p.part = part; p.cnt = cnt;
   p.H = s.H; p.I = s.I; p.E = s.E; p.G = s.G; p.wblk = s.wblk; p.ngroups = s.ngroups;
   p.S = s.g2_split; p.ntiles = s.g2_tiles; p.rows_cap = s.rows_cap;
-  const unsigned grid = unsigned(s.slots_max) * s.g2_tiles * s.g2_split;
+  const unsigned grid = unsigned(s.g2_items) * s.g2_tiles * s.g2_split;
   if (grid == 0) return hipSuccess;
   return s.g2_nj == 4 ? dispatch_gemm2_nj<4>(s, s.g2_ntt, grid, p, st)
                       : dispatch_gemm2_nj<2>(s, s.g2_ntt, grid, p, st);

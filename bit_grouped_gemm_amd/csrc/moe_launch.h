@@ -18,11 +18,13 @@ struct Shape {
   int g1_tiles;     // I / 128
   int g1_split;     // K splits over H/128 steps
   int g1_ntt;       // 16-token tiles per pass (1, 2 or 4)
+  int g1_items;     // upper bound on work items (one pass of 16 g1_ntt rows of one group)
   // GEMM2: unit = 64 g2_nj output rows of one group
   int g2_nj;        // weight tiles per wave: 4 (256-row units) when H % 256 == 0, else 2
   int g2_tiles;     // H / (64 g2_nj)
   int g2_split;     // K splits over I/128 steps
   int g2_ntt;
+  int g2_items;     // as g1_items, passes of 16 g2_ntt rows
   // groups with many rows (prefill) run the 256 x 256-token LDS-staged kernels
   int big;          // 1: both GEMMs use the big-tile kernels
   int big_cap;      // their token rows per pass: 64 or 160
@@ -36,7 +38,7 @@ struct WsLayout {
   size_t counts, offsets, expand_idx, row_token;  // layer-internal permute outputs
   size_t xq, xs, hq, hs, y;                       // layer-internal activations
   size_t part1, part2;                            // split-K partial sums (fp32)
-  size_t cnt1, cnt2;                              // split-K arrival counters (int32)
+  size_t cnt1, cnt2;                              // split-K arrival counters (int32), per work item and tile
   size_t chunk_cnt;                               // permute per-chunk expert counts (int32)
   size_t total;
 };

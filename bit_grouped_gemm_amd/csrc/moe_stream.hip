@@ -3,10 +3,10 @@
 //
 // The buffer is cut into one contiguous region per wave (a multiple of the
 // 4 KiB a wave reads per step); a wave reads its region front to back with
-// four 1 KiB loads in flight (16 bytes a lane, consecutive lanes on
-// consecutive chunks).  One workgroup of four waves per CU.  Each workgroup
-// folds what it read into one word of the sink, so the loads cannot be
-// dropped.
+// four 1 KiB non-temporal loads in flight (16 bytes a lane, consecutive
+// lanes on consecutive chunks).  Four workgroups of four waves per CU.  Each
+// workgroup folds what it read into one word of the sink, so the loads
+// cannot be dropped.
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -30,12 +30,12 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_read(const v4u* __res
   for (; s + kStreamStep <= end; s += kStreamStep) {
     v4u v[kStreamLoads];
 #pragma unroll
-    for (int u = 0; u < kStreamLoads; ++u) v[u] = src[s + u * kWave + lane];
+    for (int u = 0; u < kStreamLoads; ++u) v[u] = __builtin_nontemporal_load(src + s + u * kWave + lane);
 #pragma unroll
     for (int u = 0; u < kStreamLoads; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   for (long j = s + lane; j < end; j += kWave) {
-    const v4u v = src[j];
+    const v4u v = __builtin_nontemporal_load(src + j);
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   for (int o = kWave / 2; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, kWave);
@@ -55,7 +55,7 @@ int stream_read_grid() {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     ncu = 256;
-  return ncu;
+  return 4 * ncu;
 }
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st) {

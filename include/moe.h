@@ -189,11 +189,12 @@ int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_we
 
 /* Diagnostic: read `bytes` (a multiple of 16) of device memory at `buf`
  * once -- a plain HBM read stream, the achievable-bandwidth reference for
- * the weight-streaming GEMMs.  One workgroup of four waves per CU; each wave
- * reads one contiguous region with 16-byte loads.  `sink` (device, at least
- * 4 * CU-count bytes; 1 KiB covers an MI355X) receives the XOR of the
- * 32-bit words each workgroup read, one word per workgroup, so the XOR over
- * the first CU-count sink words equals the XOR over the buffer.
+ * the weight-streaming GEMMs.  Four workgroups of four waves per CU; each
+ * wave reads one contiguous region with 16-byte non-temporal loads.  `sink`
+ * (device, at least 16 * CU-count bytes; 4 KiB covers an MI355X) receives
+ * the XOR of the 32-bit words each workgroup read, one word per workgroup,
+ * so the XOR over the first 4 * CU-count sink words equals the XOR over the
+ * buffer.
  * MOE_ERR_NULL_ARG, MOE_ERR_MISALIGNED, MOE_ERR_BAD_SHAPE (bytes % 16) and
  * MOE_ERR_WORKSPACE (sink too small) are host checks. */
 int moe_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes, void* stream);
