@@ -366,8 +366,8 @@ def test_layer_full_size_sampled(name, T):
 
 # ------------------------------------------------------------------ big-tile (prefill) path
 BIG = {
-    # many rows per expert select the 256-row x 192-token kernels; the shared group of
-    # T rows needs two 192-token passes when T > 192
+    # many rows per expert select the 256-row x 160-token kernels; the shared group of
+    # T rows needs two 160-token passes when T > 160
     "big_mxfp4_shared": reduced("decode_mxfp4", H=512, I=256, E=4, topk=2, shared=True),
     "big_fp8": reduced("decode_fp8", H=512, I=384, E=6, topk=2),
 }
@@ -436,6 +436,37 @@ def test_layer_masked_slots_and_zero_weights():
     got = out.float().cpu().numpy()
     tol_check(got, ref, "masked")
     assert np.all(got[5] == 0)
+
+
+HEAVY = {
+    # 32-blocks (never the many-row kernels); long K and few units: split-K in
+    # both GEMMs; 64-row passes, so expert 0's T rows are several work items
+    "fp8_b32_split": reduced("tiny_fp8", H=2048, I=2048, E=6, topk=3),
+    # H not a multiple of 256 keeps MXFP4 on the decode kernels; the shared
+    # group's T rows add a second heavy group
+    "mxfp4_h1152_shared": reduced("decode_mxfp4", H=1152, I=512, E=6, topk=3, shared=True),
+}
+
+
+@pytest.mark.parametrize("name", list(HEAVY))
+def test_layer_one_hot_expert_many_passes(name):
+    """Every token routes to expert 0 (its other slots to distinct experts):
+    expert 0 holds all T rows, more than one pass of the decode GEMMs, so its
+    passes run as separate work items with their own split-K counters."""
+    moe = M()
+    wl = HEAVY[name]
+    T = 150
+    _note(f"one-hot expert {name} T={T}")
+    w, wc = weights_for(wl)
+    x, _, tw = inputs_for(wl, T, seed=12)
+    g = torch.Generator().manual_seed(12)
+    others = torch.stack([torch.randperm(wl.E - 1, generator=g)[: wl.topk - 1] + 1 for _ in range(T)])
+    ids = torch.cat([torch.zeros(T, 1, dtype=torch.int64), others], 1).to(torch.int32).to(DEV)
+    cfg = moe.Cfg.for_workload(wl, T)
+    out = moe.moe_layer(cfg, x, ids, tw, w)
+    torch.cuda.synchronize()
+    ref = oracle.layer_for(wl, T, wc).layer(x.cpu(), ids.cpu(), tw.cpu())
+    tol_check(out.float().cpu().numpy(), ref, f"one-hot {name}")
 
 
 def test_poisoned_workspace_and_determinism():
