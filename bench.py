@@ -35,6 +35,7 @@ HBM_PEAK_GBS = 8000.0
 # dense MFMA peak for an e2m1 x e4m3 contraction: the scaled MFMA takes the
 # FP8 rate when either operand is FP8 (MI355X dense FP8: 5.0 PFLOP/s)
 MFMA_PEAK_TFLOPS = 5000.0
+FP4_PEAK_TFLOPS = 10100.0
 FLUSH_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm1_decode_fp8_T64.json")
 KERNEL_SRC = os.path.join(ROOT, "bit_grouped_gemm_amd", "csrc", "moe_kernels.hip")
@@ -283,6 +284,10 @@ def prefill(moe, synth, torch, dev, reps):
     g1_flops = 2.0 * R * (2 * wl.I) * wl.H
     g1_tf = g1_flops / (stages["gemm1_swiglu"] * 1e-6) / 1e12
     tf = flops / (med * 1e-6) / 1e12
+    meas = mfma_rate_tflops(moe, torch, dev, 1)
+    # floor of the layer on HBM: every weight byte + x in + out, at the peak
+    act_bytes = 2 * 2 * T * wl.H
+    hbm_floor_us = (wbytes_all + act_bytes) / (HBM_PEAK_GBS * 1e9) * 1e6
     return {
         "workload": f"{wl.name}: H={wl.H} E={wl.E} top-{wl.topk} I={wl.I} MXFP4 weights, T={T}",
         "layer_us_median": round(med, 1), "layer_us_p10": round(float(np.percentile(lat_us, 10)), 1),
@@ -291,9 +296,31 @@ def prefill(moe, synth, torch, dev, reps):
         "weight_GBps": round(wbytes_all / (med * 1e-6) / 1e9, 1),
         "stages_us_median": stages,
         "gemm1_TFLOPs": round(g1_tf, 1), "gemm1_mfma_frac": round(g1_tf / MFMA_PEAK_TFLOPS, 4),
+        "mfma_measured_TFLOPs": round(meas, 1),
+        "mfma_frac_of_measured": round(tf / meas, 4), "gemm1_frac_of_measured": round(g1_tf / meas, 4),
+        "fp4_peak_frac": round(tf / FP4_PEAK_TFLOPS, 4),
+        "hbm_floor_us": round(hbm_floor_us, 1), "hbm_floor_frac": round(hbm_floor_us / med, 4),
         "reps": reps,
         "note": "stage times use the stage exports (fp32 y); moe_layer keeps y in bf16",
     }
+
+
+def mfma_rate_tflops(moe, torch, dev, wfmt, iters=4096):
+    """Issued rate of the scaled MFMA the prefill GEMMs run (wfmt 1: e2m1
+    weights x e4m3 activations), from the library's rate probe: median of
+    five timed launches of about a millisecond after one untimed one."""
+    sink = torch.empty(8192, dtype=torch.float32, device=dev)
+    moe.moe_mfma_rate(wfmt, iters, sink)
+    ts, fl = [], 0.0
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fl = moe.moe_mfma_rate(wfmt, iters, sink)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    return fl / (ts[len(ts) // 2] * 1e-3) / 1e12
 
 
 def stream_read_gbs(moe, buf, stream, ev):

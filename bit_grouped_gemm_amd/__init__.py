@@ -42,7 +42,8 @@ WFMT_FP8_BLOCK = 0
 WFMT_MXFP4 = 1
 
 EXPORTS = ("moe_workspace_size", "moe_permute", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm2",
-           "moe_combine", "moe_layer", "moe_prepack_weights", "moe_stream_read", "moe_status_str")
+           "moe_combine", "moe_layer", "moe_prepack_weights", "moe_stream_read", "moe_mfma_rate",
+           "moe_status_str")
 
 
 class MoeCfg(C.Structure):
@@ -83,6 +84,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     L.moe_layer.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp]
     L.moe_prepack_weights.argtypes = [cfgp, wp, wp, vp]
     L.moe_stream_read.argtypes = [vp, sz, vp, sz, vp]
+    L.moe_mfma_rate.argtypes = [C.c_int, C.c_int, vp, sz, C.POINTER(C.c_double), vp]
     L.moe_status_str.argtypes = [C.c_int]
     L.moe_status_str.restype = C.c_char_p
     for n in EXPORTS:
@@ -257,6 +259,16 @@ def moe_stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None) -> t
     _check("moe_stream_read", load().moe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                                       sink.numel() * sink.element_size(), _stream()))
     return sink
+
+
+def moe_mfma_rate(wfmt: int, iters: int, sink: torch.Tensor) -> float:
+    """Enqueue the scaled-MFMA rate probe (all operands 1.0); returns the FLOP
+    count enqueued.  `sink` (float32, device) receives 1536 * iters per
+    workgroup."""
+    flops = C.c_double(0.0)
+    _check("moe_mfma_rate", load().moe_mfma_rate(int(wfmt), int(iters), _ptr(sink),
+                                                  sink.numel() * sink.element_size(), C.byref(flops), _stream()))
+    return flops.value
 
 
 def raw_call(name: str, *args) -> int:

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(BUILD, "libmoe.so")
-SOURCES = ["moe_api.hip", "moe_kernels.hip", "moe_gemm_big.hip", "moe_tile.hip", "moe_stream.hip"]
+SOURCES = ["moe_api.hip", "moe_kernels.hip", "moe_gemm_big.hip", "moe_tile.hip", "moe_diag.hip"]
 HEADERS = ["moe_device.h", "moe_launch.h", os.path.join("..", "..", "include", "moe.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

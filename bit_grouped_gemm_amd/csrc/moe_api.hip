@@ -400,6 +400,15 @@ int moe_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes
   return hip_status(launch_stream_read(buf, bytes, static_cast<uint32_t*>(sink), static_cast<hipStream_t>(stream)));
 }
 
+int moe_mfma_rate(int wfmt, int iters, void* sink, size_t sink_bytes, double* flops, void* stream) {
+  if (!sink) return MOE_ERR_NULL_ARG;
+  if (misaligned(sink)) return MOE_ERR_MISALIGNED;
+  if (wfmt != MOE_WFMT_FP8_BLOCK && wfmt != MOE_WFMT_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (iters < 1 || iters > 65536) return MOE_ERR_BAD_SHAPE;
+  if (sink_bytes < 4 * size_t(mfma_rate_grid())) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_mfma_rate(wfmt, iters, static_cast<float*>(sink), flops, static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_str(int status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -1,6 +1,8 @@
-// moe_stream.hip -- a plain HBM read stream, the achievable-bandwidth
-// reference the weight-streaming GEMMs are compared with.
+// moe_diag.hip -- diagnostics the kernels are measured against: a plain HBM
+// read stream (the achievable bandwidth) and the issued rate of the scaled
+// MFMA the GEMMs use (the achievable matrix-core rate).
 //
+// Read stream:
 // The buffer is cut into one contiguous region per wave (a multiple of the
 // 4 KiB a wave reads per step); a wave reads its region front to back with
 // four 1 KiB non-temporal loads in flight (16 bytes a lane, consecutive
@@ -48,7 +50,51 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_read(const v4u* __res
   }
 }
 
+// Issued-rate probe: every wave runs `iters` rounds of kRateAcc independent
+// 16x16x128 scaled MFMAs (operand format FA x e4m3, unit scales) on
+// operands made of the codes a_word / b_word, so the matrix pipe never waits
+// on a result; four workgroups of four waves per CU.  Lane 0 of wave 0
+// stores the sum of its accumulators' elements: with both operands 1.0
+// every MFMA adds exactly 128 to each element, so the stored value is
+// 4 * 128 * kRateAcc * iters (exact in fp32 for iters <= 65536).
+constexpr int kRateAcc = 3;
+
+template <int FA>
+__global__ __launch_bounds__(kStreamThreads) void k_mfma_rate(uint32_t a_word, uint32_t b_word, int iters,
+                                                             float* __restrict__ sink) {
+  const int aw = int(a_word), bw = int(b_word);
+  const v8i a = {aw, aw, aw, aw, aw, aw, aw, aw};
+  const v8i b = {bw, bw, bw, bw, bw, bw, bw, bw};
+  v4f acc[kRateAcc];
+#pragma unroll
+  for (int j = 0; j < kRateAcc; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < kRateAcc; ++j) acc[j] = mfma_scaled_acc<FA, kFmtE4M3>(a, b, acc[j], kUnitScale, kUnitScale);
+  }
+  if (threadIdx.x == 0) {
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kRateAcc; ++j) t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    sink[blockIdx.x] = t;
+  }
+}
+
 }  // namespace
+
+int mfma_rate_grid() { return stream_read_grid(); }
+
+hipError_t launch_mfma_rate(int wfmt, int iters, float* sink, double* flops, hipStream_t st) {
+  const int grid = mfma_rate_grid();
+  if (flops) *flops = double(grid) * (kStreamThreads / kWave) * double(iters) * kRateAcc * (16.0 * 16.0 * 128.0 * 2.0);
+  if (wfmt == 0)  // e4m3 1.0 = 0x38 in every byte
+    hipLaunchKernelGGL(k_mfma_rate<kFmtE4M3>, dim3(unsigned(grid)), dim3(kStreamThreads), 0, st, 0x38383838u,
+                       0x38383838u, iters, sink);
+  else  // e2m1 1.0 = 0x2 in every nibble
+    hipLaunchKernelGGL(k_mfma_rate<kFmtE2M1>, dim3(unsigned(grid)), dim3(kStreamThreads), 0, st, 0x22222222u,
+                       0x38383838u, iters, sink);
+  return hipGetLastError();
+}
 
 int stream_read_grid() {
   int dev = 0, ncu = 256;

@@ -73,9 +73,12 @@ hipError_t launch_gemm1_big(const Shape& s, const uint8_t* xq, const float* xs, 
 hipError_t launch_gemm2_big(const Shape& s, const uint8_t* hq, const float* hs, const int32_t* offsets,
                             WeightPtrs w2, float* y, uint16_t* yb, int min_rows, hipStream_t st);
 
-// plain read stream over a device buffer (moe_stream.hip)
+// diagnostics (moe_diag.hip): plain read stream over a device buffer, and
+// the issued rate of the scaled MFMA (flops: host, the FLOP count enqueued)
 int stream_read_grid();
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
+int mfma_rate_grid();
+hipError_t launch_mfma_rate(int wfmt, int iters, float* sink, double* flops, hipStream_t st);
 
 hipError_t launch_tile_weights(int wfmt, int mats, int N, int K, const uint8_t* w, const uint8_t* s, uint8_t* w_tiled,
                                uint8_t* s_tiled, hipStream_t st);

@@ -199,6 +199,19 @@ int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_we
  * MOE_ERR_WORKSPACE (sink too small) are host checks. */
 int moe_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes, void* stream);
 
+/* Diagnostic: the issued rate of the scaled 16x16x128 MFMA the GEMMs use,
+ * for the operand formats of `wfmt` (MOE_WFMT_FP8_BLOCK: e4m3 x e4m3;
+ * MOE_WFMT_MXFP4: e2m1 weights x e4m3 activations).  Four workgroups of four
+ * waves per CU each run `iters` (1 .. 65536) rounds of three independent
+ * MFMAs on operands that are all 1.0 with unit scales; `sink` (device, at
+ * least 16 * CU-count bytes; 4 KiB covers an MI355X) receives one fp32 per
+ * workgroup, exactly 1536 * iters.  `*flops` (host, may be NULL) is set to the
+ * FLOP count enqueued (2 * 16 * 16 * 128 per MFMA), so FLOP/s = *flops / the
+ * call's duration on `stream`.  MOE_ERR_NULL_ARG (sink), MOE_ERR_MISALIGNED,
+ * MOE_ERR_UNSUPPORTED (other wfmt), MOE_ERR_BAD_SHAPE (iters) and
+ * MOE_ERR_WORKSPACE (sink too small) are host checks. */
+int moe_mfma_rate(int wfmt, int iters, void* sink, size_t sink_bytes, double* flops, void* stream);
+
 /* Static description of an error code (host only). */
 const char* moe_status_str(int status);
 

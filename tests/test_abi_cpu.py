@@ -175,3 +175,14 @@ def test_stream_read_argument_errors(lib):
     assert call(FAKE, 64, FAKE + 8, 1 << 15) == moe.MOE_ERR_MISALIGNED
     assert call(FAKE, 65, FAKE, 1 << 15) == moe.MOE_ERR_BAD_SHAPE
     assert call(FAKE, 64, FAKE, 4) == moe.MOE_ERR_WORKSPACE
+
+
+def test_mfma_rate_argument_errors(lib):
+    fl = C.c_double(0.0)
+    call = lambda wfmt, iters, sink, sn: moe.raw_call("moe_mfma_rate", wfmt, iters, sink, C.c_size_t(sn), C.byref(fl), None)
+    assert call(0, 16, None, 1 << 12) == moe.MOE_ERR_NULL_ARG
+    assert call(0, 16, FAKE + 4, 1 << 12) == moe.MOE_ERR_MISALIGNED
+    assert call(2, 16, FAKE, 1 << 12) == moe.MOE_ERR_UNSUPPORTED
+    assert call(0, 0, FAKE, 1 << 12) == moe.MOE_ERR_BAD_SHAPE
+    assert call(1, 65537, FAKE, 1 << 12) == moe.MOE_ERR_BAD_SHAPE
+    assert call(1, 16, FAKE, 16) == moe.MOE_ERR_WORKSPACE
