@@ -44,14 +44,14 @@ KERNEL_SRC = os.path.join(ROOT, "bit_grouped_gemm_amd", "csrc", "moe_kernels.hip
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_fp8")
     ap.add_argument("--tokens", default=None, help="comma-separated T values (default: the workload's sweep)")
     ap.add_argument("--roofline-T", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=4096 MXFP4 prefill section")
-    ap.add_argument("--prefill-reps", type=int, default=10)
+    ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle timing")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times): the known-size "

@@ -92,10 +92,10 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   };
   s.g1_split = fit(s.g1_split, H / 128, 2L * I);
   s.g2_split = fit(s.g2_split, I / 128, H);
-  // Big-tile kernels once experts hold enough rows that one 256-token pass
-  // beats the decode kernel's 16..64-token passes; they need 128-wide
-  // activation groups (one MFMA K step per scale), 128x128 e4m3 blocks or
-  // MXFP4, and H a multiple of 256.
+  // Big-tile kernels once experts hold enough rows that one pass of up to
+  // 160 (or 64) token rows per 256 weight rows beats the decode kernel's
+  // 16..64-row passes; they need 128-wide activation groups (one MFMA K step
+  // per scale), 128x128 e4m3 blocks or MXFP4, and H a multiple of 256.
   const double groups = std::fmin(double(E), double(T) * k);
   const double avg_rows = groups > 0 ? double(T) * k / groups : 0.0;
   // the big-tile kernels keep a pass's token scales in LDS: K <= 8192 for both GEMMs

@@ -477,7 +477,8 @@ __device__ __forceinline__ bool arrive_last(int32_t* counter, int S, int* s_flag
 }
 
 // ---------------------------------------------------------------------
-// GEMM1: unit = (group, 128 h-columns, K split).  Wave w owns h-columns
+// GEMM1: unit = (work item, 128 h-columns, K split), a work item being one
+// pass of 16 NTT rows of one group (nth_item).  Wave w owns h-columns
 // [32w, 32w+32) of the unit: weight tiles j = 0,1 are gate rows
 // n0+32w+16j+(0..15) and j = 2,3 the up rows I+n0+32w+16(j-2)+(0..15), so
 // the gate and up values of one h element land in the same lane.
@@ -631,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------
-// GEMM2: unit = (group, 64 NJ output rows, K split); wave w owns output rows
+// GEMM2: unit = (work item, 64 NJ output rows, K split); wave w owns output rows
 // n0 + 16 NJ w + 16 j + (0..15), j < NJ (NJ = 4 when H allows 256-row
 // units: twice the weight bytes in flight per wave).
 // ---------------------------------------------------------------------

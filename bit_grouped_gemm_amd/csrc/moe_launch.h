@@ -25,7 +25,8 @@ struct Shape {
   int g2_split;     // K splits over I/128 steps
   int g2_ntt;
   int g2_items;     // as g1_items, passes of 16 g2_ntt rows
-  // groups with many rows (prefill) run the 256 x 256-token LDS-staged kernels
+  // groups with many rows (prefill, larger decode batches) run the LDS-staged
+  // kernels: 256 weight rows x big_cap token rows per pass
   int big;          // 1: both GEMMs use the big-tile kernels
   int big_cap;      // their token rows per pass: 64 or 160
   // permute: slots per chunk and chunk count; one chunk = one block places
