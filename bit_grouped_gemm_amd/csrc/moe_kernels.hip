@@ -578,8 +578,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
     }
   }
   const int nks = H / 128, kps = nks / S, ks0 = split * kps, ks1 = ks0 + kps;
-  // this workgroup's one pass (work item) of the group's rows
-  for (int pass = pass0; pass < pass0 + 1; ++pass) {
+  {  // this workgroup's one pass (work item) of the group's rows
+    const int pass = pass0;
     const float* bsc[NTT];
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
@@ -613,7 +613,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm1(GemmParams p) {
   }
   if (S == 1) return;
   if (!arrive_last(p.cnt + item * nt + tile, S, &s_flag)) return;
-  for (int pass = pass0; pass < pass0 + 1; ++pass) {
+  {
+    const int pass = pass0;
     v4f acc[4][NTT];
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
@@ -677,8 +678,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
     }
   }
   const int nks = I / 128, kps = nks / S, ks0 = split * kps, ks1 = ks0 + kps;
-  // this workgroup's one pass (work item) of the group's rows
-  for (int pass = pass0; pass < pass0 + 1; ++pass) {
+  {  // this workgroup's one pass (work item) of the group's rows
+    const int pass = pass0;
     const float* bsc[NTT];
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
