@@ -15,6 +15,9 @@ namespace moe {
 #ifndef MOE_SPLIT_TARGET_WG
 #define MOE_SPLIT_TARGET_WG 256
 #endif
+#ifndef MOE_SPLIT_TARGET_WG2
+#define MOE_SPLIT_TARGET_WG2 MOE_SPLIT_TARGET_WG
+#endif
 // average rows per touched group from which the big-tile kernels take over
 // (measured cold-cache crossovers, H=4096 E=64 top-8: e4m3 between 12 and 16
 // rows, MXFP4 between 16 and 24)
@@ -31,7 +34,7 @@ namespace moe {
 #define MOE_SPLIT_MIN_KSTEPS 4
 #endif
 
-static int choose_split(long units, int nks) {
+static int choose_split(long units, int nks, long target = MOE_SPLIT_TARGET_WG) {
   // Split K (a divisor of the K-step count) only until the launch has about
   // one workgroup per CU: small decode layers then reach every CU, while
   // larger ones avoid the partial-sum round trip through memory, which costs
@@ -42,7 +45,7 @@ static int choose_split(long units, int nks) {
     if (nks % d) continue;
     if (nks / d < MOE_SPLIT_MIN_KSTEPS) break;
     best = d;
-    if (units * d >= MOE_SPLIT_TARGET_WG) break;
+    if (units * d >= target) break;
   }
   return best;
 }
@@ -80,7 +83,7 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   s.g1_items = items_bound(s.rows_cap, s.slots_max, 16 * s.g1_ntt);
   s.g2_items = items_bound(s.rows_cap, s.slots_max, 16 * s.g2_ntt);
   s.g1_split = choose_split(long(s.slots_max) * s.g1_tiles, H / 128);
-  s.g2_split = choose_split(long(s.slots_max) * s.g2_tiles, I / 128);
+  s.g2_split = choose_split(long(s.slots_max) * s.g2_tiles, I / 128, MOE_SPLIT_TARGET_WG2);
   // partial sums are addressed with 32-bit byte offsets: keep them under 2 GiB
   auto fit = [&](int S, int nks, long row_floats) {
     while (S > 1 && 4L * S * s.rows_cap * row_floats >= (1L << 31)) {
