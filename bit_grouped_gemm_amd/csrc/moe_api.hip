@@ -30,6 +30,11 @@ namespace moe {
 #ifndef MOE_G2_NJ
 #define MOE_G2_NJ 4
 #endif
+// token tiles per decode pass: sized for the mean row count of a touched
+// group plus this many standard deviations of a Poisson count
+#ifndef MOE_NTT_SIGMAS
+#define MOE_NTT_SIGMAS 3.0
+#endif
 #ifndef MOE_SPLIT_MIN_KSTEPS
 #define MOE_SPLIT_MIN_KSTEPS 4
 #endif
@@ -55,7 +60,7 @@ static int choose_ntt(int T, int k, int E) {
   const double groups = std::fmin(double(E), rows);
   if (groups <= 0) return 1;
   const double avg = rows / groups;
-  const double est = avg + 3.0 * std::sqrt(avg) + 1.0;
+  const double est = avg + MOE_NTT_SIGMAS * std::sqrt(avg) + 1.0;
   return est <= 16 ? 1 : (est <= 32 ? 2 : 4);
 }
 
