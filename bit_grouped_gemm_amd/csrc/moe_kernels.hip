@@ -536,11 +536,12 @@ __device__ __forceinline__ void swiglu_requant_store(const v4f (&acc)[4][NTT], c
   }
 }
 
-// Two token tiles with 128-blocks: registers capped at 168 so three
-// workgroups share a CU (the compiler fits it without spills), which runs a
-// 64-expert T = 64 layer's 768 units in one round instead of one and a half.
+// Occupancy with 128-blocks: two token tiles capped at 168 registers (three
+// workgroups per CU, which runs a 64-expert T = 64 layer's 768 units in one
+// round instead of one and a half), one token tile at 128 (four per CU); the
+// compiler fits both without spills.
 template <int WF, int NTT, int B32>
-__global__ __launch_bounds__(kThreads, (NTT == 2 && !B32) ? 3 : 1) void k_gemm1(GemmParams p) {
+__global__ __launch_bounds__(kThreads, B32 ? 1 : NTT == 2 ? 3 : NTT == 1 ? 4 : 1) void k_gemm1(GemmParams p) {
   __shared__ int s_wsum[4], s_res[2], s_flag;
   __shared__ float s_red[NTT][4][16];
   const int S = p.S, nt = p.ntiles;
