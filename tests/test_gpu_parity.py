@@ -60,6 +60,22 @@ REDUCED = {
     "mxfp4_split_shared": reduced("decode_mxfp4", H=2048, I=1024, E=8, topk=2, shared=True),
 }
 
+BIG = {
+    # many rows per expert select the 256-row x 160-token kernels; the shared group of
+    # T rows needs two 160-token passes when T > 160
+    "big_mxfp4_shared": reduced("decode_mxfp4", H=512, I=256, E=4, topk=2, shared=True),
+    "big_fp8": reduced("decode_fp8", H=512, I=384, E=6, topk=2),
+}
+
+# stage-test cases: the decode-kernel cases at a few dozen tokens, and the
+# many-row (prefill) kernels at enough tokens per expert to take that path
+STAGE = [(n, None) for n in REDUCED] + [(n, 200) for n in BIG]
+
+
+def stage_case(name):
+    return REDUCED[name] if name in REDUCED else BIG[name]
+
+
 _WCACHE = {}
 
 
@@ -234,11 +250,11 @@ def dec_e4m3_np(codes):
     return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 
-@pytest.mark.parametrize("name", list(REDUCED))
-def test_gemm1_stage(name):
+@pytest.mark.parametrize("name,T", STAGE)
+def test_gemm1_stage(name, T):
     moe = M()
-    wl = REDUCED[name]
-    T = 37 if name != "tiny_fp8" else 16
+    wl = stage_case(name)
+    T = T or (37 if name != "tiny_fp8" else 16)
     _note(f"gemm1 {name} T={T}")
     w, wc = weights_for(wl)
     x, ids, tw = inputs_for(wl, T, seed=2)
@@ -277,11 +293,11 @@ def test_gemm1_stage(name):
     _note(f"  max |gpu deq h - oracle h| / group scale = {(np.abs(dg - h_ref) / (448 * scale)).max():.3e}")
 
 
-@pytest.mark.parametrize("name", list(REDUCED))
-def test_gemm2_stage(name):
+@pytest.mark.parametrize("name,T", STAGE)
+def test_gemm2_stage(name, T):
     moe = M()
-    wl = REDUCED[name]
-    T = 29
+    wl = stage_case(name)
+    T = T or 29
     _note(f"gemm2 {name} T={T}")
     w, wc = weights_for(wl)
     x, ids, tw = inputs_for(wl, T, seed=3)
@@ -365,12 +381,6 @@ def test_layer_full_size_sampled(name, T):
 
 
 # ------------------------------------------------------------------ big-tile (prefill) path
-BIG = {
-    # many rows per expert select the 256-row x 160-token kernels; the shared group of
-    # T rows needs two 160-token passes when T > 160
-    "big_mxfp4_shared": reduced("decode_mxfp4", H=512, I=256, E=4, topk=2, shared=True),
-    "big_fp8": reduced("decode_fp8", H=512, I=384, E=6, topk=2),
-}
 
 
 @pytest.mark.parametrize("name", list(BIG))
