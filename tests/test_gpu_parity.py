@@ -479,6 +479,27 @@ def test_layer_one_hot_expert_many_passes(name):
     tol_check(out.float().cpu().numpy(), ref, f"one-hot {name}")
 
 
+def test_one_hot_expert_poisoned_workspace():
+    """The per-item split-K counters of a heavy group are cleared inside every
+    call: a workspace filled with 0xFF gives the same bits as a zeroed one."""
+    moe = M()
+    wl = HEAVY["fp8_b32_split"]
+    T = 150
+    w, _ = weights_for(wl)
+    x, _, tw = inputs_for(wl, T, seed=13)
+    g = torch.Generator().manual_seed(13)
+    others = torch.stack([torch.randperm(wl.E - 1, generator=g)[: wl.topk - 1] + 1 for _ in range(T)])
+    ids = torch.cat([torch.zeros(T, 1, dtype=torch.int64), others], 1).to(torch.int32).to(DEV)
+    cfg = moe.Cfg.for_workload(wl, T)
+    ws = moe.workspace(cfg)
+    ws.fill_(0xFF)
+    a = moe.moe_layer(cfg, x, ids, tw, w, ws=ws).clone()
+    ws.fill_(0x00)
+    b = moe.moe_layer(cfg, x, ids, tw, w, ws=ws).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_poisoned_workspace_and_determinism():
     moe = M()
     for name, T in (("fp8_zipf_shared", 37), ("mxfp4", 1), ("fp8_b128", 2)):
