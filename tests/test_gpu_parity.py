@@ -479,6 +479,24 @@ def test_layer_one_hot_expert_many_passes(name):
     tol_check(out.float().cpu().numpy(), ref, f"one-hot {name}")
 
 
+@pytest.mark.parametrize("name,T", [("big_fp8", 200), ("big_fp8", 700), ("big_mxfp4_shared", 200)])
+def test_big_tiles_bitwise_deterministic(name, T):
+    """The many-row kernels share LDS tables and ring stages between waves:
+    repeated calls (one from a poisoned workspace) must agree bit for bit, which
+    the tolerance checks cannot show."""
+    moe = M()
+    wl = BIG[name]
+    w, _ = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=14)
+    cfg = moe.Cfg.for_workload(wl, T)
+    ws = moe.workspace(cfg)
+    ws.fill_(0xFF)
+    outs = [moe.moe_layer(cfg, x, ids, tw, w, ws=ws).clone() for _ in range(4)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(outs[0].view(torch.int16), o.view(torch.int16))
+
+
 def test_one_hot_expert_poisoned_workspace():
     """The per-item split-K counters of a heavy group are cleared inside every
     call: a workspace filled with 0xFF gives the same bits as a zeroed one."""
