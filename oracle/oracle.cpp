@@ -166,9 +166,25 @@ struct WSet {
   const void* sw2s;
 };
 
+// Decoded value of every code, filled once from the decoders above (the
+// weight dequantisation below looks codes up instead of re-deriving them).
+struct DecodeTables {
+  double e4m3[256], e2m1[16], e8m0[256];
+  DecodeTables() {
+    for (int c = 0; c < 256; ++c) e4m3[c] = dec_e4m3(uint8_t(c));
+    for (int c = 0; c < 16; ++c) e2m1[c] = dec_e2m1(uint8_t(c));
+    for (int c = 0; c < 256; ++c) e8m0[c] = dec_e8m0(uint8_t(c));
+  }
+};
+const DecodeTables& tables() {
+  static const DecodeTables t;
+  return t;
+}
+
 // Dequantised weight value of matrix `which` (1: gate|up [2I,H], 2: down [H,I])
 // of expert e (e == E: the shared expert), row n, column kk.
 double wval(const Cfg& c, const WSet& w, int which, int e, int64_t n, int64_t kk) {
+  const DecodeTables& tab = tables();
   const bool sh = e == c.E;
   const int64_t N = which == 1 ? 2LL * c.I : c.H;
   const int64_t K = which == 1 ? c.H : c.I;
@@ -177,7 +193,7 @@ double wval(const Cfg& c, const WSet& w, int which, int e, int64_t n, int64_t kk
   const int64_t ee = sh ? 0 : e;
   if (c.wfmt == 0) {  // FP8 e4m3 + fp32 scale per wblk x wblk block
     const int64_t b = c.wblk;
-    const double code = dec_e4m3(codes[(ee * N + n) * K + kk]);
+    const double code = tab.e4m3[codes[(ee * N + n) * K + kk]];
     const float* s = static_cast<const float*>(sc);
     int64_t kb = kk / b;
     if (g_mutation == 2 && kb == 0) return code;  // planted: drop the first K-block scale
@@ -187,7 +203,7 @@ double wval(const Cfg& c, const WSet& w, int which, int e, int64_t n, int64_t kk
   const uint8_t byte = codes[(ee * N + n) * (K / 2) + kk / 2];
   const uint8_t nib = (kk & 1) ? (byte >> 4) : (byte & 15);
   const uint8_t* s = static_cast<const uint8_t*>(sc);
-  return dec_e2m1(nib) * dec_e8m0(s[(ee * N + n) * (K / 32) + kk / 32]);
+  return tab.e2m1[nib] * tab.e8m0[s[(ee * N + n) * (K / 32) + kk / 32]];
 }
 
 int expert_of_row(const int32_t* offsets, int ngroups, int64_t r) {
@@ -196,34 +212,42 @@ int expert_of_row(const int32_t* offsets, int ngroups, int64_t r) {
   return -1;
 }
 
-// GEMM1 + SwiGLU for one row: a = dequantised activation row (fp64, length H)
-// -> h (fp32, length I).  gate = rows [0, I), up = rows [I, 2I).
-void gemm1_swiglu_row(const Cfg& c, const WSet& w, int e, const double* a, float* h) {
-  std::vector<double> g(2 * size_t(c.I));
-  for (int64_t n = 0; n < 2LL * c.I; ++n) {
-    double acc = 0.0;
-    for (int64_t kk = 0; kk < c.H; ++kk) acc += a[kk] * wval(c, w, 1, e, n, kk);
-    g[n] = acc;
-  }
-  for (int64_t n = 0; n < c.I; ++n) {
-    double gate = g[n], up = g[c.I + n];
-    if (g_mutation == 1) std::swap(gate, up);  // planted: gate and up swapped
-    const double silu = gate / (1.0 + std::exp(-gate));
-    h[n] = float(silu * up);
-  }
+// Weight rows [n0, n0 + nn) of matrix `which` (1: gate|up [2I,H], 2: down
+// [H,I]) of group e, dequantised to fp64: each entry is wval(), the decoded
+// code times its scale, which is exact in fp64.
+void dequant_weight_rows(const Cfg& c, const WSet& w, int which, int e, int64_t n0, int64_t nn, double* out) {
+  const int64_t K = which == 1 ? c.H : c.I;
+  for (int64_t n = 0; n < nn; ++n)
+    for (int64_t kk = 0; kk < K; ++kk) out[n * K + kk] = wval(c, w, which, e, n0 + n, kk);
 }
 
-// GEMM2 for one row: dequantised requantised h (fp64, length I) -> y (length H)
-void gemm2_row(const Cfg& c, const WSet& w, int e, const double* hd, double* y) {
-  for (int64_t n = 0; n < c.H; ++n) {
-    double acc = 0.0;
-    for (int64_t kk = 0; kk < c.I; ++kk) acc += hd[kk] * wval(c, w, 2, e, n, kk);
-    y[n] = acc;
-  }
+// One dot product in fp64, summed in index order.
+double dot(const double* a, const double* b, int64_t n) {
+  double acc = 0.0;
+  for (int64_t i = 0; i < n; ++i) acc += a[i] * b[i];
+  return acc;
+}
+
+// SwiGLU of one output column: silu(gate) * up in fp64, rounded to fp32
+// (left half through SiLU times the right half).
+float swiglu(double gate, double up) {
+  if (g_mutation == 1) std::swap(gate, up);  // planted: gate and up swapped
+  const double silu = gate / (1.0 + std::exp(-gate));
+  return float(silu * up);
 }
 
 void dequant_row(const uint8_t* q, const float* s, int64_t len, int G, double* out) {
   for (int64_t i = 0; i < len; ++i) out[i] = dec_e4m3(q[i]) * double(s[i / G]);
+}
+
+// The listed rows (indices into `rows`) that belong to each group.
+std::vector<std::vector<int64_t>> rows_by_group(const int32_t* offsets, int ng, int64_t nrows, const int64_t* rows) {
+  std::vector<std::vector<int64_t>> m(ng);
+  for (int64_t i = 0; i < nrows; ++i) {
+    const int g = expert_of_row(offsets, ng, rows[i]);
+    if (g >= 0) m[g].push_back(i);
+  }
+  return m;
 }
 
 }  // namespace
@@ -302,34 +326,64 @@ void oracle_permute(const int32_t* ids, int T, int k, int E, int has_shared, int
 // Inputs: xq [T,H], xs [T,H/G], row_token, offsets (group list).
 // Outputs per listed row i: h [nrows, I] (fp32, before requant),
 // hq [nrows, I] e4m3, hs [nrows, I/G].
+// For row i of group e and h column n: G_gate = sum over kk of a[kk] *
+// W1[e][n][kk], G_up the same over row I + n, each one fp64 dot product in
+// K order; h = swiglu(G_gate, G_up); then each G consecutive h values of
+// the row are requantised together.  The work is split into independent
+// tasks of (group, G consecutive h columns): a task dequantises the gate
+// and up weight rows of its columns once and runs them against every
+// listed row of its group (no sum is split or reordered by this).
 void oracle_gemm1(const Cfg* c, const WSet* w, const uint8_t* xq, const float* xs,
                   const int32_t* row_token, const int32_t* offsets, int64_t nrows,
                   const int64_t* rows, float* h, uint8_t* hq, float* hs) {
   const int ng = c->E + (c->has_shared ? 1 : 0);
+  const int64_t H = c->H, I = c->I, G = c->G;
+  std::vector<double> a(std::max<int64_t>(nrows, 1) * H);  // dequantised activation of each listed row
   parallel_for(nrows, [&](int64_t i) {
-    const int64_t r = rows[i];
-    const int e = expert_of_row(offsets, ng, r);
-    const int t = row_token[r];
-    std::vector<double> a(c->H);
-    dequant_row(xq + int64_t(t) * c->H, xs + int64_t(t) * (c->H / c->G), c->H, c->G, a.data());
-    float* hr = h + i * c->I;
-    gemm1_swiglu_row(*c, *w, e, a.data(), hr);
-    for (int64_t g = 0; g < c->I / c->G; ++g)
-      quant_group(hr + g * c->G, c->G, hq + i * c->I + g * c->G, hs + i * (c->I / c->G) + g);
+    const int t = row_token[rows[i]];
+    dequant_row(xq + int64_t(t) * H, xs + int64_t(t) * (H / G), H, c->G, &a[i * H]);
+  });
+  const auto members = rows_by_group(offsets, ng, nrows, rows);
+  const int64_t nch = I / G;
+  parallel_for(int64_t(ng) * nch, [&](int64_t task) {
+    const int e = int(task / nch);
+    const int64_t n0 = (task % nch) * G;
+    if (members[e].empty()) return;
+    std::vector<double> wg(G * H), wu(G * H);
+    dequant_weight_rows(*c, *w, 1, e, n0, G, wg.data());
+    dequant_weight_rows(*c, *w, 1, e, I + n0, G, wu.data());
+    for (const int64_t i : members[e]) {
+      float* hr = h + i * I + n0;
+      for (int64_t n = 0; n < G; ++n) hr[n] = swiglu(dot(&a[i * H], &wg[n * H], H), dot(&a[i * H], &wu[n * H], H));
+      quant_group(hr, c->G, hq + i * I + n0, hs + i * (I / G) + n0 / G);
+    }
   });
 }
 
 // Grouped GEMM2 for the listed rows: hq [R, I], hs [R, I/G] (indexed by row id)
-// -> y [nrows, H] in fp64.
+// -> y [nrows, H] in fp64: y[i][n] = sum over kk of hd[kk] * W2[e][n][kk],
+// one fp64 dot product in K order, hd the row's dequantised codes.  Tasks of
+// (group, 128 output columns) dequantise their weight rows once.
 void oracle_gemm2(const Cfg* c, const WSet* w, const uint8_t* hq, const float* hs,
                   const int32_t* offsets, int64_t nrows, const int64_t* rows, double* y) {
   const int ng = c->E + (c->has_shared ? 1 : 0);
+  const int64_t H = c->H, I = c->I, G = c->G;
+  std::vector<double> hd(std::max<int64_t>(nrows, 1) * I);
   parallel_for(nrows, [&](int64_t i) {
     const int64_t r = rows[i];
-    const int e = expert_of_row(offsets, ng, r);
-    std::vector<double> hd(c->I);
-    dequant_row(hq + r * c->I, hs + r * (c->I / c->G), c->I, c->G, hd.data());
-    gemm2_row(*c, *w, e, hd.data(), y + i * c->H);
+    dequant_row(hq + r * I, hs + r * (I / G), I, c->G, &hd[i * I]);
+  });
+  const auto members = rows_by_group(offsets, ng, nrows, rows);
+  constexpr int64_t kCols = 128;  // H is a multiple of 128
+  const int64_t nch = H / kCols;
+  parallel_for(int64_t(ng) * nch, [&](int64_t task) {
+    const int e = int(task / nch);
+    const int64_t n0 = (task % nch) * kCols;
+    if (members[e].empty()) return;
+    std::vector<double> wd(kCols * I);
+    dequant_weight_rows(*c, *w, 2, e, n0, kCols, wd.data());
+    for (const int64_t i : members[e])
+      for (int64_t n = 0; n < kCols; ++n) y[i * H + n0 + n] = dot(&hd[i * I], &wd[n * I], I);
   });
 }
 
