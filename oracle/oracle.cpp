@@ -258,7 +258,9 @@ void oracle_set_threads(int n) { g_threads = n; }
 int oracle_get_threads() { return default_threads(); }
 // Test-only: plant a known mistake (0 = none, 1 = gate/up swapped,
 // 2 = first K-block weight scale dropped, 3 = unstable row order inside an
-// expert, 4 = offsets shifted by one) so tests can show their pins catch it.
+// expert, 4 = offsets shifted by one, 5 = the stage combine ignores routing
+// weights, 6 = the stage combine reads token 0's shared row for every token)
+// so tests can show their pins catch it.
 void oracle_set_mutation(int m) { g_mutation = m; }
 
 double oracle_dec_e4m3(int c) { return dec_e4m3(uint8_t(c)); }
@@ -399,11 +401,13 @@ void oracle_combine(const Cfg* c, const float* y, const int32_t* expand_idx,
     for (int j = 0; j < c->k; ++j) {
       const int32_t r = expand_idx[t * c->k + j];
       if (r < 0) continue;
-      const double wt = topk_w[t * c->k + j];
+      double wt = topk_w[t * c->k + j];
+      if (g_mutation == 5) wt = 1.0;  // planted: routing weight ignored
       for (int64_t n = 0; n < c->H; ++n) o[n] += wt * double(y[int64_t(r) * c->H + n]);
     }
     if (c->has_shared) {
-      const int64_t r = offsets[c->E] + t;
+      int64_t r = offsets[c->E] + t;
+      if (g_mutation == 6) r = offsets[c->E];  // planted: every token takes token 0's shared row
       for (int64_t n = 0; n < c->H; ++n) o[n] += double(y[r * c->H + n]);
     }
   });

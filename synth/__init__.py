@@ -134,12 +134,15 @@ def gen_routing(T: int, E: int, k: int, routing: str, seed: int, wid: int,
     return ids.to(torch.int32).to(device), w.to(device)
 
 
+_FP8_MAX = 448.0   # largest e4m3 magnitude: a block's maximum maps onto it
+
+
 def _quant_fp8_blocks(w: torch.Tensor, b: int) -> Tuple[torch.Tensor, torch.Tensor]:
     """fp32 [N,K] -> (e4m3 codes uint8 [N,K], fp32 scales [N/b, K/b])."""
     N, K = w.shape
     blk = w.reshape(N // b, b, K // b, b)
     amax = blk.abs().amax(dim=(1, 3)).clamp_min(2.0 ** -64)
-    mult = torch.full_like(amax, 448.0) / amax
+    mult = torch.full_like(amax, _FP8_MAX) / amax
     q = (blk * mult[:, None, :, None]).to(torch.float8_e4m3fn)
     return q.reshape(N, K).view(torch.uint8), (1.0 / mult)
 

@@ -352,6 +352,96 @@ def test_masked_slots_are_ignored():
     assert np.array_equal(lay.layer(x, ids_m, tw), lay.layer(x, ids, tw_z))
 
 
+# ------------------------------------------------------------ stage combine
+def _dense_routing_product(y, ids, tw, E, has_shared):
+    """The combine as one matrix product: P [T, rows] holds each valid slot's
+    routing weight in the column of the row its expert gave it (expert e's
+    rows are offsets[e] .. offsets[e+1] - 1, taken by its slots in flat-index
+    order; the shared group follows), so out = P @ y (numpy's matmul)."""
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    counts = np.bincount(flat[valid], minlength=E)
+    start = np.concatenate([[0], np.cumsum(counts)])
+    P = np.zeros((T, y.shape[0]))
+    seen = np.zeros(E, np.int64)
+    for i in range(T * k):                    # slots in flat-index order
+        e = flat[i]
+        if 0 <= e < E:
+            P[i // k, start[e] + seen[e]] += tw.reshape(-1)[i]
+            seen[e] += 1
+    if has_shared:
+        for t in range(T):
+            P[t, start[E] + t] += 1.0
+    return P @ y.astype(np.float64)
+
+
+COMBINE_CASES = [(37, 4, 9, False), (29, 8, 32, True), (1, 8, 64, True), (16, 2, 8, False)]
+
+
+def _combine_case(T, k, E, has_shared, seed):
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    if T > 3:
+        ids[1, 0] = -1                         # masked slots: negative and past E
+        ids[2, k - 1] = E + 2
+        ids[3, :] = -1                         # a token with every slot masked
+    tw = rng.random((T, k)).astype(np.float32) + 0.05
+    counts, offsets, eidx, rtok = oracle.permute(ids, E, has_shared)
+    y = rng.standard_normal((max(len(rtok), 1), 128)).astype(np.float32)
+    wl = synth.Workload("combine", H=128, E=E, topk=k, I=128, wfmt=0, wblk=128, act_group=128,
+                        routing="uniform", shared=has_shared, tokens=(T,), wid=0)
+    lay = oracle.Layer.for_workload(wl, T, synth.Weights(*(torch.zeros(1, dtype=torch.uint8),) * 4))
+    return lay, y, ids, tw, eidx, offsets
+
+
+def _combine_agrees(T, k, E, has_shared, seed=0) -> bool:
+    lay, y, ids, tw, eidx, offsets = _combine_case(T, k, E, has_shared, seed)
+    got = lay.combine(y, eidx, offsets, tw)
+    ref = _dense_routing_product(y, ids, tw, E, has_shared)
+    return bool(np.all(np.abs(got - ref) <= 1e-12 * np.abs(ref).max()))
+
+
+@pytest.mark.parametrize("T,k,E,has_shared", COMBINE_CASES)
+def test_stage_combine_equals_routing_matrix_product(T, k, E, has_shared):
+    """oracle_combine (the stage reference) against a dense routing matrix
+    times y: masked slots add nothing, each slot's weight multiplies its own
+    row, and every token adds its own shared row."""
+    assert _combine_agrees(T, k, E, has_shared)
+    lay, y, ids, tw, eidx, offsets = _combine_case(T, k, E, has_shared, 0)
+    got = lay.combine(y, eidx, offsets, tw)
+    if T > 3 and not has_shared:
+        assert np.all(got[3] == 0)             # every slot masked, no shared expert
+
+
+def test_stage_combine_of_layer_rows_equals_layer():
+    """The stage combine over the layer's own GEMM2 rows (rounded to fp32)
+    reproduces the layer's fp64 combine to fp32 rounding."""
+    wl = SMALL["fp8_shared_zipf"]
+    T = 7
+    w = synth.gen_weights(wl, seed=15)
+    x, ids, tw = synth.gen_inputs(wl, T, seed=15)
+    lay = oracle.layer_for(wl, T, w)
+    xq, xs = oracle.quant_act(x, wl.act_group)
+    counts, offsets, eidx, rtok = oracle.permute(ids, wl.E, True)
+    R = int(offsets[-1])
+    _, hq, hs = lay.gemm1(xq, xs, rtok, offsets, range(R))
+    y = lay.gemm2(hq, hs, offsets, range(R)).astype(np.float32)
+    got = lay.combine(y, eidx, offsets, tw)
+    ref = lay.layer(x, ids, tw)
+    assert np.abs(got - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("mutation", [5, 6])
+def test_planted_combine_mistakes_are_caught(mutation):
+    assert all(_combine_agrees(*c) for c in COMBINE_CASES)
+    oracle.set_mutation(mutation)
+    try:
+        assert not all(_combine_agrees(*c) for c in COMBINE_CASES), f"mutation {mutation} slipped through"
+    finally:
+        oracle.set_mutation(0)
+
+
 # ------------------------------------------------------------ worked examples
 def _golden_case(ex):
     c = ex["cfg"]
