@@ -13,6 +13,7 @@ Entry points (same names as the C ABI):
     moe_combine(cfg, y, expand_idx, offsets, topk_weights) -> out
     moe_layer(cfg, x, topk_ids, topk_weights, weights, ws=None, out=None) -> out
     moe_prepack_weights(cfg, weights) -> TiledWeights
+    moe_encode_e4m3(v) -> codes   (diagnostic: the quantisers' fp32 -> e4m3 conversion)
 
 The GEMM entry points read expert weights in the tiled layout: convert the
 canonical row-major tensors once with moe_prepack_weights(cfg, weights)
@@ -43,7 +44,7 @@ WFMT_MXFP4 = 1
 
 EXPORTS = ("moe_workspace_size", "moe_permute", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm2",
            "moe_combine", "moe_layer", "moe_prepack_weights", "moe_stream_read", "moe_mfma_rate",
-           "moe_status_str")
+           "moe_encode_e4m3", "moe_status_str")
 
 
 class MoeCfg(C.Structure):
@@ -52,7 +53,8 @@ class MoeCfg(C.Structure):
 
 
 class MoeWeights(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in ("w1", "w1s", "w2", "w2s", "sw1", "sw1s", "sw2", "sw2s")]
+    _fields_ = [(n, C.c_void_p) for n in ("w1", "w1s", "w2", "w2s", "sw1", "sw1s", "sw2", "sw2s")] + \
+        [("prepacked", C.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -85,6 +87,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     L.moe_prepack_weights.argtypes = [cfgp, wp, wp, vp]
     L.moe_stream_read.argtypes = [vp, sz, vp, sz, vp]
     L.moe_mfma_rate.argtypes = [C.c_int, C.c_int, vp, sz, C.POINTER(C.c_double), vp]
+    L.moe_encode_e4m3.argtypes = [vp, sz, vp, vp]
     L.moe_status_str.argtypes = [C.c_int]
     L.moe_status_str.restype = C.c_char_p
     for n in EXPORTS:
@@ -143,9 +146,11 @@ def _check(fn: str, rc: int) -> None:
 
 
 def weights_struct(w) -> MoeWeights:
-    """moe_weights from an object with w1, w1s, w2, w2s[, sw1, sw1s, sw2, sw2s] tensors."""
+    """moe_weights from an object with w1, w1s, w2, w2s[, sw1, sw1s, sw2, sw2s] tensors
+    and an optional `prepacked` flag (absent: 0, the canonical row-major layout)."""
     g = lambda n: _ptr(getattr(w, n, None))
-    return MoeWeights(g("w1"), g("w1s"), g("w2"), g("w2s"), g("sw1"), g("sw1s"), g("sw2"), g("sw2s"))
+    return MoeWeights(g("w1"), g("w1s"), g("w2"), g("w2s"), g("sw1"), g("sw1s"), g("sw2"), g("sw2s"),
+                      int(getattr(w, "prepacked", 0)))
 
 
 def _u16(x: torch.Tensor) -> torch.Tensor:
@@ -227,7 +232,7 @@ def moe_layer(cfg: Cfg, x, topk_ids, topk_weights, weights, ws: Optional[torch.T
 
 @dataclasses.dataclass
 class TiledWeights:
-    """Expert weights in the layout the GEMM entry points read."""
+    """Expert weights in the layout the GEMM entry points read (prepacked = 1)."""
     w1: torch.Tensor
     w1s: torch.Tensor
     w2: torch.Tensor
@@ -236,6 +241,7 @@ class TiledWeights:
     sw1s: Optional[torch.Tensor] = None
     sw2: Optional[torch.Tensor] = None
     sw2s: Optional[torch.Tensor] = None
+    prepacked: int = 1
 
 
 def moe_prepack_weights(cfg: Cfg, weights) -> TiledWeights:
@@ -244,7 +250,9 @@ def moe_prepack_weights(cfg: Cfg, weights) -> TiledWeights:
     names = ["w1", "w1s", "w2", "w2s"] + (["sw1", "sw1s", "sw2", "sw2s"] if cfg.has_shared else [])
     out = TiledWeights(**{n: torch.empty_like(getattr(weights, n)) for n in names})
     c, src, dst = cfg.c(), weights_struct(weights), weights_struct(out)
+    dst.prepacked = 0
     _check("moe_prepack_weights", load().moe_prepack_weights(C.byref(c), C.byref(src), C.byref(dst), _stream()))
+    out.prepacked = int(dst.prepacked)
     return out
 
 
@@ -269,6 +277,14 @@ def moe_mfma_rate(wfmt: int, iters: int, sink: torch.Tensor) -> float:
     _check("moe_mfma_rate", load().moe_mfma_rate(int(wfmt), int(iters), _ptr(sink),
                                                   sink.numel() * sink.element_size(), C.byref(flops), _stream()))
     return flops.value
+
+
+def moe_encode_e4m3(v: torch.Tensor, codes: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """e4m3 codes (uint8, same shape) of fp32 values by the quantisers' conversion."""
+    if codes is None:
+        codes = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check("moe_encode_e4m3", load().moe_encode_e4m3(_ptr(v), v.numel(), _ptr(codes), _stream()))
+    return codes
 
 
 def raw_call(name: str, *args) -> int:

@@ -169,8 +169,8 @@ namespace {
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
-int check_cfg(const moe_cfg* c) {
-  if (!c) return MOE_ERR_NULL_ARG;
+// Shape and format checks of a (non-null) cfg.
+int check_shape(const moe_cfg* c) {
   if (c->T < 0 || c->H < 1 || c->I < 1 || c->E < 1 || c->topk < 1 || c->topk > c->E) return MOE_ERR_BAD_SHAPE;
   if (c->topk > 32 || c->E > 1024) return MOE_ERR_BAD_SHAPE;
   if (c->H % 128 || c->I % 128) return MOE_ERR_BAD_SHAPE;
@@ -195,22 +195,42 @@ Shape shape_of(const moe_cfg* c) {
   return make_shape(c->T, c->H, c->I, c->E, c->topk, c->wfmt, c->wblk, c->act_group, c->has_shared);
 }
 
-// Weight pointers: all four routed tensors, plus the shared four when used.
-int check_weights(const moe_cfg* c, const moe_weights* w) {
+// Argument checks of the layer entry points, in the order include/moe.h
+// documents: NULL pointers first (the cfg, every required buffer -- NULL is
+// accepted only for buffers of zero bytes, i.e. T == 0 -- and the weight
+// tensors), then the shape, then alignment, then the weights' layout flag.
+using PtrList = std::initializer_list<std::pair<const void*, bool>>;  // (pointer, required)
+
+// The weight tensors a call reads: all four routed ones, plus the shared
+// four when the cfg has a shared expert.
+int weights_null(const moe_cfg* c, const moe_weights* w) {
   if (!w || !w->w1 || !w->w1s || !w->w2 || !w->w2s) return MOE_ERR_NULL_ARG;
-  if (c->has_shared && (!w->sw1 || !w->sw1s || !w->sw2 || !w->sw2s)) return MOE_ERR_NULL_ARG;
-  const void* ps[8] = {w->w1, w->w1s, w->w2, w->w2s, w->sw1, w->sw1s, w->sw2, w->sw2s};
-  for (int i = 0; i < (c->has_shared ? 8 : 4); ++i)
-    if (misaligned(ps[i])) return MOE_ERR_MISALIGNED;
+  if (c->has_shared == 1 && (!w->sw1 || !w->sw1s || !w->sw2 || !w->sw2s)) return MOE_ERR_NULL_ARG;
   return MOE_OK;
 }
 
-// Required pointers: NULL is accepted only for buffers of zero bytes (T == 0).
-int check_ptrs(std::initializer_list<std::pair<const void*, bool>> ps) {
+// Alignment of the weight tensors and their layout flag: `tiled` = 1 the
+// layout the GEMMs read (prepacked), 0 canonical, -1 either.
+int weights_layout(const moe_cfg* c, const moe_weights* w, int tiled) {
+  const void* ps[8] = {w->w1, w->w1s, w->w2, w->w2s, w->sw1, w->sw1s, w->sw2, w->sw2s};
+  for (int i = 0; i < (c->has_shared ? 8 : 4); ++i)
+    if (misaligned(ps[i])) return MOE_ERR_MISALIGNED;
+  if (w->prepacked != 0 && w->prepacked != 1) return MOE_ERR_UNSUPPORTED;
+  if (tiled >= 0 && w->prepacked != tiled) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// w == nullptr with needs_w false: the call takes no weights.
+int check_args(const moe_cfg* c, PtrList ps, const moe_weights* w = nullptr, bool needs_w = false) {
+  if (!c) return MOE_ERR_NULL_ARG;
   for (auto& pr : ps)
     if (pr.second && !pr.first) return MOE_ERR_NULL_ARG;
+  int rc;
+  if (needs_w && (rc = weights_null(c, w))) return rc;
+  if ((rc = check_shape(c))) return rc;
   for (auto& pr : ps)
     if (pr.first && misaligned(pr.first)) return MOE_ERR_MISALIGNED;
+  if (needs_w && (rc = weights_layout(c, w, 1))) return rc;
   return MOE_OK;
 }
 
@@ -221,8 +241,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 extern "C" {
 
 int moe_workspace_size(const moe_cfg* cfg, size_t* bytes) {
-  if (!bytes) return MOE_ERR_NULL_ARG;
-  const int rc = check_cfg(cfg);
+  if (!cfg || !bytes) return MOE_ERR_NULL_ARG;
+  const int rc = check_shape(cfg);
   if (rc) return rc;
   *bytes = make_ws_layout(shape_of(cfg)).total;
   return MOE_OK;
@@ -231,14 +251,14 @@ int moe_workspace_size(const moe_cfg* cfg, size_t* bytes) {
 int moe_permute(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, int32_t* counts,
                 int32_t* offsets, int32_t* expand_idx, int32_t* row_token, uint8_t* xq, float* xs, void* ws,
                 size_t ws_bytes, void* stream) {
-  int rc = check_cfg(cfg);
+  const bool has_rows = cfg && cfg->T > 0;
+  // more than 4096 slots are placed in chunks whose counts live in the workspace
+  const bool chunked = cfg && int64_t(cfg->T) * cfg->topk > 4096;
+  int rc = check_args(cfg, {{x, has_rows}, {topk_ids, has_rows}, {counts, true}, {offsets, true},
+                            {expand_idx, has_rows}, {row_token, has_rows}, {xq, has_rows}, {xs, has_rows},
+                            {ws, chunked}});
   if (rc) return rc;
-  const bool has_rows = cfg->T > 0;
   const Shape s = shape_of(cfg);
-  const bool chunked = s.perm_chunks > 1;  // needs the workspace for per-chunk counts
-  rc = check_ptrs({{x, has_rows}, {topk_ids, has_rows}, {counts, true}, {offsets, true},
-                   {expand_idx, has_rows}, {row_token, has_rows}, {xq, has_rows}, {xs, has_rows}, {ws, chunked}});
-  if (rc) return rc;
   const WsLayout L = make_ws_layout(s);
   if (chunked && ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   int32_t* chunk_cnt = chunked ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.chunk_cnt) : nullptr;
@@ -249,13 +269,10 @@ int moe_permute(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, 
 int moe_grouped_gemm1_swiglu(const moe_cfg* cfg, const uint8_t* xq, const float* xs, const int32_t* row_token,
                              const int32_t* offsets, const moe_weights* w, uint8_t* hq, float* hs, void* ws,
                              size_t ws_bytes, void* stream) {
-  int rc = check_cfg(cfg);
+  const bool has_rows = cfg && cfg->T > 0;
+  int rc = check_args(cfg, {{xq, has_rows}, {xs, has_rows}, {row_token, has_rows}, {offsets, true},
+                            {hq, has_rows}, {hs, has_rows}, {ws, true}}, w, true);
   if (rc) return rc;
-  const bool has_rows = cfg->T > 0;
-  rc = check_ptrs({{xq, has_rows}, {xs, has_rows}, {row_token, has_rows}, {offsets, true}, {hq, has_rows},
-                   {hs, has_rows}, {ws, true}});
-  if (rc) return rc;
-  if ((rc = check_weights(cfg, w))) return rc;
   const Shape s = shape_of(cfg);
   const WsLayout L = make_ws_layout(s);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -279,12 +296,9 @@ int moe_grouped_gemm1_swiglu(const moe_cfg* cfg, const uint8_t* xq, const float*
 
 int moe_grouped_gemm2(const moe_cfg* cfg, const uint8_t* hq, const float* hs, const int32_t* offsets,
                       const moe_weights* w, float* y, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_cfg(cfg);
+  const bool has_rows = cfg && cfg->T > 0;
+  int rc = check_args(cfg, {{hq, has_rows}, {hs, has_rows}, {offsets, true}, {y, has_rows}, {ws, true}}, w, true);
   if (rc) return rc;
-  const bool has_rows = cfg->T > 0;
-  rc = check_ptrs({{hq, has_rows}, {hs, has_rows}, {offsets, true}, {y, has_rows}, {ws, true}});
-  if (rc) return rc;
-  if ((rc = check_weights(cfg, w))) return rc;
   const Shape s = shape_of(cfg);
   const WsLayout L = make_ws_layout(s);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -308,11 +322,9 @@ int moe_grouped_gemm2(const moe_cfg* cfg, const uint8_t* hq, const float* hs, co
 
 int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* expand_idx, const int32_t* offsets,
                 const float* topk_weights, uint16_t* out, void* stream) {
-  int rc = check_cfg(cfg);
-  if (rc) return rc;
-  const bool has_rows = cfg->T > 0;
-  rc = check_ptrs({{y, has_rows}, {expand_idx, has_rows}, {offsets, true}, {topk_weights, has_rows},
-                   {out, has_rows}});
+  const bool has_rows = cfg && cfg->T > 0;
+  const int rc = check_args(cfg, {{y, has_rows}, {expand_idx, has_rows}, {offsets, true}, {topk_weights, has_rows},
+                                  {out, has_rows}});
   if (rc) return rc;
   const Shape s = shape_of(cfg);
   return hip_status(
@@ -321,12 +333,10 @@ int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* expand_idx, c
 
 int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
               const moe_weights* w, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_cfg(cfg);
+  const bool has_rows = cfg && cfg->T > 0;
+  int rc = check_args(cfg, {{x, has_rows}, {topk_ids, has_rows}, {topk_weights, has_rows}, {out, has_rows},
+                            {ws, true}}, w, true);
   if (rc) return rc;
-  const bool has_rows = cfg->T > 0;
-  rc = check_ptrs({{x, has_rows}, {topk_ids, has_rows}, {topk_weights, has_rows}, {out, has_rows}, {ws, true}});
-  if (rc) return rc;
-  if ((rc = check_weights(cfg, w))) return rc;
   const Shape s = shape_of(cfg);
   const WsLayout L = make_ws_layout(s);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -368,11 +378,11 @@ int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, co
 }
 
 int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_weights* packed, void* stream) {
-  int rc = check_cfg(cfg);
-  if (rc) return rc;
-  if ((rc = check_weights(cfg, canonical))) return rc;
-  if (!packed) return MOE_ERR_NULL_ARG;
-  if ((rc = check_weights(cfg, packed))) return rc;
+  if (!cfg || !canonical || !packed) return MOE_ERR_NULL_ARG;
+  int rc;
+  if ((rc = weights_null(cfg, canonical)) || (rc = weights_null(cfg, packed))) return rc;
+  if ((rc = check_shape(cfg))) return rc;
+  if ((rc = weights_layout(cfg, canonical, 0)) || (rc = weights_layout(cfg, packed, -1))) return rc;
   const moe_cfg& c = *cfg;
   const bool mx = c.wfmt == MOE_WFMT_MXFP4;
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -397,6 +407,7 @@ int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_we
       if ((rc = hip_status(hipMemcpyAsync(q.stl, q.s, sb, hipMemcpyDeviceToDevice, st)))) return rc;
     }
   }
+  packed->prepacked = 1;
   return MOE_OK;
 }
 
@@ -415,6 +426,13 @@ int moe_mfma_rate(int wfmt, int iters, void* sink, size_t sink_bytes, double* fl
   if (iters < 1 || iters > 65536) return MOE_ERR_BAD_SHAPE;
   if (sink_bytes < 4 * size_t(mfma_rate_grid())) return MOE_ERR_WORKSPACE;
   return hip_status(launch_mfma_rate(wfmt, iters, static_cast<float*>(sink), flops, static_cast<hipStream_t>(stream)));
+}
+
+int moe_encode_e4m3(const float* v, size_t n, uint8_t* codes, void* stream) {
+  if (n > 0 && (!v || !codes)) return MOE_ERR_NULL_ARG;
+  if (misaligned(v) || misaligned(codes)) return MOE_ERR_MISALIGNED;
+  if (n >= (size_t(1) << 40)) return MOE_ERR_BAD_SHAPE;
+  return hip_status(launch_encode_e4m3(v, long(n), codes, static_cast<hipStream_t>(stream)));
 }
 
 const char* moe_status_str(int status) {

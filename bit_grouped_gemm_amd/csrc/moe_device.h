@@ -59,6 +59,12 @@ __device__ __forceinline__ uint32_t enc_e4m3x4(float a, float b, float c, float 
   return uint32_t(w);
 }
 
+// SwiGLU of one h element, left half through SiLU times the right half:
+// silu(gate) * up with silu(z) = z / (1 + e^-z), IEEE division and the
+// library exponential.  Every GEMM1 epilogue uses this one formula, so an
+// h value does not depend on which kernel its group's row count selects.
+__device__ __forceinline__ float swiglu(float gate, float up) { return gate / (1.0f + expf(-gate)) * up; }
+
 // Quantisation multiplier and dequant scale of a group with absolute max a.
 __device__ __forceinline__ float quant_mult(float amax) { return 448.0f / fmaxf(amax, 0x1p-64f); }
 

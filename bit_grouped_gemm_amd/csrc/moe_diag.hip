@@ -1,6 +1,8 @@
 // moe_diag.hip -- diagnostics the kernels are measured against: a plain HBM
-// read stream (the achievable bandwidth) and the issued rate of the scaled
-// MFMA the GEMMs use (the achievable matrix-core rate).
+// read stream (the achievable bandwidth), the issued rate of the scaled
+// MFMA the GEMMs use (the achievable matrix-core rate), and the fp32 ->
+// e4m3 conversion every quantiser uses, exposed on its own so it can be
+// checked on every fp32 bit pattern.
 //
 // Read stream:
 // The buffer is cut into one contiguous region per wave (a multiple of the
@@ -9,6 +11,8 @@
 // lanes on consecutive chunks).  Four workgroups of four waves per CU.  Each
 // workgroup folds what it read into one word of the sink, so the loads
 // cannot be dropped.
+#include <algorithm>
+
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -80,7 +84,28 @@ __global__ __launch_bounds__(kStreamThreads) void k_mfma_rate(uint32_t a_word, u
   }
 }
 
+// The quantisers' fp32 -> e4m3 conversion (enc_e4m3x4: saturation at +-448,
+// round to nearest even, sign kept) on n values, four per thread.
+__global__ __launch_bounds__(kStreamThreads) void k_encode_e4m3(const float* __restrict__ v, long n,
+                                                               uint8_t* __restrict__ codes) {
+  const long n4 = n / 4;
+  const long stride = long(gridDim.x) * kStreamThreads;
+  for (long i = long(blockIdx.x) * kStreamThreads + threadIdx.x; i < n4; i += stride) {
+    const v4f x = reinterpret_cast<const v4f*>(v)[i];
+    reinterpret_cast<uint32_t*>(codes)[i] = enc_e4m3x4(x[0], x[1], x[2], x[3]);
+  }
+  const long t = n4 * 4 + threadIdx.x;  // the last n % 4 values, by block 0
+  if (blockIdx.x == 0 && t < n) codes[t] = uint8_t(enc_e4m3x4(v[t], 0.0f, 0.0f, 0.0f) & 0xFFu);
+}
+
 }  // namespace
+
+hipError_t launch_encode_e4m3(const float* v, long n, uint8_t* codes, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const long blocks = std::min<long>(4096, (n / 4 + kStreamThreads - 1) / kStreamThreads + 1);
+  hipLaunchKernelGGL(k_encode_e4m3, dim3(unsigned(blocks)), dim3(kStreamThreads), 0, st, v, n, codes);
+  return hipGetLastError();
+}
 
 int mfma_rate_grid() { return stream_read_grid(); }
 

@@ -359,14 +359,18 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
   };
 
   // ---- accumulators: e4m3 weights promote each step's MFMA result with a
-  // VALU FMA (acc += d * ws * xs).  MXFP4 weights carry their scales inside
-  // the MFMA, and the accumulator is kept in units of the current step's
-  // token scale: when a step's fragments are read it is multiplied by
-  // xs_prev / xs_cur, then the MFMA adds the step's product in place; the
-  // epilogue multiplies by the last step's xs.  Token scales are positive
-  // (at least 2^-64 / 448), so the ratio is always defined.
+  // VALU FMA (acc += d * ws * xs).  MXFP4 weights carry their e8m0 scales
+  // inside the MFMA, and so does each token's scale xs = mt * 2^et (mt in
+  // [1, 2)): its power of two 2^et is the MFMA's B-operand scale, exact
+  // whatever the exponent.  The accumulator is kept in units of the current
+  // step's mantissa mt: when a step's fragments are read it is multiplied by
+  // mt_prev / mt_cur, a ratio in (1/2, 2) that cannot overflow or underflow
+  // however far apart two steps' token scales are (an all-zero group next to
+  // a huge one), then the MFMA adds the step's product in place; the epilogue
+  // multiplies by the last step's mt.  Token scales are positive normal
+  // floats (at least 2^-64 / 448), so the split is always defined.
   v4f acc[4][NTMAX];
-  float xsp[NTMAX];  // MXFP4: the token scales of the previous step
+  float xsp[NTMAX];  // MXFP4: the token-scale mantissas of the previous step
   auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -404,8 +408,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
         for (int q = 0; q < 2; ++q)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float gt = acc[q][tt][i], up = acc[q + 2][tt][i];
-            const float v = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+            const float v = swiglu(acc[q][tt][i], acc[q + 2][tt][i]);
             acc[q][tt][i] = v;
             amax = fmaxf(amax, fabsf(v));
           }
@@ -520,6 +523,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
     int sa[4];
     float wsv[4];
     float xsv[NA];
+    int sb[NA];  // MXFP4: e8m0 code of each token's scale exponent (B-operand scale)
     v8i bf[NA];
     // the fragments of step k in stage st; MXFP4: rescale to its token scales
     auto READ = [&](const uint8_t* st, int k) __attribute__((always_inline)) {
@@ -550,8 +554,13 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
       if (WF == 1) {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
-          const float rr = xsp[tt] * __builtin_amdgcn_rcpf(xsv[tt]);
-          xsp[tt] = xsv[tt];
+          // xs = mantissa * 2^(e - 127): the biased exponent field is the
+          // e8m0 code of that power of two; the mantissa keeps the low bits
+          const uint32_t u = __float_as_uint(xsv[tt]);
+          sb[tt] = int(u >> 23);
+          const float mt = __uint_as_float((u & 0x007FFFFFu) | 0x3F800000u);
+          const float rr = xsp[tt] * __builtin_amdgcn_rcpf(mt);
+          xsp[tt] = mt;
 #pragma unroll
           for (int q = 0; q < 4; ++q) acc[q][tt] *= rr;
         }
@@ -566,7 +575,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
         if (WF == 1) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            acc[q][tt] = mfma_scaled_acc<kFmtE2M1, kFmtE4M3>(af[q], bf[tt], acc[q][tt], sa[q], kUnitScale);
+            acc[q][tt] = mfma_scaled_acc<kFmtE2M1, kFmtE4M3>(af[q], bf[tt], acc[q][tt], sa[q], sb[tt]);
         } else {
           v4f d[4];
 #pragma unroll

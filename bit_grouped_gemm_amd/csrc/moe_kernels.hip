@@ -496,8 +496,7 @@ __device__ __forceinline__ void swiglu_requant_store(const v4f (&acc)[4][NTT], c
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float gt = acc[jt][t][i], up = acc[2 + jt][t][i];
-        const float v = gt / (1.0f + expf(-gt)) * up;
+        const float v = swiglu(acc[jt][t][i], acc[2 + jt][t][i]);
         h[t][jt * 4 + i] = v;
         amax[t] = fmaxf(amax[t], fabsf(v));
       }

@@ -80,6 +80,7 @@ int stream_read_grid();
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 int mfma_rate_grid();
 hipError_t launch_mfma_rate(int wfmt, int iters, float* sink, double* flops, hipStream_t st);
+hipError_t launch_encode_e4m3(const float* v, long n, uint8_t* codes, hipStream_t st);
 
 hipError_t launch_tile_weights(int wfmt, int mats, int N, int K, const uint8_t* w, const uint8_t* s, uint8_t* w_tiled,
                                uint8_t* s_tiled, hipStream_t st);

@@ -24,7 +24,11 @@
  *   - Outputs are fully overwritten; nothing accumulates into caller memory.
  *   - Return value: MOE_OK or an error code below.  Every error except
  *     MOE_ERR_HIP is detected on the host before anything is enqueued.
- *     Device faults surface at the caller's next synchronisation.
+ *     NULL pointers are rejected first, before any shape, size or layout
+ *     check (the onnxruntime QMoE PR's expert store likewise rejects null or
+ *     zero-byte buffers before range validation); a pointer may be NULL only
+ *     where its buffer has zero bytes (T = 0) or the call documents it as
+ *     optional.  Device faults surface at the caller's next synchronisation.
  *   - Pointers must be 16-byte aligned (MOE_ERR_MISALIGNED otherwise).
  *
  * Number formats
@@ -82,22 +86,35 @@ typedef struct moe_cfg {
   int32_t has_shared;
 } moe_cfg;
 
-/* Expert weights (host struct of device pointers) as the GEMM entry points
- * read them: codes and MXFP4 scales in the TILED layout written by
- * moe_prepack_weights from the canonical row-major tensors below; e4m3
- * block scales stay row-major.  Row-major tensors -- FP8: w1 uint8 [E][2I][H] (rows 0..I-1
- * gate, I..2I-1 up, K contiguous), w1s float [E][2I/wblk][H/wblk]; w2 uint8
- * [E][H][I], w2s float [E][H/wblk][I/wblk].  MXFP4: w1 uint8 [E][2I][H/2],
- * w1s uint8 [E][2I][H/32]; w2 uint8 [E][H][I/2], w2s uint8 [E][H][I/32].
- * The tiled tensors have the same sizes.  sw1..sw2s: the shared expert with
- * a leading dimension of 1 (may be NULL when has_shared == 0). */
+/* Expert weights (host struct of device pointers).
+ *   prepacked = 0: the CANONICAL row-major tensors -- FP8: w1 uint8
+ *     [E][2I][H] (rows 0..I-1 gate, I..2I-1 up, K contiguous), w1s float
+ *     [E][2I/wblk][H/wblk]; w2 uint8 [E][H][I], w2s float [E][H/wblk][I/wblk].
+ *     MXFP4: w1 uint8 [E][2I][H/2], w1s uint8 [E][2I][H/32]; w2 uint8
+ *     [E][H][I/2], w2s uint8 [E][H][I/32].
+ *   prepacked = 1: the same tensors in the TILED layout written by
+ *     moe_prepack_weights (codes and MXFP4 scales re-laid out, e4m3 block
+ *     scales unchanged; same sizes).
+ * The GEMM entry points and moe_layer read only the tiled layout and return
+ * MOE_ERR_UNSUPPORTED for prepacked == 0, the way the FusedDeepMoE family
+ * analysis's framework kernel entry takes GMM1 weights already permuted
+ * (its gmm1_permuted_weight argument) and the onnxruntime QMoE PR marks
+ * pre-arranged weights with a weights_prepacked flag.
+ * sw1..sw2s: the shared expert with a leading dimension of 1 (may be NULL
+ * when has_shared == 0). */
 typedef struct moe_weights {
   const void *w1, *w1s, *w2, *w2s;
   const void *sw1, *sw1s, *sw2, *sw2s;
+  int32_t prepacked;
 } moe_weights;
 
 /* Bytes of workspace moe_layer and the stage calls need for this shape
- * (host only; no device work).  *bytes is written on MOE_OK. */
+ * (host only; no device work).  *bytes is written on MOE_OK.  The caller
+ * allocates it once per shape and passes it to every call, as the
+ * FusedDeepMoE family analysis sizes its operator workspace on the host
+ * from the tiling (W4A8 workspace computation: a fixed reserve plus the
+ * stage buffers).  Layer intermediates, split-K partial sums and arrival
+ * counters live there; contents on entry do not matter. */
 int moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
 
 /* Steps 1-4: expert histogram, exclusive prefix-scan offsets (the group
@@ -171,8 +188,11 @@ int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, co
  * kernel entry).  Every tensor of `canonical` is read and the matching one
  * of `packed` written (w1, w1s, w2, w2s, and sw1..sw2s when has_shared);
  * `packed` holds buffers of the canonical sizes, distinct from the
- * canonical ones (MOE_ERR_UNSUPPORTED otherwise).  Only cfg's E, H, I,
- * wfmt, wblk and has_shared matter (the rest must still be valid).
+ * canonical ones (MOE_ERR_UNSUPPORTED otherwise).  canonical->prepacked
+ * must be 0 (MOE_ERR_UNSUPPORTED otherwise: the tensors are already
+ * tiled); on MOE_OK packed->prepacked is set to 1 (the struct itself is
+ * host memory written by the call).  Only cfg's E, H, I, wfmt, wblk and
+ * has_shared matter (the rest must still be valid).
  *
  * Tiled layout of a [mats][N][K] tensor: tile (k step ks, row tile rt) =
  * rows 16 rt..16 rt+15 x K 128 ks..128 ks+127, stored at
@@ -211,6 +231,17 @@ int moe_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes
  * MOE_ERR_UNSUPPORTED (other wfmt), MOE_ERR_BAD_SHAPE (iters) and
  * MOE_ERR_WORKSPACE (sink too small) are host checks. */
 int moe_mfma_rate(int wfmt, int iters, void* sink, size_t sink_bytes, double* flops, void* stream);
+
+/* Diagnostic: the fp32 -> e4m3 conversion every quantiser of the layer
+ * uses (activation codes in moe_permute, requantised h in GEMM1), applied
+ * to n values: saturation at +-448, round to nearest even, the sign kept
+ * (values that round to zero give 0x00 or 0x80) -- the activation rule's
+ * "code = e4m3(x * m)" step.  v (device, n fp32; NaN is outside the
+ * contract) -> codes (device, n bytes).  Exposed so the conversion can be
+ * checked against an independent encoder on every finite fp32 pattern.
+ * MOE_ERR_NULL_ARG (v or codes NULL with n > 0), MOE_ERR_MISALIGNED and
+ * MOE_ERR_BAD_SHAPE (n >= 2^40) are host checks. */
+int moe_encode_e4m3(const float* v, size_t n, uint8_t* codes, void* stream);
 
 /* Static description of an error code (host only). */
 const char* moe_status_str(int status);

@@ -85,7 +85,8 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails it
 
 
 def _w(**kw):
-    f = dict(w1=FAKE, w1s=FAKE, w2=FAKE, w2s=FAKE, sw1=None, sw1s=None, sw2=None, sw2s=None)
+    """Tiled (prepacked) fake weights unless prepacked=0 is given."""
+    f = dict(w1=FAKE, w1s=FAKE, w2=FAKE, w2s=FAKE, sw1=None, sw1s=None, sw2=None, sw2s=None, prepacked=1)
     f.update(kw)
     return moe.MoeWeights(**f)
 
@@ -151,16 +152,63 @@ def test_product_path_does_not_touch_the_oracle():
                 assert "oracle" not in src, f
 
 
+def test_canonical_weights_are_rejected_by_the_gemms(lib):
+    """The GEMM entry points read only the tiled layout: weights flagged
+    canonical (prepacked = 0), or with any flag other than 0 / 1, are
+    rejected before anything is enqueued."""
+    c = cfg()
+    cc = c.c()
+    _, n = ws_size(c)
+    for flag in (0, 2, -1):
+        w = _w(prepacked=flag)
+        assert moe.raw_call("moe_layer", C.byref(cc), FAKE, FAKE, FAKE, C.byref(w), FAKE, FAKE, n,
+                            None) == moe.MOE_ERR_UNSUPPORTED
+        assert moe.raw_call("moe_grouped_gemm1_swiglu", C.byref(cc), FAKE, FAKE, FAKE, FAKE, C.byref(w), FAKE,
+                            FAKE, FAKE, n, None) == moe.MOE_ERR_UNSUPPORTED
+        assert moe.raw_call("moe_grouped_gemm2", C.byref(cc), FAKE, FAKE, FAKE, C.byref(w), FAKE, FAKE, n,
+                            None) == moe.MOE_ERR_UNSUPPORTED
+    # the binding marks canonical tensors (no prepacked attribute) as 0 and tiled ones as 1
+    assert moe.weights_struct(object()).prepacked == 0
+
+
+def test_null_pointers_are_rejected_before_shape_checks(lib):
+    """A NULL required pointer wins over an invalid shape (NULL buffers are
+    rejected before range validation)."""
+    bad = cfg(topk=0, H=200).c()
+    w = _w()
+    assert moe.raw_call("moe_layer", C.byref(bad), None, FAKE, FAKE, C.byref(w), FAKE, FAKE, 1 << 20,
+                        None) == moe.MOE_ERR_NULL_ARG
+    assert moe.raw_call("moe_layer", C.byref(bad), FAKE, FAKE, FAKE, C.byref(_w(w2=None)), FAKE, FAKE, 1 << 20,
+                        None) == moe.MOE_ERR_NULL_ARG
+    assert moe.raw_call("moe_layer", C.byref(bad), FAKE, FAKE, FAKE, C.byref(w), FAKE, FAKE, 1 << 20,
+                        None) == moe.MOE_ERR_BAD_SHAPE
+    assert moe.raw_call("moe_combine", C.byref(bad), FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_NULL_ARG
+    # alignment is checked after the shape
+    assert moe.raw_call("moe_layer", C.byref(bad), FAKE + 4, FAKE, FAKE, C.byref(w), FAKE, FAKE, 1 << 20,
+                        None) == moe.MOE_ERR_BAD_SHAPE
+
+
+def test_encode_e4m3_argument_errors(lib):
+    call = lambda v, n, q: moe.raw_call("moe_encode_e4m3", v, C.c_size_t(n), q, None)
+    assert call(None, 4, FAKE) == moe.MOE_ERR_NULL_ARG
+    assert call(FAKE, 4, None) == moe.MOE_ERR_NULL_ARG
+    assert call(FAKE + 4, 4, FAKE) == moe.MOE_ERR_MISALIGNED
+    assert call(FAKE, 1 << 40, FAKE) == moe.MOE_ERR_BAD_SHAPE
+    assert call(None, 0, None) == moe.MOE_OK          # nothing to encode: nothing enqueued
+
+
 def test_prepack_argument_errors(lib):
     c = cfg()
     cc = c.c()
-    src, dst = _w(), _w(w1=FAKE + 256, w1s=FAKE + 512, w2=FAKE + 768, w2s=FAKE + 1024)
+    src, dst = _w(prepacked=0), _w(w1=FAKE + 256, w1s=FAKE + 512, w2=FAKE + 768, w2s=FAKE + 1024, prepacked=0)
     call = lambda cfgp, a, b: moe.raw_call("moe_prepack_weights", cfgp, a, b, None)
     assert call(None, C.byref(src), C.byref(dst)) == moe.MOE_ERR_NULL_ARG
     assert call(C.byref(cc), None, C.byref(dst)) == moe.MOE_ERR_NULL_ARG
     assert call(C.byref(cc), C.byref(src), None) == moe.MOE_ERR_NULL_ARG
     assert call(C.byref(cc), C.byref(src), C.byref(_w(w2=None))) == moe.MOE_ERR_NULL_ARG
     assert call(C.byref(cc), C.byref(src), C.byref(_w(w1=FAKE + 8))) == moe.MOE_ERR_MISALIGNED
+    # the source must be canonical: already tiled tensors are not re-laid out
+    assert call(C.byref(cc), C.byref(_w(prepacked=1)), C.byref(dst)) == moe.MOE_ERR_UNSUPPORTED
     assert call(C.byref(cfg(topk=0).c()), C.byref(src), C.byref(dst)) == moe.MOE_ERR_BAD_SHAPE
     assert call(C.byref(cc), C.byref(src), C.byref(src)) == moe.MOE_ERR_UNSUPPORTED   # in place
     cs = cfg(has_shared=1).c()

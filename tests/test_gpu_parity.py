@@ -360,10 +360,21 @@ FULL = [(n, T) for n in ("decode_fp8", "decode_mxfp4") for T in synth.WORKLOADS[
        [("prefill_mxfp4", 4096)]
 
 
+def sample_tokens(T, seed):
+    """Tokens whose layer output is checked at full size: every token up to
+    T = 64, 64 of them up to T = 256 and 256 beyond (always the first and
+    the last); tokens are independent once the permute is fixed."""
+    n = T if T <= 64 else (64 if T <= 256 else 256)
+    rng = np.random.default_rng(seed)
+    return sorted(set([0, T - 1] + list(rng.choice(T, size=n, replace=False))))
+
+
 @pytest.mark.parametrize("name,T", FULL)
 def test_layer_full_size_sampled(name, T):
-    """Full workload shapes, launched exactly as the bench launches them;
-    every index output checked bit-exact, the output on sampled tokens."""
+    """Full workload shapes, launched exactly as the bench launches them:
+    the permute / quantisation outputs of the same shape and inputs checked
+    bit-exact against the oracle, the layer output on sampled tokens (at
+    least 64 of 256, 256 of 4096) against the oracle's within the bound."""
     moe = M()
     wl = synth.WORKLOADS[name]
     _note(f"full {name} T={T}")
@@ -372,9 +383,15 @@ def test_layer_full_size_sampled(name, T):
     cfg = moe.Cfg.for_workload(wl, T)
     ws = moe.workspace(cfg)
     out = moe.moe_layer(cfg, x, ids, tw, w, ws=ws)
+    perm = moe.moe_permute(cfg, x, ids, ws=moe.workspace(cfg))
     torch.cuda.synchronize()
-    rng = np.random.default_rng(T)
-    toks = sorted(set([0, T - 1] + list(rng.choice(T, size=min(T, 10), replace=False))))
+    counts, offsets, eidx, rtok, xq, xs = [t.cpu().numpy() for t in perm]
+    rc, ro, re_, rr = oracle.permute(ids.cpu(), wl.E, wl.shared)
+    assert np.array_equal(counts, rc) and np.array_equal(offsets, ro)
+    assert np.array_equal(eidx, re_) and np.array_equal(rtok, rr)
+    qx, qs = oracle.quant_act(x.cpu(), wl.act_group)
+    assert np.array_equal(xq, qx) and np.array_equal(xs.view(np.uint32), qs.view(np.uint32))
+    toks = sample_tokens(T, T)
     ref = oracle.layer_for(wl, T, wc).layer(x.cpu(), ids.cpu(), tw.cpu(), toks=toks)
     tol_check(out.float().cpu().numpy()[toks], ref, f"{name} T={T} sampled {len(toks)}")
     assert torch.isfinite(out.float()).all()
@@ -576,6 +593,148 @@ def test_worked_examples_on_gpu():
             for i, v in ex["expect_out"][str(t)]:
                 want[i] = v
             assert np.array_equal(got[t], want), (ex["name"], t, got[t][:4])
+
+
+# ------------------------------------------------------------ extreme activation ranges
+# (case, T): the decode e4m3 kernels (128- and 32-blocks) and MXFP4 kernels,
+# and the many-row e4m3 and MXFP4 kernels (enough rows per expert to select them)
+EXTREME = [("fp8_b128", 37), ("fp8_b32", 37), ("mxfp4", 37), ("big_fp8", 200), ("big_mxfp4_shared", 200)]
+
+
+def extreme_rows(x, G):
+    """Overwrite some tokens' 128-groups with all-zero, subnormal and very
+    large (1e16 .. 3e17) values, next to ordinary N(0,1) groups, in every
+    order: the per-step token scales then differ by up to ~2^130 between
+    neighbouring K steps.  h = silu(g) * up stays finite in fp32."""
+    x = x.float().clone()
+    T, H = x.shape
+    ng = H // G
+    factors = [0.0, 1e16, 1e-39, 1.0, 3e17, 0.0, 1e-20, 1e16]
+    for t in range(0, T, 3):
+        for gi in range(ng):
+            f = factors[(gi + t) % len(factors)]
+            if f != 1.0:
+                x[t, gi * G:(gi + 1) * G] *= f
+    x[1] = 0.0                                            # an all-zero token
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("name,T", EXTREME)
+def test_layer_extreme_activation_ranges(name, T):
+    """Rows whose 128-groups mix all-zero, subnormal and very large values,
+    on each GEMM kernel path: the output is finite and each token's row
+    matches the oracle within the bound taken over that row alone."""
+    moe = M()
+    wl = stage_case(name)
+    _note(f"extreme {name} T={T}")
+    w, wc = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=21)
+    x = extreme_rows(x, wl.act_group).to(DEV)
+    cfg = moe.Cfg.for_workload(wl, T)
+    out = moe.moe_layer(cfg, x, ids, tw, w)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    ref = oracle.layer_for(wl, T, wc).layer(x.cpu(), ids.cpu(), tw.cpu())
+    assert np.isfinite(ref).all() and np.abs(ref).max() > 1e20
+    err = np.abs(got - ref).max(axis=1)
+    bound = 1e-2 * np.abs(ref).max(axis=1) + 1e-3
+    worst = int(np.argmax(err / bound))
+    _note(f"  worst token {worst}: err {err[worst]:.3e} bound {bound[worst]:.3e}")
+    assert np.all(err <= bound)
+    assert np.all(got[1] == ref[1])                       # all-zero token: shared expert / zero exactly
+
+
+# ------------------------------------------------------------ weight layout flag
+def test_canonical_weights_rejected_and_prepack_marks_tiled():
+    """moe_layer refuses weights flagged canonical (it reads only the tiled
+    layout); moe_prepack_weights flags its output as tiled."""
+    moe = M()
+    wl = REDUCED["fp8_b128"]
+    T = 5
+    w = synth.gen_weights(wl, seed=1, device=DEV)
+    cfg = moe.Cfg.for_workload(wl, T)
+    x, ids, tw = inputs_for(wl, T, seed=1)
+    out = torch.full((T, wl.H), 7.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_layer(cfg, x, ids, tw, w, out=out)
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert bool((out.float() == 7.0).all())               # nothing was enqueued
+    wt = moe.moe_prepack_weights(cfg, w)
+    assert wt.prepacked == 1
+    moe.moe_layer(cfg, x, ids, tw, wt, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+
+
+# ------------------------------------------------------------ fp32 -> e4m3 conversion
+def test_e4m3_conversion_every_fp32_pattern():
+    """The quantisers' hardware fp32 -> e4m3 conversion (saturating, round to
+    nearest even, sign kept) against PyTorch's conversion of the value
+    clamped to +-448, on every finite fp32 bit pattern (NaN and inf replaced
+    by 0), and on a structured CPU sample against PyTorch's CPU conversion
+    and the oracle's brute-force encoder."""
+    moe = M()
+    chunk = 1 << 28
+    bad = 0
+    for c in range(1 << 32 >> 28):
+        _note(f"  e4m3 patterns chunk {c}")
+        bits = torch.arange(c * chunk, (c + 1) * chunk, dtype=torch.int64, device=DEV).to(torch.int32)
+        v = bits.view(torch.float32)
+        v = torch.where(torch.isfinite(v), v, torch.zeros_like(v))
+        got = moe.moe_encode_e4m3(v)
+        want = v.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+        bad += int((got != want).sum().item())
+        del bits, v, got, want
+    assert bad == 0, f"{bad} fp32 patterns encode differently"
+    # every sign, exponent and top-8 mantissa bits, with four low-bit patterns
+    # (round bit and sticky bits set or clear): the rounding boundaries
+    hi = torch.arange(1 << 17, dtype=torch.int64) << 15
+    pats = torch.cat([hi | lo for lo in (0, 1, 0x4000, 0x7FFF)]).to(torch.int32)
+    vals = pats.view(torch.float32)
+    vals = vals[torch.isfinite(vals)]
+    got = moe.moe_encode_e4m3(vals.to(DEV)).cpu().numpy()
+    want = vals.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+    assert np.array_equal(got, oracle.enc_e4m3_array(vals.numpy()))
+
+
+# ------------------------------------------------------------ graph capture
+@pytest.mark.parametrize("name,T", [("fp8_b128", 37), ("mxfp4_split_shared", 3), ("big_mxfp4_shared", 200)])
+def test_layer_graph_capture_replays_bitexact(name, T):
+    """moe_layer enqueues only kernels (no memsets, no host work), so it can
+    be captured in a graph: every replay, with unrelated eager layer calls and
+    synchronisations in between, equals the direct call bit for bit."""
+    moe = M()
+    wl = stage_case(name)
+    _note(f"graph {name} T={T}")
+    w, _ = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=17)
+    cfg = moe.Cfg.for_workload(wl, T)
+    ws = moe.workspace(cfg)
+    ws.fill_(0xFF)
+    out = torch.empty(T, wl.H, dtype=torch.bfloat16, device=DEV)
+    ref = moe.moe_layer(cfg, x, ids, tw, w, ws=ws).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.moe_layer(cfg, x, ids, tw, w, ws=ws, out=out)   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        moe.moe_layer(cfg, x, ids, tw, w, ws=ws, out=out)
+    x2, ids2, tw2 = inputs_for(wl, T, seed=18)
+    for rep in range(4):
+        out.zero_()
+        ws.fill_(0xA5 if rep % 2 else 0x00)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+        moe.moe_layer(cfg, x2, ids2, tw2, w)                # unrelated eager work between replays
+        torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("nbytes", [16, 4096 + 48, (1 << 24) + 16 * 37])
