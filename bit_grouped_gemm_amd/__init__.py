@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
     moe_grouped_gemm2(cfg, hq, hs, offsets, weights, ws) -> y
     moe_combine(cfg, y, expand_idx, offsets, topk_weights) -> out
     moe_layer(cfg, x, topk_ids, topk_weights, weights, ws=None, out=None) -> out
+    moe_layer_static(cfg, x, topk_ids, topk_weights, weights, out=None) -> out   (no workspace)
     moe_prepack_weights(cfg, weights) -> TiledWeights
     moe_encode_e4m3(v) -> codes   (diagnostic: the quantisers' fp32 -> e4m3 conversion)
 
@@ -43,8 +44,8 @@ WFMT_FP8_BLOCK = 0
 WFMT_MXFP4 = 1
 
 EXPORTS = ("moe_workspace_size", "moe_permute", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm2",
-           "moe_combine", "moe_layer", "moe_prepack_weights", "moe_stream_read", "moe_mfma_rate",
-           "moe_encode_e4m3", "moe_status_str")
+           "moe_combine", "moe_layer", "moe_layer_static", "moe_prepack_weights", "moe_stream_read",
+           "moe_mfma_rate", "moe_encode_e4m3", "moe_status_str")
 
 
 class MoeCfg(C.Structure):
@@ -84,6 +85,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     L.moe_grouped_gemm2.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp]
     L.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
     L.moe_layer.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp]
+    L.moe_layer_static.argtypes = [cfgp, vp, vp, vp, wp, vp, vp]
     L.moe_prepack_weights.argtypes = [cfgp, wp, wp, vp]
     L.moe_stream_read.argtypes = [vp, sz, vp, sz, vp]
     L.moe_mfma_rate.argtypes = [C.c_int, C.c_int, vp, sz, C.POINTER(C.c_double), vp]
@@ -227,6 +229,21 @@ def moe_layer(cfg: Cfg, x, topk_ids, topk_weights, weights, ws: Optional[torch.T
     c, w = cfg.c(), weights_struct(weights)
     _check("moe_layer", load().moe_layer(C.byref(c), _ptr(_u16(x)), _ptr(topk_ids), _ptr(topk_weights), C.byref(w),
                                          _ptr(_u16(out)), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+STATIC_SCRATCH_BYTES = 64 << 20  # MOE_STATIC_SCRATCH_BYTES
+
+
+def moe_layer_static(cfg: Cfg, x, topk_ids, topk_weights, weights,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_layer with the library's static per-GPU scratch instead of a
+    workspace (the call allocates nothing on the library side)."""
+    if out is None:
+        out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device=x.device)
+    c, w = cfg.c(), weights_struct(weights)
+    _check("moe_layer_static", load().moe_layer_static(C.byref(c), _ptr(_u16(x)), _ptr(topk_ids), _ptr(topk_weights),
+                                                       C.byref(w), _ptr(_u16(out)), _stream()))
     return out
 
 

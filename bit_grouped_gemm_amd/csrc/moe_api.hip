@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
+#include <mutex>
 #include <utility>
 
 #include "../../include/moe.h"
@@ -167,6 +168,9 @@ using namespace moe;
 
 namespace {
 
+constexpr size_t kStaticScratchBytes = MOE_STATIC_SCRATCH_BYTES;
+static_assert(kStaticScratchBytes % 256 == 0, "scratch size");
+
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 // Shape and format checks of a (non-null) cfg.
@@ -235,6 +239,75 @@ int check_args(const moe_cfg* c, PtrList ps, const moe_weights* w = nullptr, boo
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// The layer's launch sequence over a scratch region `b` of at least L.total
+// bytes (a caller's workspace, or this GPU's static scratch array).
+int enqueue_layer(const Shape& s, const WsLayout& L, const uint16_t* x, const int32_t* topk_ids,
+                  const float* topk_weights, const moe_weights* w, uint16_t* out, char* b, hipStream_t st) {
+  int rc;
+  int32_t* counts = reinterpret_cast<int32_t*>(b + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  int32_t* eidx = reinterpret_cast<int32_t*>(b + L.expand_idx);
+  int32_t* rtok = reinterpret_cast<int32_t*>(b + L.row_token);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(b + L.xq);
+  float* xs = reinterpret_cast<float*>(b + L.xs);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(b + L.hq);
+  float* hs = reinterpret_cast<float*>(b + L.hs);
+  // GEMM2 rows stay inside the layer as bf16 (half the bytes of the fp32
+  // rows the stage export returns); the combine accumulates them in fp32
+  uint16_t* yb = reinterpret_cast<uint16_t*>(b + L.y);
+  int32_t* cnt1 = reinterpret_cast<int32_t*>(b + L.cnt1);
+  int32_t* cnt2 = reinterpret_cast<int32_t*>(b + L.cnt2);
+  // the routing kernel zeroes every split-K arrival counter of the call
+  const int nclear = int((L.total - L.cnt1) / 4);
+  int32_t* chunk_cnt = reinterpret_cast<int32_t*>(b + L.chunk_cnt);
+  if ((rc = hip_status(launch_route_quant(s, x, topk_ids, counts, offsets, eidx, rtok, xq, xs, cnt1, nclear,
+                                          chunk_cnt, st))))
+    return rc;
+  if (s.T == 0) return MOE_OK;
+  const WeightPtrs w1{static_cast<const uint8_t*>(w->w1), w->w1s, static_cast<const uint8_t*>(w->sw1), w->sw1s};
+  const WeightPtrs w2{static_cast<const uint8_t*>(w->w2), w->w2s, static_cast<const uint8_t*>(w->sw2), w->sw2s};
+  if (s.big) {
+    if ((rc = hip_status(launch_gemm1_big(s, xq, xs, rtok, offsets, w1, hq, hs, 1, st)))) return rc;
+    if ((rc = hip_status(launch_gemm2_big(s, hq, hs, offsets, w2, nullptr, yb, 1, st)))) return rc;
+  } else {
+    if ((rc = hip_status(launch_gemm1(s, xq, xs, rtok, offsets, w1, hq, hs,
+                                      reinterpret_cast<float*>(b + L.part1), cnt1, st))))
+      return rc;
+    if ((rc = hip_status(launch_gemm2(s, hq, hs, offsets, w2, nullptr, yb, reinterpret_cast<float*>(b + L.part2),
+                                      cnt2, st))))
+      return rc;
+  }
+  return hip_status(launch_combine(s, nullptr, yb, eidx, offsets, topk_weights, out, st));
+}
+
+// Scratch of moe_layer_static: one file-scope device array, which every GPU
+// the library runs on holds (its own copy, at its own address) until the
+// process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory, so it is never passed to a kernel or a copy: its device
+// address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and kept in scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+char* scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch array (the current device: the one the stream
+// belongs to); the first call on a device resolves the address.
+int static_scratch(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    scratch_ptr[dev] = static_cast<char*>(p);
+  }
+  *out = scratch_ptr[dev];
+  return MOE_OK;
+}
 
 }  // namespace
 
@@ -340,41 +413,22 @@ int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, co
   const Shape s = shape_of(cfg);
   const WsLayout L = make_ws_layout(s);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-  char* b = static_cast<char*>(ws);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  int32_t* counts = reinterpret_cast<int32_t*>(b + L.counts);
-  int32_t* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
-  int32_t* eidx = reinterpret_cast<int32_t*>(b + L.expand_idx);
-  int32_t* rtok = reinterpret_cast<int32_t*>(b + L.row_token);
-  uint8_t* xq = reinterpret_cast<uint8_t*>(b + L.xq);
-  float* xs = reinterpret_cast<float*>(b + L.xs);
-  uint8_t* hq = reinterpret_cast<uint8_t*>(b + L.hq);
-  float* hs = reinterpret_cast<float*>(b + L.hs);
-  // GEMM2 rows stay inside the layer as bf16 (half the bytes of the fp32
-  // rows the stage export returns); the combine accumulates them in fp32
-  uint16_t* yb = reinterpret_cast<uint16_t*>(b + L.y);
-  int32_t* cnt1 = reinterpret_cast<int32_t*>(b + L.cnt1);
-  int32_t* cnt2 = reinterpret_cast<int32_t*>(b + L.cnt2);
-  const int nclear = int((L.total - L.cnt1) / 4);
-  int32_t* chunk_cnt = reinterpret_cast<int32_t*>(b + L.chunk_cnt);
-  if ((rc = hip_status(launch_route_quant(s, x, topk_ids, counts, offsets, eidx, rtok, xq, xs, cnt1, nclear,
-                                          chunk_cnt, st))))
-    return rc;
-  if (!has_rows) return MOE_OK;
-  const WeightPtrs w1{static_cast<const uint8_t*>(w->w1), w->w1s, static_cast<const uint8_t*>(w->sw1), w->sw1s};
-  const WeightPtrs w2{static_cast<const uint8_t*>(w->w2), w->w2s, static_cast<const uint8_t*>(w->sw2), w->sw2s};
-  if (s.big) {
-    if ((rc = hip_status(launch_gemm1_big(s, xq, xs, rtok, offsets, w1, hq, hs, 1, st)))) return rc;
-    if ((rc = hip_status(launch_gemm2_big(s, hq, hs, offsets, w2, nullptr, yb, 1, st)))) return rc;
-  } else {
-    if ((rc = hip_status(launch_gemm1(s, xq, xs, rtok, offsets, w1, hq, hs,
-                                      reinterpret_cast<float*>(b + L.part1), cnt1, st))))
-      return rc;
-    if ((rc = hip_status(launch_gemm2(s, hq, hs, offsets, w2, nullptr, yb, reinterpret_cast<float*>(b + L.part2),
-                                      cnt2, st))))
-      return rc;
-  }
-  return hip_status(launch_combine(s, nullptr, yb, eidx, offsets, topk_weights, out, st));
+  return enqueue_layer(s, L, x, topk_ids, topk_weights, w, out, static_cast<char*>(ws),
+                       static_cast<hipStream_t>(stream));
+}
+
+int moe_layer_static(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                     const moe_weights* w, uint16_t* out, void* stream) {
+  const bool has_rows = cfg && cfg->T > 0;
+  int rc = check_args(cfg, {{x, has_rows}, {topk_ids, has_rows}, {topk_weights, has_rows}, {out, has_rows}}, w,
+                      true);
+  if (rc) return rc;
+  const Shape s = shape_of(cfg);
+  const WsLayout L = make_ws_layout(s);
+  if (L.total > kStaticScratchBytes) return MOE_ERR_WORKSPACE;
+  char* base = nullptr;
+  if ((rc = static_scratch(&base))) return rc;
+  return enqueue_layer(s, L, x, topk_ids, topk_weights, w, out, base, static_cast<hipStream_t>(stream));
 }
 
 int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_weights* packed, void* stream) {

@@ -180,6 +180,28 @@ int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* expand_idx, c
 int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
               const moe_weights* w, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_layer for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation and kernels as moe_layer, bit-identical results, but
+ * no workspace argument.  Scratch is a static device array of
+ * MOE_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on every GPU it
+ * runs on until the process ends; shapes whose moe_workspace_size exceeds
+ * it return MOE_ERR_WORKSPACE (host check; e.g. the H=4096 E=64 top-8
+ * I=1536 layer fits up to T = 256, the H=7168 E=256 top-8 I=2048 layer
+ * with a shared expert up to T = 192).  The call allocates and frees
+ * nothing.  The device is the current one (the stream's); the first call on
+ * a device looks up the array's address (hipGetSymbolAddress), so make it
+ * once outside any graph capture; later calls only enqueue kernels.
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents (the kernels clear what must start at zero): calls that
+ * overlap on one GPU -- on different streams, or from different threads --
+ * race and must be serialised by the caller.
+ * Arguments and errors as moe_layer, plus MOE_ERR_HIP if the array's
+ * address cannot be resolved and MOE_ERR_UNSUPPORTED for device ids >= 64. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+int moe_layer_static(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                     const moe_weights* w, uint16_t* out, void* stream);
+
 /* One-time re-layout of a layer's expert weights (canonical row-major, as
  * above) into the tiled layout the GEMM entry points read -- the step a
  * caller runs when weights are loaded, as the FusedDeepMoE family analysis

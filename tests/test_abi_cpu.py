@@ -234,3 +234,19 @@ def test_mfma_rate_argument_errors(lib):
     assert call(0, 0, FAKE, 1 << 12) == moe.MOE_ERR_BAD_SHAPE
     assert call(1, 65537, FAKE, 1 << 12) == moe.MOE_ERR_BAD_SHAPE
     assert call(1, 16, FAKE, 16) == moe.MOE_ERR_WORKSPACE
+
+
+def test_static_entry_point_host_checks(lib):
+    """moe_layer_static takes moe_layer's arguments minus the workspace and
+    refuses, on the host, shapes whose workspace exceeds its static array."""
+    c = cfg()
+    cc = c.c()
+    w = _w()
+    call = lambda cfgp, x, wp: moe.raw_call("moe_layer_static", cfgp, x, FAKE, FAKE, wp, FAKE, None)
+    assert call(None, FAKE, C.byref(w)) == moe.MOE_ERR_NULL_ARG
+    assert call(C.byref(cc), None, C.byref(w)) == moe.MOE_ERR_NULL_ARG
+    assert call(C.byref(cc), FAKE, C.byref(_w(prepacked=0))) == moe.MOE_ERR_UNSUPPORTED
+    big = cfg(T=256, H=7168, I=2048, E=256, topk=8, wblk=128, act_group=128, has_shared=1)
+    assert ws_size(big)[1] > moe.STATIC_SCRATCH_BYTES
+    bc = big.c()
+    assert call(C.byref(bc), FAKE, C.byref(_w(sw1=FAKE, sw1s=FAKE, sw2=FAKE, sw2s=FAKE))) == moe.MOE_ERR_WORKSPACE
