@@ -49,9 +49,11 @@ __device__ __forceinline__ uint32_t enc_e4m3(float v) {
 
 // Four fp32 -> four e4m3 codes (byte i = value i) with the same rounding as
 // enc_e4m3, by the hardware conversion: the values are clamped to +-448 (the
-// saturation) and converted two at a time with round-to-nearest-even.  This
-// was checked against enc_e4m3 on every finite fp32 bit pattern (all 2^32
-// minus inf/NaN, on an MI355X): identical codes, signed zeros included.
+// saturation) and converted two at a time with round-to-nearest-even.  The
+// GPU test suite runs this conversion (exported as moe_encode_e4m3) on every
+// finite fp32 bit pattern against PyTorch's conversion of the clamped value,
+// and on the rounding boundaries against the CPU oracle's brute-force
+// encoder: identical codes, signed zeros included.
 __device__ __forceinline__ uint32_t enc_e4m3x4(float a, float b, float c, float d) {
   const auto sat = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
