@@ -64,6 +64,7 @@ def lib() -> C.CDLL:
         L.oracle_combine.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp]
         L.oracle_layer.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp]
         L.oracle_bruteforce.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp]
+        L.oracle_router.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp]
         L.oracle_set_threads.argtypes = [i32]
         L.oracle_set_mutation.argtypes = [i32]
         _lib = L
@@ -165,6 +166,20 @@ def permute(ids, E: int, has_shared: bool):
     rtok = np.empty(max(T * k + T * int(has_shared), 1), np.int32)
     lib().oracle_permute(_p(ids), T, k, E, int(has_shared), _p(counts), _p(offsets), _p(eidx), _p(rtok))
     return counts, offsets, eidx, rtok[: T * k + T * int(has_shared)]
+
+
+def router(x, wg, k: int):
+    """Router: x bf16 [T,H], wg bf16 [E,H] -> (ids int32 [T,k], weights fp32
+    [T,k], logits fp64 [T,E])."""
+    x, wg = _np(x), _np(wg)
+    assert x.dtype == np.uint16 and wg.dtype == np.uint16
+    T, H = x.shape
+    E = wg.shape[0]
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    lg = np.empty((T, E), np.float64)
+    lib().oracle_router(_p(x), _p(wg), T, H, E, k, _p(ids), _p(w), _p(lg))
+    return ids, w, lg
 
 
 class Layer:

@@ -24,7 +24,13 @@
 //   5. the top-k weighted combine back to token order (ReducePermute:
 //      accumulate each token's expert outputs), plus an always-on shared
 //      expert with weight 1 (GC-MoE abstract: shared experts as an option;
-//      FusedDeepMoE shared-expert path: all tokens, one group).
+//      FusedDeepMoE shared-expert path: all tokens, one group);
+//   6. the router in front of the layer (the routing GEMM plus the routing
+//      selection the DeepGEMM 26/09 news page's Mega Gate paragraph fuses
+//      into one kernel): logits = x . Wg^T, the top-k experts by logit (ties
+//      to the lower expert id), routing weights = the softmax of the k
+//      selected logits (the full softmax renormalised over the top-k, as the
+//      workload description states).
 //
 // Number formats (the pages name FP8, FP4 and MXFP4 but print no bit
 // layouts; these are the OCP 8-bit float E4M3FN and Microscaling e2m1 /
@@ -259,8 +265,10 @@ int oracle_get_threads() { return default_threads(); }
 // Test-only: plant a known mistake (0 = none, 1 = gate/up swapped,
 // 2 = first K-block weight scale dropped, 3 = unstable row order inside an
 // expert, 4 = offsets shifted by one, 5 = the stage combine ignores routing
-// weights, 6 = the stage combine reads token 0's shared row for every token)
-// so tests can show their pins catch it.
+// weights, 6 = the stage combine reads token 0's shared row for every token,
+// 7 = the router breaks logit ties towards the higher expert id, 8 = the
+// router's softmax runs over all E logits) so tests can show their pins
+// catch it.
 void oracle_set_mutation(int m) { g_mutation = m; }
 
 double oracle_dec_e4m3(int c) { return dec_e4m3(uint8_t(c)); }
@@ -469,6 +477,48 @@ void oracle_layer(const Cfg* c, const WSet* w, const uint16_t* x, const int32_t*
       const double* yr = &y_l[pos[offsets[c->E] + t] * H];
       for (int64_t n = 0; n < H; ++n) o[n] += yr[n];
     }
+  });
+}
+
+// Router for T tokens: x bf16 [T][H], wg bf16 [E][H] (one gate row per
+// expert).  logit[t][e] = sum over h of x[t][h] * wg[e][h] in fp64 (every
+// product is exact), summed in h order; ids[t][0..k) = the k experts with
+// the largest logits in descending order, equal logits going to the lower
+// expert id (k rounds of: take the largest logit not yet taken, the lowest
+// id among equal ones); weights[t][j] = exp(l_j - l_0) / sum over the k
+// selected of exp(l_i - l_0), in fp64, rounded to fp32.  logits (optional,
+// may be NULL): fp64 [T][E].
+void oracle_router(const uint16_t* x, const uint16_t* wg, int64_t T, int64_t H, int E, int k, int32_t* ids,
+                   float* weights, double* logits) {
+  parallel_for(T, [&](int64_t t) {
+    std::vector<double> l(E);
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int64_t h = 0; h < H; ++h)
+        acc += double(bf16_to_f32(x[t * H + h])) * double(bf16_to_f32(wg[int64_t(e) * H + h]));
+      l[e] = acc;
+      if (logits) logits[t * E + e] = acc;
+    }
+    std::vector<char> taken(E, 0);
+    std::vector<double> sel(k);
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        const bool better = best < 0 || l[e] > l[best] || (g_mutation == 7 && l[e] == l[best]);
+        if (better) best = e;  // strict '>' keeps the lower id among equal logits
+      }
+      taken[best] = 1;
+      ids[t * k + j] = best;
+      sel[j] = l[best];
+    }
+    double sum = 0.0;
+    if (g_mutation == 8) {  // planted: softmax over all E logits, not renormalised over the top-k
+      for (int e = 0; e < E; ++e) sum += std::exp(l[e] - sel[0]);
+    } else {
+      for (int j = 0; j < k; ++j) sum += std::exp(sel[j] - sel[0]);
+    }
+    for (int j = 0; j < k; ++j) weights[t * k + j] = float(std::exp(sel[j] - sel[0]) / sum);
   });
 }
 

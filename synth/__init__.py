@@ -241,6 +241,17 @@ def gen_weights(wl: Workload, seed: int = 0, device="cpu") -> Weights:
     return out
 
 
+_TID_GATE = 8
+
+
+def gen_gate(wl: Workload, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Router gate weights bf16 [E, H] (one row per expert), N(0, 0.02)
+    rounded to bf16, so that gate logits of N(0,1) activations have a spread
+    of 0.02 * sqrt(H)."""
+    g = _gen(device, stream_seed(seed, wl.wid, _TID_GATE, 0))
+    return (torch.randn(wl.E, wl.H, generator=g, device=device, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+
+
 def gen_inputs(wl: Workload, T: int, seed: int = 0, device="cpu"):
     """(x bf16 [T,H], topk_ids int32 [T,k], topk_weights fp32 [T,k])."""
     x = gen_x(T, wl.H, seed, wl.wid, device)
