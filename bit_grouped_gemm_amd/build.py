@@ -21,17 +21,30 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libmoe.so in-tree (always recompiles)."""
-    os.makedirs(BUILD, exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+DRIVER_SRC = "moe_bench_main.cpp"
+DRIVER = os.path.join(BUILD, "moe_bench")
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libmoe.so in-tree (always recompiles), then the standalone C++
+    driver moe_bench linked against it (a torch-free caller of the ABI, used
+    for profiling)."""
+    os.makedirs(BUILD, exist_ok=True)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    tmp = DRIVER + ".tmp"
+    _run([HIPCC, "-O2", "-std=c++17", "-Wall", os.path.join(CSRC, DRIVER_SRC), "-L" + BUILD, "-lmoe",
+          "-Wl,-rpath,$ORIGIN", "-o", tmp], verbose)
+    os.replace(tmp, DRIVER)
     return LIB
 
 

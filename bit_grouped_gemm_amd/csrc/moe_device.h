@@ -52,7 +52,7 @@ __device__ __forceinline__ uint32_t enc_e4m3(float v) {
 // saturation) and converted two at a time with round-to-nearest-even.  The
 // GPU test suite runs this conversion (exported as moe_encode_e4m3) on every
 // finite fp32 bit pattern against PyTorch's conversion of the clamped value,
-// and on the rounding boundaries against the CPU oracle's brute-force
+// and on the rounding boundaries against a brute-force CPU
 // encoder: identical codes, signed zeros included.
 __device__ __forceinline__ uint32_t enc_e4m3x4(float a, float b, float c, float d) {
   const auto sat = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
