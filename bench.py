@@ -55,6 +55,7 @@ def parse():
     ap.add_argument("--tokens", default=None, help="comma-separated T values (default: each workload's sweep)")
     ap.add_argument("--roofline-T", type=int, default=64)
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay latencies")
+    ap.add_argument("--no-router", action="store_true", help="skip the router (moe_route) section")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=4096 MXFP4 prefill section")
     ap.add_argument("--prefill-reps", type=int, default=20)
@@ -237,6 +238,8 @@ def main():
         "decode_workloads": {n: r for n, r in results.items() if n != args.workload},
         "setup_s": round(setup_s, 1),
     }
+    if not args.no_router:
+        line["router"] = router_section(moe, synth, torch, flush, stream, ev)
     if not args.no_cpu_baseline:
         sw = sweeps[args.workload]
         line["cpu_baseline"] = cpu_baseline(sw.wl, sw.w_rm, sw.cases[sw.RT], sw.RT, args.cpu_seconds)
@@ -287,6 +290,37 @@ def summarize(sw, rec, graph_us):
                            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                            "algorithmic_bytes": int(g1_bytes), "avg_launch_us": stage_us["gemm1_swiglu"]},
     }
+
+
+def router_section(moe, synth, torch, flush, stream, ev, reps=20):
+    """moe_route (gate GEMM + top-k + softmax, one kernel) on the decode FP8
+    layer's shape (H=4096, E=64, top-8) at T = 1, 64, 256 and the prefill
+    shape (H=7168, E=256, top-8) at T = 4096, cold caches: median latency,
+    bytes moved (x, gate rows, ids and weights) per second, TFLOP/s."""
+    out = {}
+    for name, T in (("decode_fp8", 1), ("decode_fp8", 64), ("decode_fp8", 256), ("prefill_mxfp4", 4096)):
+        wl = synth.WORKLOADS[name]
+        wg = synth.gen_gate(wl, seed=0, device=flush.device)
+        x = synth.gen_x(T, wl.H, 0, wl.wid, device=flush.device)
+        cfg = moe.Cfg.for_workload(wl, T)
+        ids = torch.empty(T, wl.topk, dtype=torch.int32, device=flush.device)
+        w = torch.empty(T, wl.topk, dtype=torch.float32, device=flush.device)
+        moe.moe_route(cfg, x, wg, ids, w)
+        ts = []
+        for _ in range(reps):
+            flush.sum(dtype=torch.int64)
+            a, b = ev(), ev()
+            a.record(stream)
+            moe.moe_route(cfg, x, wg, ids, w)
+            b.record(stream)
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e3
+        nbytes = 2 * T * wl.H + 2 * wl.E * wl.H + 8 * T * wl.topk
+        out[f"H{wl.H}_E{wl.E}_T{T}"] = {"latency_us_median": round(us, 2), "bytes": nbytes,
+                                        "GBps": round(nbytes / us / 1e3, 1),
+                                        "TFLOPs": round(2.0 * T * wl.E * wl.H / us / 1e6, 2)}
+    return out
 
 
 def graph_latencies(moe, torch, sweeps, flush, stream, ev, reps):

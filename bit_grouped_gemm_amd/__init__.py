@@ -14,6 +14,7 @@ Entry points (same names as the C ABI):
     moe_layer(cfg, x, topk_ids, topk_weights, weights, ws=None, out=None) -> out
     moe_layer_static(cfg, x, topk_ids, topk_weights, weights, out=None) -> out   (no workspace)
     moe_prepack_weights(cfg, weights) -> TiledWeights
+    moe_route(cfg, x, gate_w) -> (topk_ids, topk_weights)   (the router in front of the layer)
     moe_encode_e4m3(v) -> codes   (diagnostic: the quantisers' fp32 -> e4m3 conversion)
 
 The GEMM entry points read expert weights in the tiled layout: convert the
@@ -45,7 +46,7 @@ WFMT_MXFP4 = 1
 
 EXPORTS = ("moe_workspace_size", "moe_permute", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm2",
            "moe_combine", "moe_layer", "moe_layer_static", "moe_prepack_weights", "moe_stream_read",
-           "moe_mfma_rate", "moe_encode_e4m3", "moe_status_str")
+           "moe_mfma_rate", "moe_encode_e4m3", "moe_route", "moe_status_str")
 
 
 class MoeCfg(C.Structure):
@@ -90,6 +91,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     L.moe_stream_read.argtypes = [vp, sz, vp, sz, vp]
     L.moe_mfma_rate.argtypes = [C.c_int, C.c_int, vp, sz, C.POINTER(C.c_double), vp]
     L.moe_encode_e4m3.argtypes = [vp, sz, vp, vp]
+    L.moe_route.argtypes = [cfgp, vp, vp, vp, vp, vp]
     L.moe_status_str.argtypes = [C.c_int]
     L.moe_status_str.restype = C.c_char_p
     for n in EXPORTS:
@@ -294,6 +296,20 @@ def moe_mfma_rate(wfmt: int, iters: int, sink: torch.Tensor) -> float:
     _check("moe_mfma_rate", load().moe_mfma_rate(int(wfmt), int(iters), _ptr(sink),
                                                   sink.numel() * sink.element_size(), C.byref(flops), _stream()))
     return flops.value
+
+
+def moe_route(cfg: Cfg, x: torch.Tensor, gate_w: torch.Tensor, ids: Optional[torch.Tensor] = None,
+              weights: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Router: bf16 x [T,H] and gate rows [E,H] -> (topk_ids int32 [T,topk],
+    topk_weights fp32 [T,topk]), the layer's routing inputs."""
+    if ids is None:
+        ids = torch.empty(cfg.T, cfg.topk, dtype=torch.int32, device=x.device)
+    if weights is None:
+        weights = torch.empty(cfg.T, cfg.topk, dtype=torch.float32, device=x.device)
+    c = cfg.c()
+    _check("moe_route", load().moe_route(C.byref(c), _ptr(_u16(x)), _ptr(_u16(gate_w)), _ptr(ids), _ptr(weights),
+                                         _stream()))
+    return ids, weights
 
 
 def moe_encode_e4m3(v: torch.Tensor, codes: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -482,6 +482,16 @@ int moe_mfma_rate(int wfmt, int iters, void* sink, size_t sink_bytes, double* fl
   return hip_status(launch_mfma_rate(wfmt, iters, static_cast<float*>(sink), flops, static_cast<hipStream_t>(stream)));
 }
 
+int moe_route(const moe_cfg* cfg, const uint16_t* x, const uint16_t* gate_w, int32_t* topk_ids, float* topk_weights,
+              void* stream) {
+  const bool has_rows = cfg && cfg->T > 0;
+  const int rc = check_args(cfg, {{x, has_rows}, {gate_w, true}, {topk_ids, has_rows}, {topk_weights, has_rows}});
+  if (rc) return rc;
+  if (cfg->E > 256) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_route_gemm(cfg->T, cfg->H, cfg->E, cfg->topk, x, gate_w, topk_ids, topk_weights,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 int moe_encode_e4m3(const float* v, size_t n, uint8_t* codes, void* stream) {
   if (n > 0 && (!v || !codes)) return MOE_ERR_NULL_ARG;
   if (misaligned(v) || misaligned(codes)) return MOE_ERR_MISALIGNED;

@@ -180,6 +180,24 @@ int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* expand_idx, c
 int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
               const moe_weights* w, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
+/* The router in front of the layer, one kernel (the routing GEMM and the
+ * routing selection fused, as the DeepGEMM 26/09 news page describes its
+ * Mega Gate): for every token t,
+ *   logit[e] = sum_h x[t][h] * gate_w[e][h]    (bf16 products, fp32 sums)
+ *   topk_ids[t][0..topk) = the topk experts with the largest logits, in
+ *     descending order, equal logits going to the lower expert id
+ *   topk_weights[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the
+ *     topk selected logits (the softmax renormalised over the top-k)
+ * The outputs are exactly moe_layer's topk_ids / topk_weights inputs.
+ *   x       bf16 [T][H]; gate_w bf16 [E][H] (one gate row per expert)
+ *   topk_ids int32 [T][topk]; topk_weights fp32 [T][topk]
+ * Uses cfg's T, H, E and topk (the rest must still be valid); E <= 256
+ * (MOE_ERR_UNSUPPORTED otherwise).  Logits are summed in fp32, so two
+ * experts whose exact logits differ by less than that rounding may come
+ * out in either order.  Errors as for every entry point. */
+int moe_route(const moe_cfg* cfg, const uint16_t* x, const uint16_t* gate_w, int32_t* topk_ids, float* topk_weights,
+              void* stream);
+
 /* moe_layer for callers that cannot allocate device memory (code under
  * graph capture, tight serving loops, harnesses that forbid allocation):
  * the same computation and kernels as moe_layer, bit-identical results, but

@@ -250,3 +250,15 @@ def test_static_entry_point_host_checks(lib):
     assert ws_size(big)[1] > moe.STATIC_SCRATCH_BYTES
     bc = big.c()
     assert call(C.byref(bc), FAKE, C.byref(_w(sw1=FAKE, sw1s=FAKE, sw2=FAKE, sw2s=FAKE))) == moe.MOE_ERR_WORKSPACE
+
+
+def test_route_argument_errors(lib):
+    c = cfg()
+    cc = c.c()
+    call = lambda cfgp, x, wg, ids, w: moe.raw_call("moe_route", cfgp, x, wg, ids, w, None)
+    assert call(None, FAKE, FAKE, FAKE, FAKE) == moe.MOE_ERR_NULL_ARG
+    assert call(C.byref(cc), FAKE, None, FAKE, FAKE) == moe.MOE_ERR_NULL_ARG
+    assert call(C.byref(cc), FAKE, FAKE, FAKE, None) == moe.MOE_ERR_NULL_ARG
+    assert call(C.byref(cc), FAKE + 2, FAKE, FAKE, FAKE) == moe.MOE_ERR_MISALIGNED
+    assert call(C.byref(cfg(topk=0).c()), FAKE, FAKE, FAKE, FAKE) == moe.MOE_ERR_BAD_SHAPE
+    assert call(C.byref(cfg(E=300, topk=8).c()), FAKE, FAKE, FAKE, FAKE) == moe.MOE_ERR_UNSUPPORTED
