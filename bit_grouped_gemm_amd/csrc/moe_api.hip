@@ -13,43 +13,29 @@
 
 namespace moe {
 
-#ifndef MOE_SPLIT_TARGET_WG
-#define MOE_SPLIT_TARGET_WG 256
-#endif
-#ifndef MOE_SPLIT_TARGET_WG2
-#define MOE_SPLIT_TARGET_WG2 MOE_SPLIT_TARGET_WG
-#endif
-// average rows per touched group from which the big-tile kernels take over
+// Split-K targets about one workgroup per CU, keeping at least four K steps
+// of 128 per workgroup.
+constexpr long kSplitTargetWG = 256;
+constexpr int kSplitMinKSteps = 4;
+// average rows per touched group from which the many-row kernels take over
 // (measured cold-cache crossovers, H=4096 E=64 top-8: e4m3 between 12 and 16
 // rows, MXFP4 between 16 and 24)
-#ifndef MOE_BIG_MIN_AVG_ROWS_FP8
-#define MOE_BIG_MIN_AVG_ROWS_FP8 14
-#endif
-#ifndef MOE_BIG_MIN_AVG_ROWS_FP4
-#define MOE_BIG_MIN_AVG_ROWS_FP4 20
-#endif
-#ifndef MOE_G2_NJ
-#define MOE_G2_NJ 4
-#endif
-// token tiles per decode pass: sized for the mean row count of a touched
-// group plus this many standard deviations of a Poisson count
-#ifndef MOE_NTT_SIGMAS
-#define MOE_NTT_SIGMAS 3.0
-#endif
-#ifndef MOE_SPLIT_MIN_KSTEPS
-#define MOE_SPLIT_MIN_KSTEPS 4
-#endif
+constexpr double kBigMinAvgRowsFp8 = 14.0;
+constexpr double kBigMinAvgRowsFp4 = 20.0;
+// decode passes hold the mean row count of a touched group plus this many
+// standard deviations of a Poisson count
+constexpr double kNttSigmas = 3.0;
 
-static int choose_split(long units, int nks, long target = MOE_SPLIT_TARGET_WG) {
+static int choose_split(long units, int nks, long target = kSplitTargetWG) {
   // Split K (a divisor of the K-step count) only until the launch has about
   // one workgroup per CU: small decode layers then reach every CU, while
   // larger ones avoid the partial-sum round trip through memory, which costs
   // more than the tail of a half-filled last round.  Each workgroup keeps at
-  // least MOE_SPLIT_MIN_KSTEPS steps of 128 K.
+  // least kSplitMinKSteps steps of 128 K.
   int best = 1;
   for (int d = 1; d <= nks; ++d) {
     if (nks % d) continue;
-    if (nks / d < MOE_SPLIT_MIN_KSTEPS) break;
+    if (nks / d < kSplitMinKSteps) break;
     best = d;
     if (units * d >= target) break;
   }
@@ -61,7 +47,7 @@ static int choose_ntt(int T, int k, int E) {
   const double groups = std::fmin(double(E), rows);
   if (groups <= 0) return 1;
   const double avg = rows / groups;
-  const double est = avg + MOE_NTT_SIGMAS * std::sqrt(avg) + 1.0;
+  const double est = avg + kNttSigmas * std::sqrt(avg) + 1.0;
   return est <= 16 ? 1 : (est <= 32 ? 2 : 4);
 }
 
@@ -84,12 +70,12 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   // four weight tiles per wave (256-row units) once a pass holds two or more
   // token tiles; with one token tile the smaller units keep more waves busy
   // (measured cold-cache: T = 64 layers 2-8 % faster, T <= 32 1-3 % slower)
-  s.g2_nj = (MOE_G2_NJ == 4 && H % 256 == 0 && s.g2_ntt >= 2) ? 4 : 2;
+  s.g2_nj = (H % 256 == 0 && s.g2_ntt >= 2) ? 4 : 2;
   s.g2_tiles = H / (64 * s.g2_nj);
   s.g1_items = items_bound(s.rows_cap, s.slots_max, 16 * s.g1_ntt);
   s.g2_items = items_bound(s.rows_cap, s.slots_max, 16 * s.g2_ntt);
   s.g1_split = choose_split(long(s.slots_max) * s.g1_tiles, H / 128);
-  s.g2_split = choose_split(long(s.slots_max) * s.g2_tiles, I / 128, MOE_SPLIT_TARGET_WG2);
+  s.g2_split = choose_split(long(s.slots_max) * s.g2_tiles, I / 128);
   // partial sums are addressed with 32-bit byte offsets: keep them under 2 GiB
   auto fit = [&](int S, int nks, long row_floats) {
     while (S > 1 && 4L * S * s.rows_cap * row_floats >= (1L << 31)) {
@@ -108,7 +94,7 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   const double groups = std::fmin(double(E), double(T) * k);
   const double avg_rows = groups > 0 ? double(T) * k / groups : 0.0;
   // the big-tile kernels keep a pass's token scales in LDS: K <= 8192 for both GEMMs
-  const double min_rows = wfmt == 1 ? MOE_BIG_MIN_AVG_ROWS_FP4 : MOE_BIG_MIN_AVG_ROWS_FP8;
+  const double min_rows = wfmt == 1 ? kBigMinAvgRowsFp4 : kBigMinAvgRowsFp8;
   s.big = (G == 128 && (wfmt == 1 || wblk == 128) && H % 256 == 0 && H <= 8192 && I <= 8192 &&
            avg_rows >= min_rows) ? 1 : 0;
   // 64 rows per pass while nearly every group fits (mean + 3 sd of a

@@ -27,10 +27,7 @@
 namespace moe {
 
 constexpr int kThreads = 256;  // 4 waves per workgroup everywhere
-#ifndef MOE_KSTAGES
-#define MOE_KSTAGES 2
-#endif
-constexpr int kStages = MOE_KSTAGES;  // register stages of the K loop
+constexpr int kStages = 2;  // register stages of the K loop
 
 // =====================================================================
 // route + quant
