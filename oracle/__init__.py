@@ -33,7 +33,7 @@ _lib: Optional[C.CDLL] = None
 
 
 class Cfg(C.Structure):
-    _fields_ = [(n, C.c_int) for n in ("T", "H", "I", "E", "k", "wfmt", "wblk", "G", "has_shared")]
+    _fields_ = [(n, C.c_int) for n in ("T", "H", "I", "E", "k", "wfmt", "wblk", "G", "has_shared", "act_fmt")]
 
 
 class WSet(C.Structure):
@@ -58,6 +58,7 @@ def lib() -> C.CDLL:
         L.oracle_enc_e4m3_array.argtypes = [vp, i64, vp]
         L.oracle_quant_rows_f32.argtypes = [vp, i64, i64, i32, vp, vp]
         L.oracle_quant_act.argtypes = [vp, i64, i64, i32, vp, vp]
+        L.oracle_quant_act_cfg.argtypes = [vp, vp, i64, vp, vp]
         L.oracle_permute.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp]
         L.oracle_gemm1.argtypes = [vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp]
         L.oracle_gemm2.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp]
@@ -155,6 +156,19 @@ def quant_act(x, G: int):
     return xq, xs
 
 
+def quant_act_mx(x):
+    """bf16 [T,H] -> MXFP4 activations: (xq uint8 [T,H/2] packed e2m1, even
+    channel in the low nibble; xs uint8 [T,H/32] e8m0 scale codes)."""
+    x = _np(x)
+    assert x.dtype == np.uint16
+    T, H = x.shape
+    c = Cfg(T, H, 128, 1, 1, 1, 32, 32, 0, 1)
+    xq = np.empty((T, H // 2), np.uint8)
+    xs = np.empty((T, H // 32), np.uint8)
+    lib().oracle_quant_act_cfg(C.byref(c), _p(x), T, _p(xq), _p(xs))
+    return xq, xs
+
+
 def permute(ids, E: int, has_shared: bool):
     """ids int32 [T,k] -> (counts, offsets, expand_idx [T*k], row_token)."""
     ids = _np(ids, np.int32)
@@ -186,9 +200,10 @@ class Layer:
     """Binds a workload's shapes and one set of canonical weights."""
 
     def __init__(self, T: int, H: int, I: int, E: int, k: int, wfmt: int, wblk: int, G: int,
-                 has_shared: bool, weights):
-        self.cfg = Cfg(T, H, I, E, k, wfmt, wblk, G, int(has_shared))
+                 has_shared: bool, weights, act_fmt: int = 0):
+        self.cfg = Cfg(T, H, I, E, k, wfmt, wblk, G, int(has_shared), int(act_fmt))
         self.T, self.H, self.I, self.E, self.k, self.G = T, H, I, E, k, G
+        self.act_fmt = int(act_fmt)
         self.has_shared = bool(has_shared)
         f32 = np.float32 if wfmt == 0 else np.uint8
         self._keep = [
@@ -202,13 +217,20 @@ class Layer:
 
     @classmethod
     def for_workload(cls, wl, T: int, weights) -> "Layer":
-        return cls(T, wl.H, wl.I, wl.E, wl.topk, wl.wfmt, wl.wblk, wl.act_group, wl.shared, weights)
+        return cls(T, wl.H, wl.I, wl.E, wl.topk, wl.wfmt, wl.wblk, wl.act_group, wl.shared, weights,
+                   getattr(wl, "act_fmt", 0))
+
+    def _cb(self, n):   # code bytes of an n-channel quantised row
+        return n // 2 if self.act_fmt == 1 else n
+
+    def _sdt(self, n):  # (scale dtype, scales per n-channel row)
+        return (np.uint8, n // 32) if self.act_fmt == 1 else (np.float32, n // self.G)
 
     def with_T(self, T: int) -> "Layer":
         other = object.__new__(Layer)
         other.__dict__.update(self.__dict__)
         c = self.cfg
-        other.cfg = Cfg(T, c.H, c.I, c.E, c.k, c.wfmt, c.wblk, c.G, c.has_shared)
+        other.cfg = Cfg(T, c.H, c.I, c.E, c.k, c.wfmt, c.wblk, c.G, c.has_shared, c.act_fmt)
         other.T = T
         return other
 
@@ -235,21 +257,24 @@ class Layer:
         return out
 
     def gemm1(self, xq, xs, row_token, offsets, rows: Sequence[int]):
-        """(h fp32 [n,I], hq uint8 [n,I], hs fp32 [n,I/G]) for the listed rows."""
-        xq, xs = _np(xq, np.uint8), _np(xs, np.float32)
+        """(h fp32 [n,I], hq, hs) for the listed rows; hq / hs in the layer's
+        activation format (FP8: uint8 [n,I], fp32 [n,I/G]; MXFP4: uint8
+        [n,I/2], uint8 [n,I/32])."""
+        sdt, _ = self._sdt(self.H)
+        xq, xs = _np(xq, np.uint8), _np(xs, sdt)
         rt, off = _np(row_token, np.int32), _np(offsets, np.int32)
         rr = np.ascontiguousarray(np.asarray(list(rows), np.int64))
         n = len(rr)
         h = np.empty((n, self.I), np.float32)
-        hq = np.empty((n, self.I), np.uint8)
-        hs = np.empty((n, self.I // self.G), np.float32)
+        hq = np.empty((n, self._cb(self.I)), np.uint8)
+        hs = np.empty((n, self._sdt(self.I)[1]), sdt)
         lib().oracle_gemm1(C.byref(self.cfg), C.byref(self.wset), _p(xq), _p(xs), _p(rt), _p(off), n,
                            _p(rr), _p(h), _p(hq), _p(hs))
         return h, hq, hs
 
     def gemm2(self, hq, hs, offsets, rows: Sequence[int]) -> np.ndarray:
         """fp64 y [n,H] for the listed rows (hq/hs indexed by row id)."""
-        hq, hs, off = _np(hq, np.uint8), _np(hs, np.float32), _np(offsets, np.int32)
+        hq, hs, off = _np(hq, np.uint8), _np(hs, self._sdt(self.I)[0]), _np(offsets, np.int32)
         rr = np.ascontiguousarray(np.asarray(list(rows), np.int64))
         y = np.empty((len(rr), self.H), np.float64)
         lib().oracle_gemm2(C.byref(self.cfg), C.byref(self.wset), _p(hq), _p(hs), _p(off), len(rr),

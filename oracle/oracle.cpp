@@ -39,6 +39,14 @@
 //   e2m1: bias 1, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}
 //   e8m0: 2^(c-127), c = 255 is NaN
 //
+// Activation formats (act_fmt): 0 = the FP8 rule above (e4m3 codes, one fp32
+// scale per G channels); 1 = MXFP4 activations, the 4-bit-activation variant
+// the FusedDeepMoE page describes for W4A8 (here e2m1 codes with one e8m0
+// power-of-two scale per 32 channels, by the Microscaling rule: X =
+// 2^(floor(log2 amax) - 2), the largest power of two with amax / X < 8,
+// codes = e2m1(v / X) rounded to nearest even, saturating at 6).  The
+// SwiGLU output is requantised with the same format.
+//
 // Precision: dot products, SwiGLU and the combine in fp64; the quantisers in
 // fp32 (multiplier, product and reciprocal each rounded to fp32), which is
 // the bit-exact contract for activation codes.  Built with -ffp-contract=off.
@@ -127,6 +135,26 @@ void quant_group(const float* v, int G, uint8_t* q, float* s) {
   *s = 1.0f / mult;
 }
 
+// One group of 32 fp32 values -> 32 e2m1 codes (one per byte, sign in bit
+// 3) and the e8m0 code of its scale X = 2^(floor(log2 amax) - 2), clamped to
+// the e8m0 range (amax = 0, or below 2^-125, gives code 0, X = 2^-127).
+// v / X is exact (X is a power of two and |v / X| < 8).
+void quant_group_mx(const float* v, uint8_t* q, uint8_t* s) {
+  float a = 0.0f;
+  for (int i = 0; i < 32; ++i) a = std::max(a, std::fabs(v[i]));
+  int code = 0;
+  if (a > 0.0f) {
+    int e = 0;
+    std::frexp(a, &e);  // a = f * 2^e, f in [0.5, 1): floor(log2 a) = e - 1
+    code = (e - 1) - 2 + 127;
+    if (g_mutation == 9) code += 1;  // planted: scale exponent one too large
+    code = std::min(std::max(code, 0), 254);
+  }
+  const double X = std::ldexp(1.0, code - 127);
+  for (int i = 0; i < 32; ++i) q[i] = enc_e2m1(float(double(v[i]) / X));
+  *s = uint8_t(code);
+}
+
 // ---------------------------------------------------------------- threading
 // Worker count: oracle_set_threads(n) if called, else OMP_NUM_THREADS, else
 // the hardware concurrency capped at 16.
@@ -158,8 +186,42 @@ void parallel_for(int64_t n, F f) {
 
 // ---------------------------------------------------------------- weights
 struct Cfg {
-  int T, H, I, E, k, wfmt, wblk, G, has_shared;
+  int T, H, I, E, k, wfmt, wblk, G, has_shared, act_fmt;
 };
+
+// ---------------------------------------------------------------- activation codec
+// Bytes of one quantised row of `len` channels: codes, then scales.
+int64_t act_code_bytes(const Cfg& c, int64_t len) { return c.act_fmt == 1 ? len / 2 : len; }
+int64_t act_scale_bytes(const Cfg& c, int64_t len) { return c.act_fmt == 1 ? len / 32 : 4 * (len / c.G); }
+
+// Quantise one fp32 row with the cfg's activation format: FP8 per G with fp32
+// scales, or MXFP4 per 32 (two codes per byte, even channel in the low nibble)
+// with e8m0 scales.
+void quant_act_row(const Cfg& c, const float* v, int64_t len, uint8_t* q, uint8_t* s) {
+  if (c.act_fmt == 1) {
+    uint8_t nib[32];
+    for (int64_t g = 0; g < len / 32; ++g) {
+      quant_group_mx(v + g * 32, nib, s + g);
+      for (int i = 0; i < 32; i += 2) q[g * 16 + i / 2] = uint8_t(nib[i] | (nib[i + 1] << 4));
+    }
+    return;
+  }
+  float* sf = reinterpret_cast<float*>(s);
+  for (int64_t g = 0; g < len / c.G; ++g) quant_group(v + g * c.G, c.G, q + g * c.G, sf + g);
+}
+
+// Dequantised row (fp64, exact) of a quantised row.
+void dequant_act_row(const Cfg& c, const uint8_t* q, const uint8_t* s, int64_t len, double* out) {
+  if (c.act_fmt == 1) {
+    for (int64_t i = 0; i < len; ++i) {
+      const uint8_t nib = (i & 1) ? (q[i / 2] >> 4) : (q[i / 2] & 15);
+      out[i] = dec_e2m1(nib) * dec_e8m0(s[i / 32]);
+    }
+    return;
+  }
+  const float* sf = reinterpret_cast<const float*>(s);
+  for (int64_t i = 0; i < len; ++i) out[i] = dec_e4m3(q[i]) * double(sf[i / c.G]);
+}
 
 struct WSet {
   const uint8_t* w1;
@@ -242,10 +304,6 @@ float swiglu(double gate, double up) {
   return float(silu * up);
 }
 
-void dequant_row(const uint8_t* q, const float* s, int64_t len, int G, double* out) {
-  for (int64_t i = 0; i < len; ++i) out[i] = dec_e4m3(q[i]) * double(s[i / G]);
-}
-
 // The listed rows (indices into `rows`) that belong to each group.
 std::vector<std::vector<int64_t>> rows_by_group(const int32_t* offsets, int ng, int64_t nrows, const int64_t* rows) {
   std::vector<std::vector<int64_t>> m(ng);
@@ -267,8 +325,8 @@ int oracle_get_threads() { return default_threads(); }
 // expert, 4 = offsets shifted by one, 5 = the stage combine ignores routing
 // weights, 6 = the stage combine reads token 0's shared row for every token,
 // 7 = the router breaks logit ties towards the higher expert id, 8 = the
-// router's softmax runs over all E logits) so tests can show their pins
-// catch it.
+// router's softmax runs over all E logits, 9 = the MXFP4 activation scale
+// exponent one too large) so tests can show their pins catch it.
 void oracle_set_mutation(int m) { g_mutation = m; }
 
 double oracle_dec_e4m3(int c) { return dec_e4m3(uint8_t(c)); }
@@ -297,6 +355,18 @@ void oracle_quant_act(const uint16_t* x, int64_t T, int64_t H, int G, uint8_t* x
     std::vector<float> row(H);
     for (int64_t i = 0; i < H; ++i) row[i] = bf16_to_f32(x[t * H + i]);
     for (int64_t g = 0; g < H / G; ++g) quant_group(row.data() + g * G, G, xq + t * H + g * G, xs + t * (H / G) + g);
+  });
+}
+
+// bf16 activations [T, H] -> the cfg's activation format: xq codes [T, code
+// bytes of H], xs scales [T, scale bytes of H] (fp32 per G for FP8, e8m0 per
+// 32 for MXFP4)
+void oracle_quant_act_cfg(const Cfg* c, const uint16_t* x, int64_t T, uint8_t* xq, uint8_t* xs) {
+  const int64_t H = c->H, cb = act_code_bytes(*c, H), sb = act_scale_bytes(*c, H);
+  parallel_for(T, [&](int64_t t) {
+    std::vector<float> row(H);
+    for (int64_t i = 0; i < H; ++i) row[i] = bf16_to_f32(x[t * H + i]);
+    quant_act_row(*c, row.data(), H, xq + t * cb, xs + t * sb);
   });
 }
 
@@ -333,9 +403,9 @@ void oracle_permute(const int32_t* ids, int T, int k, int E, int has_shared, int
 }
 
 // Grouped GEMM1 + SwiGLU + requantisation for the listed rows.
-// Inputs: xq [T,H], xs [T,H/G], row_token, offsets (group list).
-// Outputs per listed row i: h [nrows, I] (fp32, before requant),
-// hq [nrows, I] e4m3, hs [nrows, I/G].
+// Inputs: xq / xs (the cfg's activation format, one row per token),
+// row_token, offsets (group list).  Outputs per listed row i: h [nrows, I]
+// (fp32, before requant), hq / hs the requantised row in the same format.
 // For row i of group e and h column n: G_gate = sum over kk of a[kk] *
 // W1[e][n][kk], G_up the same over row I + n, each one fp64 dot product in
 // K order; h = swiglu(G_gate, G_up); then each G consecutive h values of
@@ -343,15 +413,17 @@ void oracle_permute(const int32_t* ids, int T, int k, int E, int has_shared, int
 // tasks of (group, G consecutive h columns): a task dequantises the gate
 // and up weight rows of its columns once and runs them against every
 // listed row of its group (no sum is split or reordered by this).
-void oracle_gemm1(const Cfg* c, const WSet* w, const uint8_t* xq, const float* xs,
+void oracle_gemm1(const Cfg* c, const WSet* w, const uint8_t* xq, const uint8_t* xs,
                   const int32_t* row_token, const int32_t* offsets, int64_t nrows,
-                  const int64_t* rows, float* h, uint8_t* hq, float* hs) {
+                  const int64_t* rows, float* h, uint8_t* hq, uint8_t* hs) {
   const int ng = c->E + (c->has_shared ? 1 : 0);
   const int64_t H = c->H, I = c->I, G = c->G;
+  const int64_t xcb = act_code_bytes(*c, H), xsb = act_scale_bytes(*c, H);
+  const int64_t hcb = act_code_bytes(*c, I), hsb = act_scale_bytes(*c, I);
   std::vector<double> a(std::max<int64_t>(nrows, 1) * H);  // dequantised activation of each listed row
   parallel_for(nrows, [&](int64_t i) {
-    const int t = row_token[rows[i]];
-    dequant_row(xq + int64_t(t) * H, xs + int64_t(t) * (H / G), H, c->G, &a[i * H]);
+    const int64_t t = row_token[rows[i]];
+    dequant_act_row(*c, xq + t * xcb, xs + t * xsb, H, &a[i * H]);
   });
   const auto members = rows_by_group(offsets, ng, nrows, rows);
   const int64_t nch = I / G;
@@ -365,23 +437,25 @@ void oracle_gemm1(const Cfg* c, const WSet* w, const uint8_t* xq, const float* x
     for (const int64_t i : members[e]) {
       float* hr = h + i * I + n0;
       for (int64_t n = 0; n < G; ++n) hr[n] = swiglu(dot(&a[i * H], &wg[n * H], H), dot(&a[i * H], &wu[n * H], H));
-      quant_group(hr, c->G, hq + i * I + n0, hs + i * (I / G) + n0 / G);
+      // this task's G columns are whole quantisation groups (G is the group size)
+      quant_act_row(*c, hr, G, hq + i * hcb + act_code_bytes(*c, n0), hs + i * hsb + act_scale_bytes(*c, n0));
     }
   });
 }
 
-// Grouped GEMM2 for the listed rows: hq [R, I], hs [R, I/G] (indexed by row id)
+// Grouped GEMM2 for the listed rows: hq / hs quantised rows (indexed by row id)
 // -> y [nrows, H] in fp64: y[i][n] = sum over kk of hd[kk] * W2[e][n][kk],
 // one fp64 dot product in K order, hd the row's dequantised codes.  Tasks of
 // (group, 128 output columns) dequantise their weight rows once.
-void oracle_gemm2(const Cfg* c, const WSet* w, const uint8_t* hq, const float* hs,
+void oracle_gemm2(const Cfg* c, const WSet* w, const uint8_t* hq, const uint8_t* hs,
                   const int32_t* offsets, int64_t nrows, const int64_t* rows, double* y) {
   const int ng = c->E + (c->has_shared ? 1 : 0);
-  const int64_t H = c->H, I = c->I, G = c->G;
+  const int64_t H = c->H, I = c->I;
+  const int64_t hcb = act_code_bytes(*c, I), hsb = act_scale_bytes(*c, I);
   std::vector<double> hd(std::max<int64_t>(nrows, 1) * I);
   parallel_for(nrows, [&](int64_t i) {
     const int64_t r = rows[i];
-    dequant_row(hq + r * I, hs + r * (I / G), I, c->G, &hd[i * I]);
+    dequant_act_row(*c, hq + r * hcb, hs + r * hsb, I, &hd[i * I]);
   });
   const auto members = rows_by_group(offsets, ng, nrows, rows);
   constexpr int64_t kCols = 128;  // H is a multiple of 128
@@ -427,10 +501,11 @@ void oracle_combine(const Cfg* c, const float* y, const int32_t* expand_idx,
 // Optional: xq/xs/counts/offsets/expand_idx/row_token outputs (may be NULL).
 void oracle_layer(const Cfg* c, const WSet* w, const uint16_t* x, const int32_t* ids,
                   const float* topk_w, int64_t ntok, const int64_t* toks, double* out) {
-  const int64_t T = c->T, H = c->H, k = c->k;
-  std::vector<uint8_t> xq(T * H);
-  std::vector<float> xs(T * (H / c->G));
-  oracle_quant_act(x, T, H, c->G, xq.data(), xs.data());
+  const int64_t T = c->T, H = c->H, k = c->k, I = c->I;
+  const int64_t xcb = act_code_bytes(*c, H), xsb = act_scale_bytes(*c, H);
+  const int64_t hcb = act_code_bytes(*c, I), hsb = act_scale_bytes(*c, I);
+  std::vector<uint8_t> xq(std::max<int64_t>(T, 1) * xcb), xs(std::max<int64_t>(T, 1) * xsb);
+  oracle_quant_act_cfg(c, x, T, xq.data(), xs.data());
   const int ng = c->E + (c->has_shared ? 1 : 0);
   std::vector<int32_t> counts(ng), offsets(ng + 1), eidx(T * k), rtok(T * k + (c->has_shared ? T : 0));
   oracle_permute(ids, c->T, c->k, c->E, c->has_shared, counts.data(), offsets.data(), eidx.data(),
@@ -445,17 +520,16 @@ void oracle_layer(const Cfg* c, const WSet* w, const uint16_t* x, const int32_t*
   std::sort(rows.begin(), rows.end());
   rows.erase(std::unique(rows.begin(), rows.end()), rows.end());
   const int64_t nr = int64_t(rows.size());
-  std::vector<float> h(nr * c->I), hs_l(nr * (c->I / c->G));
-  std::vector<uint8_t> hq_l(nr * c->I);
+  std::vector<float> h(std::max<int64_t>(nr, 1) * I);
+  std::vector<uint8_t> hq_l(std::max<int64_t>(nr, 1) * hcb), hs_l(std::max<int64_t>(nr, 1) * hsb);
   oracle_gemm1(c, w, xq.data(), xs.data(), rtok.data(), offsets.data(), nr, rows.data(), h.data(),
                hq_l.data(), hs_l.data());
   // scatter the listed rows' codes into row-indexed buffers for GEMM2
   const int64_t Rcap = int64_t(rtok.size());
-  std::vector<uint8_t> hq(std::max<int64_t>(Rcap, 1) * c->I, 0);
-  std::vector<float> hs(std::max<int64_t>(Rcap, 1) * (c->I / c->G), 0.0f);
+  std::vector<uint8_t> hq(std::max<int64_t>(Rcap, 1) * hcb, 0), hs(std::max<int64_t>(Rcap, 1) * hsb, 0);
   for (int64_t i = 0; i < nr; ++i) {
-    std::memcpy(&hq[rows[i] * c->I], &hq_l[i * c->I], c->I);
-    std::memcpy(&hs[rows[i] * (c->I / c->G)], &hs_l[i * (c->I / c->G)], sizeof(float) * (c->I / c->G));
+    std::memcpy(&hq[rows[i] * hcb], &hq_l[i * hcb], hcb);
+    std::memcpy(&hs[rows[i] * hsb], &hs_l[i * hsb], hsb);
   }
   std::vector<double> y_l(nr * H);
   oracle_gemm2(c, w, hq.data(), hs.data(), offsets.data(), nr, rows.data(), y_l.data());
@@ -528,7 +602,7 @@ void oracle_router(const uint16_t* x, const uint16_t* wg, int64_t T, int64_t H, 
 // requantise h with the same rule and add w * y; plus the shared expert.
 void oracle_bruteforce(const Cfg* c, const WSet* w, const uint16_t* x, const int32_t* ids,
                        const float* topk_w, int64_t ntok, const int64_t* toks, double* out) {
-  const int64_t H = c->H, I = c->I, G = c->G;
+  const int64_t H = c->H, I = c->I;
   const int nexp = c->E + (c->has_shared ? 1 : 0);
   // which experts are used by the listed tokens
   std::vector<char> used(nexp, 0);
@@ -553,11 +627,10 @@ void oracle_bruteforce(const Cfg* c, const WSet* w, const uint16_t* x, const int
     // quantise this token (same rule as the activation quantiser)
     std::vector<float> xr(H);
     for (int64_t n = 0; n < H; ++n) xr[n] = bf16_to_f32(x[t * H + n]);
-    std::vector<uint8_t> q(H);
-    std::vector<float> s(H / G);
-    for (int64_t g = 0; g < H / G; ++g) quant_group(&xr[g * G], int(G), &q[g * G], &s[g]);
+    std::vector<uint8_t> q(act_code_bytes(*c, H)), s(act_scale_bytes(*c, H));
+    quant_act_row(*c, xr.data(), H, q.data(), s.data());
     std::vector<double> xd(H);
-    for (int64_t n = 0; n < H; ++n) xd[n] = dec_e4m3(q[n]) * double(s[n / G]);
+    dequant_act_row(*c, q.data(), s.data(), H, xd.data());
     double* o = out + i * H;
     for (int64_t n = 0; n < H; ++n) o[n] = 0.0;
     auto run_expert = [&](int e, double wt) {
@@ -572,11 +645,10 @@ void oracle_bruteforce(const Cfg* c, const WSet* w, const uint16_t* x, const int
         const double gt = gu[n];
         h[n] = float(gt / (1.0 + std::exp(-gt)) * gu[I + n]);
       }
-      std::vector<uint8_t> hq(I);
-      std::vector<float> hs(I / G);
-      for (int64_t g = 0; g < I / G; ++g) quant_group(&h[g * G], int(G), &hq[g * G], &hs[g]);
+      std::vector<uint8_t> hq(act_code_bytes(*c, I)), hs(act_scale_bytes(*c, I));
+      quant_act_row(*c, h.data(), I, hq.data(), hs.data());
       std::vector<double> hd(I);
-      for (int64_t n = 0; n < I; ++n) hd[n] = dec_e4m3(hq[n]) * double(hs[n / G]);
+      dequant_act_row(*c, hq.data(), hs.data(), I, hd.data());
       for (int64_t n = 0; n < H; ++n) {
         double acc = 0.0;
         for (int64_t kk = 0; kk < I; ++kk) acc += W2d[e][n * I + kk] * hd[kk];

@@ -51,6 +51,7 @@ class Workload:
     shared: bool         # one always-on shared expert with weight 1
     tokens: Tuple[int, ...]
     wid: int             # workload id mixed into the seeds
+    act_fmt: int = 0     # 0: FP8 e4m3 activations (fp32 scale per act_group); 1: MXFP4 (e8m0 per 32)
 
     def with_shape(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -76,6 +77,11 @@ WORKLOADS: Dict[str, Workload] = {
     "prefill_mxfp4": Workload("prefill_mxfp4", H=7168, E=256, topk=8, I=2048, wfmt=FMT_MXFP4,
                               wblk=32, act_group=128, routing="uniform", shared=False,
                               tokens=(4096,), wid=4),
+    # the 4-bit-activation variant of the prefill layer: MXFP4 weights and MXFP4
+    # activations (e2m1 with an e8m0 scale per 32 channels), same shapes and routing
+    "prefill_mxfp4_a4": Workload("prefill_mxfp4_a4", H=7168, E=256, topk=8, I=2048, wfmt=FMT_MXFP4,
+                                 wblk=32, act_group=32, routing="uniform", shared=False,
+                                 tokens=(4096,), wid=5, act_fmt=1),
 }
 
 _MASK64 = (1 << 64) - 1
