@@ -17,7 +17,9 @@ Output: one JSON line.  value = aggregate effective weight bandwidth over
 the sweep (touched-expert weight bytes / HIP-event layer time).  After the
 timed decode steps, a "prefill" section measures the MXFP4 layer at T=4096
 (H=7168, E=256, top-8, I=2048): layer latency and TFLOP/s, per-stage times,
-and GEMM1's rate against the MFMA peak of its operand formats.
+and GEMM1's rate against the MFMA peak of its operand formats; "prefill_a4"
+does the same for the layer with MXFP4 activations as well (e2m1 x e2m1
+GEMMs, against the FP4 peak).
 """
 from __future__ import annotations
 
@@ -247,6 +249,8 @@ def main():
         del sweeps, flush
         torch.cuda.empty_cache()
         line["prefill"] = prefill(moe, synth, torch, dev, args.prefill_reps)
+        torch.cuda.empty_cache()
+        line["prefill_a4"] = prefill(moe, synth, torch, dev, args.prefill_reps, "prefill_mxfp4_a4")
     print(json.dumps(line), flush=True)
 
 
@@ -351,10 +355,14 @@ def graph_latencies(moe, torch, sweeps, flush, stream, ev, reps):
     return out
 
 
-def prefill(moe, synth, torch, dev, reps):
-    """The MXFP4 layer at T=4096: its 6 GB of weights exceed every cache, so
-    each call streams them from HBM."""
-    wl = synth.WORKLOADS["prefill_mxfp4"]
+def prefill(moe, synth, torch, dev, reps, name="prefill_mxfp4"):
+    """An MXFP4 layer at T=4096: its 6 GB of weights exceed every cache, so
+    each call streams them from HBM.  prefill_mxfp4 runs e2m1 weights against
+    e4m3 activations (the FP8 MFMA rate); prefill_mxfp4_a4 has e2m1 on both
+    sides (the FP4 rate)."""
+    wl = synth.WORKLOADS[name]
+    a4 = getattr(wl, "act_fmt", 0) == 1
+    peak = FP4_PEAK_TFLOPS if a4 else MFMA_PEAK_TFLOPS
     T = wl.tokens[0]
     w_rm = synth.gen_weights(wl, seed=0, device=dev)
     w = moe.moe_prepack_weights(moe.Cfg.for_workload(wl, 1), w_rm)
@@ -397,18 +405,19 @@ def prefill(moe, synth, torch, dev, reps):
     g1_flops = 2.0 * R * (2 * wl.I) * wl.H
     g1_tf = g1_flops / (stages["gemm1_swiglu"] * 1e-6) / 1e12
     tf = flops / (med * 1e-6) / 1e12
-    meas = mfma_rate_tflops(moe, torch, dev, 1)
+    meas = mfma_rate_tflops(moe, torch, dev, 2 if a4 else 1)
     # floor of the layer on HBM: every weight byte + x in + out, at the peak
     act_bytes = 2 * 2 * T * wl.H
     hbm_floor_us = (wbytes_all + act_bytes) / (HBM_PEAK_GBS * 1e9) * 1e6
+    acts = "MXFP4 activations (e2m1, e8m0 per 32)" if a4 else "e4m3 activations (fp32 scale per 128)"
     return {
-        "workload": f"{wl.name}: H={wl.H} E={wl.E} top-{wl.topk} I={wl.I} MXFP4 weights, T={T}",
+        "workload": f"{wl.name}: H={wl.H} E={wl.E} top-{wl.topk} I={wl.I} MXFP4 weights, {acts}, T={T}",
         "layer_us_median": round(med, 1), "layer_us_p10": round(float(np.percentile(lat_us, 10)), 1),
         "layer_us_p90": round(float(np.percentile(lat_us, 90)), 1),
-        "TFLOPs": round(tf, 1), "mfma_peak_TFLOPs": MFMA_PEAK_TFLOPS, "mfma_frac": round(tf / MFMA_PEAK_TFLOPS, 4),
+        "TFLOPs": round(tf, 1), "mfma_peak_TFLOPs": peak, "mfma_frac": round(tf / peak, 4),
         "weight_GBps": round(wbytes_all / (med * 1e-6) / 1e9, 1),
         "stages_us_median": stages,
-        "gemm1_TFLOPs": round(g1_tf, 1), "gemm1_mfma_frac": round(g1_tf / MFMA_PEAK_TFLOPS, 4),
+        "gemm1_TFLOPs": round(g1_tf, 1), "gemm1_mfma_frac": round(g1_tf / peak, 4),
         "mfma_measured_TFLOPs": round(meas, 1),
         "mfma_frac_of_measured": round(tf / meas, 4), "gemm1_frac_of_measured": round(g1_tf / meas, 4),
         "fp4_peak_frac": round(tf / FP4_PEAK_TFLOPS, 4),

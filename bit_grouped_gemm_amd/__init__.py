@@ -51,7 +51,7 @@ EXPORTS = ("moe_workspace_size", "moe_permute", "moe_grouped_gemm1_swiglu", "moe
 
 class MoeCfg(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("T", "H", "I", "E", "topk", "wfmt", "wblk", "act_group",
-                                          "has_shared")]
+                                          "has_shared", "act_fmt")]
 
 
 class MoeWeights(C.Structure):
@@ -117,14 +117,26 @@ class Cfg:
     wblk: int
     act_group: int
     has_shared: int = 0
+    act_fmt: int = 0  # 0: e4m3 + fp32 scale per act_group; 1: MXFP4 (e2m1 + e8m0 per 32)
 
     def c(self) -> MoeCfg:
         return MoeCfg(self.T, self.H, self.I, self.E, self.topk, self.wfmt, self.wblk, self.act_group,
-                      self.has_shared)
+                      self.has_shared, self.act_fmt)
 
     @classmethod
     def for_workload(cls, wl, T: int) -> "Cfg":
-        return cls(T, wl.H, wl.I, wl.E, wl.topk, wl.wfmt, wl.wblk, wl.act_group, int(wl.shared))
+        return cls(T, wl.H, wl.I, wl.E, wl.topk, wl.wfmt, wl.wblk, wl.act_group, int(wl.shared),
+                   int(getattr(wl, "act_fmt", 0)))
+
+    def act_tensors(self, rows: int, width: int, device) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Empty (codes, scales) of `rows` quantised activation rows of `width`
+        channels: e4m3 [rows][width] + fp32 [rows][width / act_group], or for
+        MXFP4 e2m1 pairs [rows][width / 2] + e8m0 [rows][width / 32]."""
+        if self.act_fmt == 1:
+            return (torch.empty(rows, width // 2, dtype=torch.uint8, device=device),
+                    torch.empty(rows, width // 32, dtype=torch.uint8, device=device))
+        return (torch.empty(rows, width, dtype=torch.uint8, device=device),
+                torch.empty(rows, width // self.act_group, dtype=torch.float32, device=device))
 
     def with_T(self, T: int) -> "Cfg":
         return dataclasses.replace(self, T=T)
@@ -180,8 +192,7 @@ def moe_permute(cfg: Cfg, x: torch.Tensor, topk_ids: torch.Tensor, ws: Optional[
     offsets = torch.empty(E + 1 + sh, dtype=torch.int32, device=dev)
     eidx = torch.empty(T * k, dtype=torch.int32, device=dev)
     rtok = torch.empty(T * k + T * sh, dtype=torch.int32, device=dev)
-    xq = torch.empty(T, cfg.H, dtype=torch.uint8, device=dev)
-    xs = torch.empty(T, cfg.H // cfg.act_group, dtype=torch.float32, device=dev)
+    xq, xs = cfg.act_tensors(T, cfg.H, dev)
     c = cfg.c()
     ws = workspace(cfg, dev) if ws is None else ws  # per-chunk counts when T*topk > 4096
     _check("moe_permute", load().moe_permute(C.byref(c), _ptr(_u16(x)), _ptr(topk_ids), _ptr(counts),
@@ -194,8 +205,7 @@ def moe_grouped_gemm1_swiglu(cfg: Cfg, xq, xs, row_token, offsets, weights, ws: 
                              rows: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     dev = xq.device
     R = rows if rows is not None else cfg.T * cfg.topk + cfg.T * cfg.has_shared
-    hq = torch.empty(R, cfg.I, dtype=torch.uint8, device=dev)
-    hs = torch.empty(R, cfg.I // cfg.act_group, dtype=torch.float32, device=dev)
+    hq, hs = cfg.act_tensors(R, cfg.I, dev)
     ws = workspace(cfg, dev) if ws is None else ws
     c, w = cfg.c(), weights_struct(weights)
     _check("moe_grouped_gemm1_swiglu",

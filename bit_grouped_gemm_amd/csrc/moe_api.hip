@@ -59,9 +59,10 @@ static int items_bound(long N, long Gn, int R) {
   return int(std::min(N, (N + Gn * (R - 1)) / R));
 }
 
-Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, int shared) {
+Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, int shared, int af) {
   Shape s{};
   s.T = T; s.H = H; s.I = I; s.E = E; s.k = k; s.wfmt = wfmt; s.wblk = wblk; s.G = G; s.shared = shared;
+  s.af = af;
   s.ngroups = E + shared;
   s.rows_cap = T * k + T * shared;
   s.slots_max = (T > 0) ? (std::min(E, T * k) + shared) : 0;
@@ -97,6 +98,7 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   const double min_rows = wfmt == 1 ? kBigMinAvgRowsFp4 : kBigMinAvgRowsFp8;
   s.big = (G == 128 && (wfmt == 1 || wblk == 128) && H % 256 == 0 && H <= 8192 && I <= 8192 &&
            avg_rows >= min_rows) ? 1 : 0;
+  if (af == 1) s.big = 1;  // 4-bit activations run the many-row kernels at every T
   // 64 rows per pass while nearly every group fits (mean + 3 sd of a
   // Poisson count), which leaves LDS for a deeper ring; 160 beyond
   s.big_cap = avg_rows + 3.0 * std::sqrt(avg_rows) + 1.0 <= 64.0 ? 64 : 160;
@@ -174,15 +176,24 @@ int check_shape(const moe_cfg* c) {
     if (c->act_group != c->wblk) return MOE_ERR_BAD_SHAPE;
   } else if (c->wfmt == MOE_WFMT_MXFP4) {
     if (c->wblk != 32) return MOE_ERR_BAD_SHAPE;
-    if (c->act_group != 128) return MOE_ERR_UNSUPPORTED;
+    if (c->act_fmt == MOE_AFMT_FP8 && c->act_group != 128) return MOE_ERR_UNSUPPORTED;
   } else {
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (c->act_fmt == MOE_AFMT_MXFP4) {
+    // 4-bit activations: MXFP4 weights, one e8m0 scale per 32 channels, and
+    // the many-row kernels (their token-scale table holds K <= 8192)
+    if (c->wfmt != MOE_WFMT_MXFP4) return MOE_ERR_UNSUPPORTED;
+    if (c->act_group != 32) return MOE_ERR_BAD_SHAPE;
+    if (c->H % 256 || c->H > 8192 || c->I > 8192) return MOE_ERR_UNSUPPORTED;
+  } else if (c->act_fmt != MOE_AFMT_FP8) {
     return MOE_ERR_UNSUPPORTED;
   }
   return MOE_OK;
 }
 
 Shape shape_of(const moe_cfg* c) {
-  return make_shape(c->T, c->H, c->I, c->E, c->topk, c->wfmt, c->wblk, c->act_group, c->has_shared);
+  return make_shape(c->T, c->H, c->I, c->E, c->topk, c->wfmt, c->wblk, c->act_group, c->has_shared, c->act_fmt);
 }
 
 // Argument checks of the layer entry points, in the order include/moe.h
@@ -462,7 +473,7 @@ int moe_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes
 int moe_mfma_rate(int wfmt, int iters, void* sink, size_t sink_bytes, double* flops, void* stream) {
   if (!sink) return MOE_ERR_NULL_ARG;
   if (misaligned(sink)) return MOE_ERR_MISALIGNED;
-  if (wfmt != MOE_WFMT_FP8_BLOCK && wfmt != MOE_WFMT_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (wfmt != MOE_WFMT_FP8_BLOCK && wfmt != MOE_WFMT_MXFP4 && wfmt != MOE_RATE_E2M1_E2M1) return MOE_ERR_UNSUPPORTED;
   if (iters < 1 || iters > 65536) return MOE_ERR_BAD_SHAPE;
   if (sink_bytes < 4 * size_t(mfma_rate_grid())) return MOE_ERR_WORKSPACE;
   return hip_status(launch_mfma_rate(wfmt, iters, static_cast<float*>(sink), flops, static_cast<hipStream_t>(stream)));

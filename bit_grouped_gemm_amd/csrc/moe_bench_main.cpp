@@ -11,7 +11,8 @@
 //     three device-to-device copies of MIB MiB (the runtime's copy kernel):
 //     a transfer of known size, to scale a profiler's byte counters by
 //   moe_bench WORKLOAD T REPS [stages]
-//     WORKLOAD  decode_fp8 | decode_mxfp4 | decode_fp8_zipf_shared | prefill_mxfp4
+//     WORKLOAD  decode_fp8 | decode_mxfp4 | decode_fp8_zipf_shared | prefill_mxfp4 |
+//               prefill_mxfp4_a4
 //               (the shapes of the Python workloads of the same names)
 //     T         tokens; REPS timed moe_layer calls (after one untimed call)
 //     stages    also time REPS passes of the four stage calls
@@ -37,14 +38,15 @@ namespace {
 
 struct Shape {
   const char* name;
-  int H, E, k, I, wfmt, wblk, G, shared, zipf;
+  int H, E, k, I, wfmt, wblk, G, shared, zipf, af;
 };
 
 const Shape kShapes[] = {
-    {"decode_fp8", 4096, 64, 8, 1536, MOE_WFMT_FP8_BLOCK, 128, 128, 0, 0},
-    {"decode_mxfp4", 4096, 64, 8, 1536, MOE_WFMT_MXFP4, 32, 128, 0, 0},
-    {"decode_fp8_zipf_shared", 7168, 256, 8, 2048, MOE_WFMT_FP8_BLOCK, 128, 128, 1, 1},
-    {"prefill_mxfp4", 7168, 256, 8, 2048, MOE_WFMT_MXFP4, 32, 128, 0, 0},
+    {"decode_fp8", 4096, 64, 8, 1536, MOE_WFMT_FP8_BLOCK, 128, 128, 0, 0, MOE_AFMT_FP8},
+    {"decode_mxfp4", 4096, 64, 8, 1536, MOE_WFMT_MXFP4, 32, 128, 0, 0, MOE_AFMT_FP8},
+    {"decode_fp8_zipf_shared", 7168, 256, 8, 2048, MOE_WFMT_FP8_BLOCK, 128, 128, 1, 1, MOE_AFMT_FP8},
+    {"prefill_mxfp4", 7168, 256, 8, 2048, MOE_WFMT_MXFP4, 32, 128, 0, 0, MOE_AFMT_FP8},
+    {"prefill_mxfp4_a4", 7168, 256, 8, 2048, MOE_WFMT_MXFP4, 32, 32, 0, 0, MOE_AFMT_MXFP4},
 };
 
 uint64_t splitmix64(uint64_t& s) {
@@ -154,7 +156,7 @@ int main(int argc, char** argv) {
   const int T = std::atoi(argv[2]), reps = std::atoi(argv[3]);
   const bool stages = argc > 4 && std::string(argv[4]) == "stages";
   if (T < 0 || reps < 1) return 2;
-  moe_cfg cfg{T, s.H, s.I, s.E, s.k, s.wfmt, s.wblk, s.G, s.shared};
+  moe_cfg cfg{T, s.H, s.I, s.E, s.k, s.wfmt, s.wblk, s.G, s.shared, s.af};
 
   // ---- inputs on the host
   uint64_t st = 0x5EEDull + uint64_t(T);

@@ -67,6 +67,32 @@ __device__ __forceinline__ uint32_t enc_e4m3x4(float a, float b, float c, float 
 // h value does not depend on which kernel its group's row count selects.
 __device__ __forceinline__ float swiglu(float gate, float up) { return gate / (1.0f + expf(-gate)) * up; }
 
+// MXFP4 (Microscaling FP4): e8m0 code of the scale X = 2^(floor(log2 amax)
+// - 2) of a group with absolute maximum amax, clamped to the e8m0 range.  For
+// a normal amax floor(log2 amax) is its exponent field minus 127, so the
+// code is that field minus 2; subnormal and zero maxima (field 0) and field
+// 1 clamp to code 0 (X = 2^-127).
+__device__ __forceinline__ uint32_t mx_scale_code(float amax) {
+  const uint32_t ex = __float_as_uint(amax) >> 23;  // amax >= 0: the exponent field
+  return ex >= 2u ? ex - 2u : 0u;
+}
+
+// 1 / X = 2^(127 - code) as an fp32 (biased exponent 254 - code, always
+// normal for code <= 252); x * (1 / X) is exact.
+__device__ __forceinline__ float mx_inv_scale(uint32_t code) { return __uint_as_float((254u - code) << 23); }
+
+// fp32 -> e2m1 code (sign in bit 3): round to nearest, ties to even, |v| >= 6
+// saturates to 6.  The magnitude code counts the rounding boundaries below
+// |v|; at a boundary that lies halfway, the comparison's strictness sends it
+// to the even code (0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2.0,
+// 2.5 -> 2.0, 3.5 -> 4.0, 5.0 -> 4.0).
+__device__ __forceinline__ uint32_t enc_e2m1(float v) {
+  const float a = fabsf(v);
+  const uint32_t m = uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) + uint32_t(a >= 1.75f) +
+                     uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) + uint32_t(a > 5.0f);
+  return m | ((__float_as_uint(v) >> 28) & 8u);
+}
+
 // Quantisation multiplier and dequant scale of a group with absolute max a.
 __device__ __forceinline__ float quant_mult(float amax) { return 448.0f / fmaxf(amax, 0x1p-64f); }
 

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_read(const v4u* __res
 // 4 * 128 * kRateAcc * iters (exact in fp32 for iters <= 65536).
 constexpr int kRateAcc = 3;
 
-template <int FA>
+template <int FA, int FB>
 __global__ __launch_bounds__(kStreamThreads) void k_mfma_rate(uint32_t a_word, uint32_t b_word, int iters,
                                                              float* __restrict__ sink) {
   const int aw = int(a_word), bw = int(b_word);
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_mfma_rate(uint32_t a_word, u
   for (int j = 0; j < kRateAcc; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
-    for (int j = 0; j < kRateAcc; ++j) acc[j] = mfma_scaled_acc<FA, kFmtE4M3>(a, b, acc[j], kUnitScale, kUnitScale);
+    for (int j = 0; j < kRateAcc; ++j) acc[j] = mfma_scaled_acc<FA, FB>(a, b, acc[j], kUnitScale, kUnitScale);
   }
   if (threadIdx.x == 0) {
     float t = 0.0f;
@@ -112,12 +112,16 @@ int mfma_rate_grid() { return stream_read_grid(); }
 hipError_t launch_mfma_rate(int wfmt, int iters, float* sink, double* flops, hipStream_t st) {
   const int grid = mfma_rate_grid();
   if (flops) *flops = double(grid) * (kStreamThreads / kWave) * double(iters) * kRateAcc * (16.0 * 16.0 * 128.0 * 2.0);
-  if (wfmt == 0)  // e4m3 1.0 = 0x38 in every byte
-    hipLaunchKernelGGL(k_mfma_rate<kFmtE4M3>, dim3(unsigned(grid)), dim3(kStreamThreads), 0, st, 0x38383838u,
-                       0x38383838u, iters, sink);
-  else  // e2m1 1.0 = 0x2 in every nibble
-    hipLaunchKernelGGL(k_mfma_rate<kFmtE2M1>, dim3(unsigned(grid)), dim3(kStreamThreads), 0, st, 0x22222222u,
-                       0x38383838u, iters, sink);
+  // operands of 1.0: e4m3 0x38 in every byte, e2m1 0x2 in every nibble
+  if (wfmt == 0)
+    hipLaunchKernelGGL((k_mfma_rate<kFmtE4M3, kFmtE4M3>), dim3(unsigned(grid)), dim3(kStreamThreads), 0, st,
+                       0x38383838u, 0x38383838u, iters, sink);
+  else if (wfmt == 1)
+    hipLaunchKernelGGL((k_mfma_rate<kFmtE2M1, kFmtE4M3>), dim3(unsigned(grid)), dim3(kStreamThreads), 0, st,
+                       0x22222222u, 0x38383838u, iters, sink);
+  else
+    hipLaunchKernelGGL((k_mfma_rate<kFmtE2M1, kFmtE2M1>), dim3(unsigned(grid)), dim3(kStreamThreads), 0, st,
+                       0x22222222u, 0x22222222u, iters, sink);
   return hipGetLastError();
 }
 

@@ -35,6 +35,11 @@
 // GEMM1 mode: weight rows are 128 gate + 128 up rows (128 h columns = one
 // requantisation group of 128), epilogue SwiGLU + FP8 requantisation.
 // GEMM2 mode: 256 output rows, epilogue writes y.
+// 4-bit activations (AF = 1, MXFP4 weights only): token rows are 64 bytes per
+// K step (e2m1, two per byte) and their scales e8m0 per 32 channels, so the
+// token operand's scale goes into the MFMA's B-operand scale like the
+// weights' and the accumulators need no per-step rescale; GEMM1's epilogue
+// requantises each wave row's 32 h columns (one MXFP4 group) to e2m1 + e8m0.
 #include <algorithm>
 #include <type_traits>
 
@@ -58,15 +63,16 @@ constexpr int kXsRow = kMaxKSteps + 1;  // floats per table row (odd: conflict-f
 // (token rows, weight tiles, MXFP4 scales; spare slots load one hot line
 // into the stage's sink).  A pass's token scales, [token][k step], and the
 // unit's two e4m3 block-scale rows are read once per pass into tables.
-template <int WF, int CAP> struct BigGeo {
+template <int WF, int CAP, int AF> struct BigGeo {
   static constexpr int kTokTiles = CAP / 16;
   static constexpr int kTokPerWave = kTokTiles / 2;          // token tiles of one wave column
-  static constexpr int kTokLoads = 2 * kTokTiles;            // 8 rows x 128 B each
+  static constexpr int kTokTileBytes = AF ? 1024 : 2048;     // 16 rows x 64 B (e2m1) or 128 B (e4m3)
+  static constexpr int kTokLoads = AF ? kTokTiles : 2 * kTokTiles;  // 1 KB each: 16 x 64 B or 8 x 128 B
   static constexpr int kTokSlots = (kTokLoads + 7) / 8;      // token-row loads of one wave
   static constexpr int kWLoads = WF == 1 ? kWTiles : 2 * kWTiles;  // 1 KB each
   static constexpr int kScLoads = WF == 1 ? 1 : 0;           // 16 tiles x 64 B of e8m0 scales
   static constexpr int kL = (kTokLoads + kWLoads + kScLoads + 7) / 8;
-  static constexpr int kWOff = kTokTiles * 2048;             // token tiles: 16 rows x 128 B, chunk-swizzled
+  static constexpr int kWOff = kTokTiles * kTokTileBytes;    // token tiles, chunk-swizzled
   static constexpr int kScOff = kWOff + kWLoads * 1024;
   static constexpr int kSinkOff = kScOff + kScLoads * 1024;
   static constexpr int kStageBytes = kSinkOff + 1024;
@@ -130,6 +136,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // while a direct-to-LDS load still covers 8 whole rows (full cache lines)
 __device__ __forceinline__ int tok_swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
 
+// the same for a 1 KB tile of 64-byte rows (e2m1 tokens, chunks 0..3): the
+// chunk index is XOR-ed with (r / 4) & 3, which puts the 16 rows' chunk-c
+// reads on distinct banks; one direct-to-LDS load covers the whole tile
+__device__ __forceinline__ int tok_swz4(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
 // instruction classes the scheduler may move across a load-issue point (the
 // sched_barrier mask): ALU, VALU, SALU, MFMA, LDS reads, transcendentals --
 // not the vector-memory loads themselves
@@ -148,9 +159,10 @@ __device__ __forceinline__ void lds_barrier() {
 
 }  // namespace
 
-template <int WF, int MODE, int CAP>
+template <int WF, int MODE, int CAP, int AF>
 __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
-  using Geo = BigGeo<WF, CAP>;
+  static_assert(AF == 0 || WF == 1, "4-bit activations run with MXFP4 weights");
+  using Geo = BigGeo<WF, CAP, AF>;
   constexpr int S = Geo::kStages, L = Geo::kL, NTMAX = Geo::kTokPerWave;
   // one array per ring stage: the compiler's alias analysis then tells the
   // stages apart and waits for a stage's own direct-to-LDS loads only
@@ -171,6 +183,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
   const int K = MODE == 0 ? H : I;       // reduction length
   const int NR = MODE == 0 ? 2 * I : H;  // weight rows of the matrix
   const int kb = WF == 0 ? K : K / 2;    // bytes per weight row
+  const int ka = AF ? K / 2 : K;         // bytes per token row
   const int nks = K / 128;
   const long wstep = long(NR / 16) * kTileBytes<WF>;  // tiled weights: bytes per K step
   const long sstep = long(NR / 16) * kTileScaleBytes;
@@ -234,7 +247,10 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
   // row 8 (i % 2) + l / 8); the wave's token-scale table rows are tokens
   // w + 8 i (lane i holds the row of the i-th); rows past the pass repeat
   // its last row
-  auto tok_of_slot = [&](int j) __attribute__((always_inline)) { const int i = w + 8 * j; return (i >> 1) * 16 + (i & 1) * 8 + (lane >> 3); };
+  auto tok_of_slot = [&](int j) __attribute__((always_inline)) {
+    const int i = w + 8 * j;
+    return AF ? i * 16 + (lane >> 2) : (i >> 1) * 16 + (i & 1) * 8 + (lane >> 3);
+  };
   int pf_row[Geo::kTokSlots], pf_tab = 0;  // rows of the next pass to load (GEMM1: token ids)
   bool pf_ok = false;
   auto prefetch = [&](int4 ent, int pass) __attribute__((always_inline)) {
@@ -286,10 +302,18 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
     for (int j = 0; j < L; ++j) {
       const int i = w + 8 * j;
       if (i < Geo::kTokLoads) {
-        // lane l fills LDS chunk l % 8 of its row, i.e. global chunk (l % 8) ^ (row & 7)
-        const int rl = (i & 1) * 8 + (lane >> 3);
-        src16[j] = p.act + long(pf_row[j < Geo::kTokSlots ? j : 0]) * K + (((lane & 7) ^ (rl & 7)) << 4);
-        stride16[j] = 128;
+        const long trow = pf_row[j < Geo::kTokSlots ? j : 0];
+        if (AF) {
+          // lane l fills LDS chunk l % 4 of tile row l / 4, i.e. global chunk (l % 4) ^ ((row / 4) & 3)
+          const int rl = lane >> 2;
+          src16[j] = p.act + trow * ka + (((lane & 3) ^ ((rl >> 2) & 3)) << 4);
+          stride16[j] = 64;
+        } else {
+          // lane l fills LDS chunk l % 8 of its row, i.e. global chunk (l % 8) ^ (row & 7)
+          const int rl = (i & 1) * 8 + (lane >> 3);
+          src16[j] = p.act + trow * ka + (((lane & 7) ^ (rl & 7)) << 4);
+          stride16[j] = 128;
+        }
         dst16[j] = i * 1024;
       } else if (i < Geo::kTokLoads + Geo::kWLoads) {
         const int wi = i - Geo::kTokLoads;
@@ -397,7 +421,39 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
   uint8_t* const ebuf = stage_ptr(S - 1);
   int c_row = 0, c_npass = 0, c_n0 = 0, c_ntw = 0;
   auto epi1 = [&]() __attribute__((always_inline)) {
-    if (MODE == 0) {
+    if (MODE == 0 && AF) {
+      // 4-bit activations: the wave row's 32 h columns of a token are one
+      // MXFP4 group, so its maximum is a reduction over the wave alone; codes
+      // go to the buffer row of the token (64 bytes per unit), the e8m0 scale
+      // straight to hs
+      uint8_t* const hs8 = reinterpret_cast<uint8_t*>(p.hs);
+#pragma unroll
+      for (int tt = 0; tt < NTMAX; ++tt) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = swiglu(acc[q][tt][i], acc[q + 2][tt][i]);
+            acc[q][tt][i] = v;
+            amax = fmaxf(amax, fabsf(v));
+          }
+        amax = wave_max_xor(amax, 16);
+        amax = wave_max_xor(amax, 32);
+        if (tt >= c_ntw) continue;
+        const int idx = (2 * tt + wc) * 16 + m;
+        const uint32_t code = mx_scale_code(amax);
+        const float inv = mx_inv_scale(code);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const v4f& hv = acc[q][tt];
+          const uint32_t nib = enc_e2m1(hv[0] * inv) | (enc_e2m1(hv[1] * inv) << 4) |
+                               (enc_e2m1(hv[2] * inv) << 8) | (enc_e2m1(hv[3] * inv) << 12);
+          *reinterpret_cast<uint16_t*>(ebuf + idx * kEPitch + 16 * wr + 8 * q + 2 * g) = uint16_t(nib);
+        }
+        if (g == 0 && idx < c_npass) hs8[long(c_row + idx) * (I / 32) + c_n0 / 32 + wr] = uint8_t(code);
+      }
+    } else if (MODE == 0) {
 #pragma unroll
       for (int tt = 0; tt < NTMAX; ++tt) {
         if (WF == 1)
@@ -428,7 +484,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
         const int t0 = (2 * tt + wc) * 16;
         v4f v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = WF == 1 ? acc[q][tt] * xsp[tt] : acc[q][tt];
+        for (int q = 0; q < 4; ++q) v[q] = (WF == 1 && !AF) ? acc[q][tt] * xsp[tt] : acc[q][tt];
         if (p.yb) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -464,6 +520,14 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
   };
   auto epi2 = [&]() __attribute__((always_inline)) {
     if (MODE != 0) return;
+    if (AF) {  // the codes are in the buffer (epi1): 64 bytes per token
+      for (int c = tid; c < c_npass * 4; c += kBigThreads) {
+        const int row = c >> 2, part = c & 3;
+        *reinterpret_cast<v4u*>(p.hq + long(c_row + row) * (I / 2) + c_n0 / 2 + part * 16) =
+            *reinterpret_cast<const v4u*>(ebuf + row * kEPitch + part * 16);
+      }
+      return;
+    }
     // codes of the pass's tokens: [token][128 h columns] in the buffer
 #pragma unroll
     for (int tt = 0; tt < NTMAX; ++tt) {
@@ -547,11 +611,19 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
       for (int tt = 0; tt < NT; ++tt) {
         const int t = 2 * tt + wc;
         xsv[tt] = xs_tab[(t * 16 + m) * kXsRow + k];
-        const v4u lo = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, g));
-        const v4u hi = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, 4 + g));
-        bf[tt] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+        if (AF) {
+          // e2m1 tokens: 16 bytes (32 K) per lane; the step's four e8m0 scales
+          // of the token are one table word, byte g the scale of lane group g
+          const v4u b = *reinterpret_cast<const v4u*>(st + t * 1024 + tok_swz4(m, g));
+          bf[tt] = v8i{int(b[0]), int(b[1]), int(b[2]), int(b[3]), 0, 0, 0, 0};
+          sb[tt] = int((__float_as_uint(xsv[tt]) >> (8 * g)) & 0xFFu);
+        } else {
+          const v4u lo = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, g));
+          const v4u hi = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, 4 + g));
+          bf[tt] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+        }
       }
-      if (WF == 1) {
+      if (WF == 1 && !AF) {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
           // xs = mantissa * 2^(e - 127): the biased exponent field is the
@@ -572,7 +644,11 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
       const bool go = kn < nks;
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
-        if (WF == 1) {
+        if (AF) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[q][tt] = mfma_scaled_acc<kFmtE2M1, kFmtE2M1>(af[q], bf[tt], acc[q][tt], sa[q], sb[tt]);
+        } else if (WF == 1) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             acc[q][tt] = mfma_scaled_acc<kFmtE2M1, kFmtE4M3>(af[q], bf[tt], acc[q][tt], sa[q], sb[tt]);
@@ -699,17 +775,20 @@ static hipError_t launch_big(const Shape& s, int mode, BigParams& p, hipStream_t
   const int nwx = std::max(1, std::min(ncu / 8, p.per_xcd));
   const unsigned grid = unsigned(nwx) * 8;
   const size_t lds = 0;  // static LDS
-#define MOE_BIG_LAUNCH(WF, CAP)                                                                   \
-  do {                                                                                            \
-    if (mode == 0) hipLaunchKernelGGL((k_gemm_big<WF, 0, CAP>), dim3(grid), dim3(kBigThreads), lds, st, p); \
-    else hipLaunchKernelGGL((k_gemm_big<WF, 1, CAP>), dim3(grid), dim3(kBigThreads), lds, st, p);           \
+#define MOE_BIG_LAUNCH(WF, CAP, AF)                                                                   \
+  do {                                                                                                \
+    if (mode == 0) hipLaunchKernelGGL((k_gemm_big<WF, 0, CAP, AF>), dim3(grid), dim3(kBigThreads), lds, st, p); \
+    else hipLaunchKernelGGL((k_gemm_big<WF, 1, CAP, AF>), dim3(grid), dim3(kBigThreads), lds, st, p);           \
   } while (0)
-  if (s.wfmt == 0) {
-    if (s.big_cap == 64) MOE_BIG_LAUNCH(0, 64);
-    else MOE_BIG_LAUNCH(0, 160);
+  if (s.af == 1) {
+    if (s.big_cap == 64) MOE_BIG_LAUNCH(1, 64, 1);
+    else MOE_BIG_LAUNCH(1, 160, 1);
+  } else if (s.wfmt == 0) {
+    if (s.big_cap == 64) MOE_BIG_LAUNCH(0, 64, 0);
+    else MOE_BIG_LAUNCH(0, 160, 0);
   } else {
-    if (s.big_cap == 64) MOE_BIG_LAUNCH(1, 64);
-    else MOE_BIG_LAUNCH(1, 160);
+    if (s.big_cap == 64) MOE_BIG_LAUNCH(1, 64, 0);
+    else MOE_BIG_LAUNCH(1, 160, 0);
   }
 #undef MOE_BIG_LAUNCH
   return hipGetLastError();

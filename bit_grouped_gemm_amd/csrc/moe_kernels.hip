@@ -41,11 +41,13 @@ struct RouteParams {
   int32_t* row_token;
   uint8_t* xq;
   float* xs;
+  uint8_t* xq_scale8;  // MXFP4 activations: the e8m0 scales, [T][H/32] (aliases xs)
   int32_t* clear;
   int nclear;
   int32_t* chunk_cnt;  // chunked mode: per-chunk expert counts [nchunks][E]
   int chunk, nchunks;  // slots per chunk; nchunks == 1: one block places every slot
   int T, H, k, E, G, shared;
+  int af;              // 1: MXFP4 activations (e2m1 codes, e8m0 per 32) instead of e4m3 per G
 };
 
 // Place slots [c0, c1) (chunk b of nb): expert histogram of the chunk, the
@@ -212,6 +214,19 @@ __device__ void quant_block(const RouteParams& p, int blk) {
   }
   const int lanes = p.G / 8;  // 4 or 16, a power of two dividing 64
   for (int msk = 1; msk < lanes; msk <<= 1) amax = wave_max_xor(amax, msk);
+  if (p.af == 1) {
+    // MXFP4: one e8m0 scale per 32 channels (4 lanes), 8 e2m1 codes per thread
+    if (item < items) {
+      const uint32_t code = mx_scale_code(amax);
+      const float inv = mx_inv_scale(code);
+      uint32_t word = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) word |= enc_e2m1(f[q] * inv) << (4 * q);
+      *reinterpret_cast<uint32_t*>(p.xq + long(t) * (p.H / 2) + c0 / 2) = word;
+      if ((tid & 3) == 0) p.xq_scale8[long(t) * (p.H / 32) + c0 / 32] = uint8_t(code);
+    }
+    return;
+  }
   if (item < items) {
     const float mult = quant_mult(amax);
     const uint32_t lo = enc_e4m3x4(f[0] * mult, f[1] * mult, f[2] * mult, f[3] * mult);
@@ -818,8 +833,8 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineParams p) {
 hipError_t launch_route_quant(const Shape& s, const uint16_t* x, const int32_t* ids, int32_t* counts,
                               int32_t* offsets, int32_t* expand_idx, int32_t* row_token, uint8_t* xq,
                               float* xs, int32_t* clear, int nclear, int32_t* chunk_cnt, hipStream_t st) {
-  RouteParams p{x, ids, counts, offsets, expand_idx, row_token, xq, xs, clear, nclear,
-                chunk_cnt, s.perm_chunk, s.perm_chunks, s.T, s.H, s.k, s.E, s.G, s.shared};
+  RouteParams p{x, ids, counts, offsets, expand_idx, row_token, xq, xs, reinterpret_cast<uint8_t*>(xs), clear, nclear,
+                chunk_cnt, s.perm_chunk, s.perm_chunks, s.T, s.H, s.k, s.E, s.G, s.shared, s.af};
   const long items = long(s.T) * (s.H / 8);
   const long nq = (items + kThreads - 1) / kThreads;
   const int nlead = s.perm_chunks == 1 ? 1 : s.perm_chunks;

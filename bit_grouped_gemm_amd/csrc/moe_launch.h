@@ -11,6 +11,7 @@ namespace moe {
 // Shape facts derived once on the host from a validated moe_cfg.
 struct Shape {
   int T, H, I, E, k, wfmt, wblk, G, shared;
+  int af;           // activation format: 0 e4m3 + fp32 scale per G, 1 MXFP4 (e2m1 + e8m0 per 32)
   int ngroups;      // E + shared
   int rows_cap;     // T*k + T*shared: upper bound on permuted rows
   int slots_max;    // upper bound on non-empty groups: min(E, T*k) + shared
@@ -44,7 +45,7 @@ struct WsLayout {
   size_t total;
 };
 
-Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, int shared);
+Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, int shared, int af);
 WsLayout make_ws_layout(const Shape& s);
 
 struct WeightPtrs {

@@ -64,6 +64,7 @@ enum {
 };
 
 enum { MOE_WFMT_FP8_BLOCK = 0, MOE_WFMT_MXFP4 = 1 };
+enum { MOE_AFMT_FP8 = 0, MOE_AFMT_MXFP4 = 1 };
 
 /* Layer shape (host struct).
  *   T tokens on this GPU, H hidden size, I expert FFN width, E local experts,
@@ -76,6 +77,20 @@ enum { MOE_WFMT_FP8_BLOCK = 0, MOE_WFMT_MXFP4 = 1 };
  *   has_shared = 1 adds one always-on shared expert (same format and I) to
  *   every token with weight 1 (GC-MoE abstract: shared experts as an
  *   option; FusedDeepMoE shared-expert path: all tokens in one group).
+ *   act_fmt = MOE_AFMT_FP8: activations and the requantised SwiGLU output
+ *          are e4m3 with one fp32 scale per act_group channels (the rule
+ *          below).
+ *   act_fmt = MOE_AFMT_MXFP4: the 4-bit-activation variant (the W4A8 family
+ *          member of the FusedDeepMoE analysis, with Microscaling FP4 in
+ *          place of int4): e2m1 codes packed two per byte (even channel in
+ *          the low nibble) with one e8m0 scale per 32 channels, X =
+ *          2^(floor(log2 amax) - 2) clamped to the e8m0 range, code =
+ *          e2m1(x / X) round-to-nearest-even saturating at +-6.  Needs
+ *          wfmt = MOE_WFMT_MXFP4 (MOE_ERR_UNSUPPORTED otherwise),
+ *          act_group = 32, H a multiple of 256 and H, I <= 8192
+ *          (MOE_ERR_UNSUPPORTED otherwise).  The scale arrays the stage calls
+ *          take as float* (xs, hs) then hold e8m0 bytes: [T][H/32] and
+ *          [rows][I/32]; the code arrays xq, hq hold H/2 and I/2 bytes per row.
  * Limits: 1 <= E <= 1024, topk <= 32, H and I multiples of 128,
  *   T * topk < 2^24, T * H < 2^31 and (T * topk + T * has_shared) * I < 2^31. */
 typedef struct moe_cfg {
@@ -84,6 +99,7 @@ typedef struct moe_cfg {
   int32_t wblk;
   int32_t act_group;
   int32_t has_shared;
+  int32_t act_fmt;
 } moe_cfg;
 
 /* Expert weights (host struct of device pointers).
@@ -261,7 +277,8 @@ int moe_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes
 
 /* Diagnostic: the issued rate of the scaled 16x16x128 MFMA the GEMMs use,
  * for the operand formats of `wfmt` (MOE_WFMT_FP8_BLOCK: e4m3 x e4m3;
- * MOE_WFMT_MXFP4: e2m1 weights x e4m3 activations).  Four workgroups of four
+ * MOE_WFMT_MXFP4: e2m1 weights x e4m3 activations; MOE_RATE_E2M1_E2M1:
+ * e2m1 x e2m1, the 4-bit-activation layer's GEMMs).  Four workgroups of four
  * waves per CU each run `iters` (1 .. 65536) rounds of three independent
  * MFMAs on operands that are all 1.0 with unit scales; `sink` (device, at
  * least 16 * CU-count bytes; 4 KiB covers an MI355X) receives one fp32 per
@@ -270,6 +287,7 @@ int moe_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes
  * call's duration on `stream`.  MOE_ERR_NULL_ARG (sink), MOE_ERR_MISALIGNED,
  * MOE_ERR_UNSUPPORTED (other wfmt), MOE_ERR_BAD_SHAPE (iters) and
  * MOE_ERR_WORKSPACE (sink too small) are host checks. */
+enum { MOE_RATE_E2M1_E2M1 = 2 };
 int moe_mfma_rate(int wfmt, int iters, void* sink, size_t sink_bytes, double* flops, void* stream);
 
 /* Diagnostic: the fp32 -> e4m3 conversion every quantiser of the layer

@@ -71,6 +71,17 @@ def test_workspace_size_and_shape_errors(lib):
     assert ws_size(cfg(wfmt=1, wblk=32, act_group=128))[0] == moe.MOE_OK
     assert ws_size(cfg(wfmt=1, wblk=32, act_group=32))[0] == moe.MOE_ERR_UNSUPPORTED
     assert ws_size(cfg(wfmt=7))[0] == moe.MOE_ERR_UNSUPPORTED
+    # 4-bit activations: MXFP4 weights, groups of 32, H a multiple of 256, H and I <= 8192
+    a4 = dict(wfmt=1, wblk=32, act_group=32, act_fmt=1)
+    assert ws_size(cfg(**a4))[0] == moe.MOE_OK
+    assert ws_size(cfg(**dict(a4, T=0)))[0] == moe.MOE_OK
+    assert ws_size(cfg(**dict(a4, wfmt=0)))[0] == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(cfg(**dict(a4, act_group=128)))[0] == moe.MOE_ERR_BAD_SHAPE
+    assert ws_size(cfg(**dict(a4, H=384)))[0] == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(cfg(**dict(a4, H=8448)))[0] == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(cfg(**dict(a4, I=8320)))[0] == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(cfg(**dict(a4, act_fmt=2)))[0] == moe.MOE_ERR_UNSUPPORTED
+    assert ws_size(cfg(act_fmt=-1))[0] == moe.MOE_ERR_UNSUPPORTED
     assert moe.raw_call("moe_workspace_size", None, C.byref(C.c_size_t(0))) == moe.MOE_ERR_NULL_ARG
     cc = cfg().c()
     assert moe.raw_call("moe_workspace_size", C.byref(cc), None) == moe.MOE_ERR_NULL_ARG
@@ -230,7 +241,7 @@ def test_mfma_rate_argument_errors(lib):
     call = lambda wfmt, iters, sink, sn: moe.raw_call("moe_mfma_rate", wfmt, iters, sink, C.c_size_t(sn), C.byref(fl), None)
     assert call(0, 16, None, 1 << 12) == moe.MOE_ERR_NULL_ARG
     assert call(0, 16, FAKE + 4, 1 << 12) == moe.MOE_ERR_MISALIGNED
-    assert call(2, 16, FAKE, 1 << 12) == moe.MOE_ERR_UNSUPPORTED
+    assert call(3, 16, FAKE, 1 << 12) == moe.MOE_ERR_UNSUPPORTED
     assert call(0, 0, FAKE, 1 << 12) == moe.MOE_ERR_BAD_SHAPE
     assert call(1, 65537, FAKE, 1 << 12) == moe.MOE_ERR_BAD_SHAPE
     assert call(1, 16, FAKE, 16) == moe.MOE_ERR_WORKSPACE

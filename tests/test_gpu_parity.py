@@ -754,7 +754,7 @@ def test_stream_read_reads_every_word(nbytes):
     assert got == want
 
 
-@pytest.mark.parametrize("wfmt", [0, 1])
+@pytest.mark.parametrize("wfmt", [0, 1, 2])
 @pytest.mark.parametrize("iters", [1, 777])
 def test_mfma_rate_probe_result(wfmt, iters):
     """The MFMA rate probe computes what it claims: every workgroup's sum is
