@@ -300,7 +300,7 @@ def moe_stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None) -> t
 
 def moe_mfma_rate(wfmt: int, iters: int, sink: torch.Tensor) -> float:
     """Enqueue the scaled-MFMA rate probe (all operands 1.0); returns the FLOP
-    count enqueued.  `sink` (float32, device) receives 1536 * iters per
+    count enqueued.  `sink` (float32, device) receives 4096 * iters per
     workgroup."""
     flops = C.c_double(0.0)
     _check("moe_mfma_rate", load().moe_mfma_rate(int(wfmt), int(iters), _ptr(sink),

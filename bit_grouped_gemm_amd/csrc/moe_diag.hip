@@ -55,13 +55,13 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream_read(const v4u* __res
 }
 
 // Issued-rate probe: every wave runs `iters` rounds of kRateAcc independent
-// 16x16x128 scaled MFMAs (operand format FA x e4m3, unit scales) on
+// 16x16x128 scaled MFMAs (operand formats FA x FB, unit scales) on
 // operands made of the codes a_word / b_word, so the matrix pipe never waits
 // on a result; four workgroups of four waves per CU.  Lane 0 of wave 0
 // stores the sum of its accumulators' elements: with both operands 1.0
 // every MFMA adds exactly 128 to each element, so the stored value is
 // 4 * 128 * kRateAcc * iters (exact in fp32 for iters <= 65536).
-constexpr int kRateAcc = 3;
+constexpr int kRateAcc = 8;
 
 template <int FA, int FB>
 __global__ __launch_bounds__(kStreamThreads) void k_mfma_rate(uint32_t a_word, uint32_t b_word, int iters,

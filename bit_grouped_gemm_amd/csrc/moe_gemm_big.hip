@@ -20,12 +20,13 @@
 //     in GEMM1 two gate and the two matching up tiles, so SwiGLU pairs meet
 //     in one lane) and every second token tile, which keeps up to 4 x 5
 //     fp32 accumulator tiles in registers;
-//   * ping-pong: the two wave columns (one wave of each per SIMD) take turns
-//     -- while column 0 reads step k's fragments out of LDS and rescales its
-//     accumulators, column 1 multiplies step k - 1 from registers, and the
-//     other way round in the next half step -- so each SIMD's matrix core
-//     is fed by one wave while the other waits on LDS, instead of all eight
-//     waves waiting on the same read burst after each barrier;
+//   * ping-pong: the two wave columns (one wave of each per SIMD) run half a
+//     K step apart -- while column 0 reads step k's fragments out of LDS and
+//     rescales its accumulators, column 1 multiplies step k - 1 from
+//     registers, and the other way round in the second half -- so each
+//     SIMD's matrix core is fed by one wave while the other waits on LDS,
+//     instead of all eight waves waiting on the same read burst after each
+//     barrier; one workgroup barrier per K step;
 //   * the kernel is persistent (one workgroup per CU) and all tiles of one
 //     expert run on one XCD (workgroup ids are dealt round-robin over the 8
 //     XCDs), so the expert's token rows are fetched into that XCD's L2 once;
@@ -149,12 +150,16 @@ constexpr int kSchedMayCross = 0x0001 | 0x0002 | 0x0004 | 0x0008 | 0x0100 | 0x04
 // workgroup barrier after this wave's LDS reads and writes have completed;
 // outstanding vector-memory loads stay in flight (unlike __syncthreads,
 // whose release fence waits for them): the waits for the ring's
-// direct-to-LDS loads are explicit (wait_vmcnt)
+// direct-to-LDS loads are explicit (wait_vmcnt).  No instruction is
+// scheduled across it (the compiler would otherwise sink MFMAs, which touch
+// registers only, below the barrier into the next phase).
 __device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), other counters at their maxima
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 }  // namespace
@@ -665,22 +670,24 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
       }
       if (NT == 0 && go) issue_range(kn, iss, 0, L);
     };
-    // half steps: in A(k) column 0 reads step k while column 1 multiplies
-    // step k - 1, in B(k) column 0 multiplies step k while column 1 reads
-    // it; each side issues its loads of step k + S - 1 while it multiplies,
-    // into the stage step k - 1 used.  The two columns run separate loops
-    // with the same barriers (one straight-line order each).
+    // one barrier A(k) per step: after it column 0 reads step k's fragments
+    // and multiplies them, while column 1 first multiplies step k - 1 from
+    // registers and then reads step k, so the two columns of a SIMD stay half
+    // a step apart and one's LDS reads overlap the other's MFMAs.  Each side
+    // issues its loads of step k + S - 1 while it multiplies, into the stage
+    // step k - 1 used: every wave finished reading that stage before A(k).
+    // A(k) also publishes step k: every wave waits for its own loads of the
+    // step before it.  The two columns run separate loops with the same
+    // barriers (one straight-line order each).
     if (wc == 0) {
       wait_ring(nks - 1);
       lds_barrier();  // A(0)
       READ(st0, 0);
-      lds_barrier();  // B(0)
       MMA(S - 1, stage_ptr(S - 1));
       auto half_pair = [&](int k, const uint8_t* cur, uint8_t* iss) __attribute__((always_inline)) {
         wait_ring(nks - 1 - k);
         lds_barrier();  // A(k)
         READ(cur, k);
-        lds_barrier();  // B(k)
         MMA(k + S - 1, iss);
       };
       for (int k = 1; k < nks; k += S) {
@@ -694,13 +701,11 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
       wait_ring(nks - 1);
       lds_barrier();  // A(0)
       if (S - 1 < nks) issue_range(S - 1, stage_ptr(S - 1), 0, L);
-      lds_barrier();  // B(0)
       READ(st0, 0);
       auto half_pair = [&](int k, const uint8_t* cur, uint8_t* iss) __attribute__((always_inline)) {
         wait_ring(nks - 1 - k);
         lds_barrier();  // A(k)
         MMA(k + S - 1, iss);
-        lds_barrier();  // B(k)
         READ(cur, k);
       };
       for (int k = 1; k < nks; k += S) {

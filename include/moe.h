@@ -279,10 +279,10 @@ int moe_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes
  * for the operand formats of `wfmt` (MOE_WFMT_FP8_BLOCK: e4m3 x e4m3;
  * MOE_WFMT_MXFP4: e2m1 weights x e4m3 activations; MOE_RATE_E2M1_E2M1:
  * e2m1 x e2m1, the 4-bit-activation layer's GEMMs).  Four workgroups of four
- * waves per CU each run `iters` (1 .. 65536) rounds of three independent
+ * waves per CU each run `iters` (1 .. 65536) rounds of eight independent
  * MFMAs on operands that are all 1.0 with unit scales; `sink` (device, at
  * least 16 * CU-count bytes; 4 KiB covers an MI355X) receives one fp32 per
- * workgroup, exactly 1536 * iters.  `*flops` (host, may be NULL) is set to the
+ * workgroup, exactly 4096 * iters.  `*flops` (host, may be NULL) is set to the
  * FLOP count enqueued (2 * 16 * 16 * 128 per MFMA), so FLOP/s = *flops / the
  * call's duration on `stream`.  MOE_ERR_NULL_ARG (sink), MOE_ERR_MISALIGNED,
  * MOE_ERR_UNSUPPORTED (other wfmt), MOE_ERR_BAD_SHAPE (iters) and

@@ -758,7 +758,7 @@ def test_stream_read_reads_every_word(nbytes):
 @pytest.mark.parametrize("iters", [1, 777])
 def test_mfma_rate_probe_result(wfmt, iters):
     """The MFMA rate probe computes what it claims: every workgroup's sum is
-    exactly 1536 * iters (operands 1.0, unit scales, 3 accumulators of 4
+    exactly 4096 * iters (operands 1.0, unit scales, 8 accumulators of 4
     elements, 128 per MFMA), and the reported FLOP count matches the grid."""
     moe = M()
     _note(f"mfma_rate wfmt={wfmt} iters={iters}")
@@ -767,7 +767,7 @@ def test_mfma_rate_probe_result(wfmt, iters):
     torch.cuda.synchronize()
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     grid = 4 * ncu
-    assert flops == grid * 4 * iters * 3 * (16 * 16 * 128 * 2)
+    assert flops == grid * 4 * iters * 8 * (16 * 16 * 128 * 2)
     got = sink.cpu().numpy()
-    assert np.all(got[:grid] == 1536.0 * iters)
+    assert np.all(got[:grid] == 4096.0 * iters)
     assert np.all(got[grid:] == -1.0)
