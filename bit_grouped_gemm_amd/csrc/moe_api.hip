@@ -72,6 +72,13 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   // token tiles; with one token tile the smaller units keep more waves busy
   // (measured cold-cache: T = 64 layers 2-8 % faster, T <= 32 1-3 % slower)
   s.g2_nj = (H % 256 == 0 && s.g2_ntt >= 2) ? 4 : 2;
+  // MXFP4 weights carry half the bytes per tile: twice the tiles per wave
+  // keep as many bytes in flight, while the launch still has a unit per CU
+  // (measured cold-cache, H=4096 E=64 top-8 I=1536: GEMM2 -1 to -4.5 us at
+  // T = 8..128; at T = 1 the halved unit count costs 4 us, so not there)
+  if (wfmt == 1 && H % (128 * s.g2_nj) == 0 &&
+      long(s.slots_max) * (H / (128 * s.g2_nj)) >= kSplitTargetWG)
+    s.g2_nj *= 2;
   s.g2_tiles = H / (64 * s.g2_nj);
   s.g1_items = items_bound(s.rows_cap, s.slots_max, 16 * s.g1_ntt);
   s.g2_items = items_bound(s.rows_cap, s.slots_max, 16 * s.g2_ntt);

@@ -650,7 +650,8 @@ __global__ __launch_bounds__(kThreads, B32 ? 1 : NTT == 2 ? 3 : NTT == 1 ? 4 : 1
 // ---------------------------------------------------------------------
 // GEMM2: unit = (work item, 64 NJ output rows, K split); wave w owns output rows
 // n0 + 16 NJ w + 16 j + (0..15), j < NJ (NJ = 4 when H allows 256-row
-// units: twice the weight bytes in flight per wave).
+// units: twice the weight bytes in flight per wave; NJ = 8 for MXFP4, whose
+// tiles carry half the bytes).
 // ---------------------------------------------------------------------
 template <int WF, int NTT, int B32, int NJ>
 __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
@@ -871,7 +872,7 @@ hipError_t launch_clear(int32_t* ptr, int n, hipStream_t st) {
 
 MOE_GEMM_DISPATCH(k_gemm1)
 
-// GEMM2 also picks its weight tiles per wave (NJ = 2 or 4)
+// GEMM2 also picks its weight tiles per wave (NJ = 2, 4 or 8)
 template <int NJ>
 static hipError_t dispatch_gemm2_nj(const Shape& s, int ntt, unsigned grid, const GemmParams& p, hipStream_t st) {
   const bool b32 = s.wfmt == 0 && s.wblk == 32;
@@ -913,6 +914,7 @@ hipError_t launch_gemm2(const Shape& s, const uint8_t* hq, const float* hs, cons
   p.S = s.g2_split; p.ntiles = s.g2_tiles; p.rows_cap = s.rows_cap;
   const unsigned grid = unsigned(s.g2_items) * s.g2_tiles * s.g2_split;
   if (grid == 0) return hipSuccess;
+  if (s.g2_nj == 8) return dispatch_gemm2_nj<8>(s, s.g2_ntt, grid, p, st);
   return s.g2_nj == 4 ? dispatch_gemm2_nj<4>(s, s.g2_ntt, grid, p, st)
                       : dispatch_gemm2_nj<2>(s, s.g2_ntt, grid, p, st);
 }

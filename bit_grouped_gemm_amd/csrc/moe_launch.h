@@ -21,7 +21,7 @@ struct Shape {
   int g1_ntt;       // 16-token tiles per pass (1, 2 or 4)
   int g1_items;     // upper bound on work items (one pass of 16 g1_ntt rows of one group)
   // GEMM2: unit = 64 g2_nj output rows of one group
-  int g2_nj;        // weight tiles per wave: 4 (256-row units) when H % 256 == 0, else 2
+  int g2_nj;        // weight tiles per wave: 2, 4 (256-row units, two or more token tiles), 8 (MXFP4 at one unit per CU)
   int g2_tiles;     // H / (64 g2_nj)
   int g2_split;     // K splits over I/128 steps
   int g2_ntt;

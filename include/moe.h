@@ -221,8 +221,8 @@ int moe_route(const moe_cfg* cfg, const uint16_t* x, const uint16_t* gate_w, int
  * MOE_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on every GPU it
  * runs on until the process ends; shapes whose moe_workspace_size exceeds
  * it return MOE_ERR_WORKSPACE (host check; e.g. the H=4096 E=64 top-8
- * I=1536 layer fits up to T = 256, the H=7168 E=256 top-8 I=2048 layer
- * with a shared expert up to T = 192).  The call allocates and frees
+ * I=1536 layer fits up to T = 453, the H=7168 E=256 top-8 I=2048 layer
+ * with a shared expert up to T = 235).  The call allocates and frees
  * nothing.  The device is the current one (the stream's); the first call on
  * a device looks up the array's address (hipGetSymbolAddress), so make it
  * once outside any graph capture; later calls only enqueue kernels.

@@ -355,6 +355,33 @@ def test_layer_reduced(name, T):
     tol_check(out.float().cpu().numpy(), ref, f"{name} T={T}")
 
 
+@pytest.mark.parametrize("T", [37, 64])
+def test_layer_mxfp4_eight_tiles_per_wave(T):
+    """MXFP4 decode GEMM2 with eight weight tiles per wave (512-row units):
+    H = 2048 and 64 experts keep one unit per CU, and at T = 64 a pass holds
+    two token tiles."""
+    moe = M()
+    wl = reduced("decode_mxfp4", H=2048, I=256, E=64, topk=8)
+    _note(f"mxfp4 nj8 T={T}")
+    w, wc = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=31)
+    cfg = moe.Cfg.for_workload(wl, T)
+    out = moe.moe_layer(cfg, x, ids, tw, w)
+    counts, offsets, eidx, rtok, xq, xs = moe.moe_permute(cfg, x, ids)
+    ws = moe.workspace(cfg)
+    hq, hs = moe.moe_grouped_gemm1_swiglu(cfg, xq, xs, rtok, offsets, w, ws)
+    y = moe.moe_grouped_gemm2(cfg, hq, hs, offsets, w, ws)
+    torch.cuda.synchronize()
+    ref = oracle.layer_for(wl, T, wc).layer(x.cpu(), ids.cpu(), tw.cpu())
+    tol_check(out.float().cpu().numpy(), ref, f"mxfp4 nj8 T={T}")
+    # GEMM2 on the GPU's own h codes against the oracle's GEMM2 of the same codes
+    R = int(offsets[-1].item())
+    lay = oracle.layer_for(wl, T, wc)
+    y_ref = lay.gemm2(hq.cpu(), hs.cpu(), offsets.cpu(), range(R))
+    err = np.abs(y.cpu().numpy()[:R] - y_ref).max()
+    assert err <= 3e-4 * np.abs(y_ref).max(), err
+
+
 FULL = [(n, T) for n in ("decode_fp8", "decode_mxfp4") for T in synth.WORKLOADS[n].tokens] + \
        [("decode_fp8_zipf_shared", T) for T in synth.WORKLOADS["decode_fp8_zipf_shared"].tokens] + \
        [("prefill_mxfp4", 4096)]
