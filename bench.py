@@ -297,7 +297,7 @@ def summarize(sw, rec, graph_us):
 
 
 def router_section(moe, synth, torch, flush, stream, ev, reps=20):
-    """moe_route (gate GEMM + top-k + softmax, one kernel) on the decode FP8
+    """moe_route (gate GEMM + top-k + softmax; two kernels up to 512 tokens) on the decode FP8
     layer's shape (H=4096, E=64, top-8) at T = 1, 64, 256 and the prefill
     shape (H=7168, E=256, top-8) at T = 4096, cold caches: median latency,
     bytes moved (x, gate rows, ids and weights) per second, TFLOP/s."""
@@ -309,13 +309,15 @@ def router_section(moe, synth, torch, flush, stream, ev, reps=20):
         cfg = moe.Cfg.for_workload(wl, T)
         ids = torch.empty(T, wl.topk, dtype=torch.int32, device=flush.device)
         w = torch.empty(T, wl.topk, dtype=torch.float32, device=flush.device)
-        moe.moe_route(cfg, x, wg, ids, w)
+        nws = moe.moe_route_workspace_size(cfg)
+        ws = torch.empty(nws, dtype=torch.uint8, device=flush.device) if nws else None
+        moe.moe_route(cfg, x, wg, ids, w, ws=ws)
         ts = []
         for _ in range(reps):
             flush.sum(dtype=torch.int64)
             a, b = ev(), ev()
             a.record(stream)
-            moe.moe_route(cfg, x, wg, ids, w)
+            moe.moe_route(cfg, x, wg, ids, w, ws=ws)
             b.record(stream)
             ts.append((a, b))
         torch.cuda.synchronize()

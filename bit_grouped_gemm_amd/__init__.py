@@ -46,7 +46,7 @@ WFMT_MXFP4 = 1
 
 EXPORTS = ("moe_workspace_size", "moe_permute", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm2",
            "moe_combine", "moe_layer", "moe_layer_static", "moe_prepack_weights", "moe_stream_read",
-           "moe_mfma_rate", "moe_encode_e4m3", "moe_route", "moe_status_str")
+           "moe_mfma_rate", "moe_encode_e4m3", "moe_route", "moe_route_workspace_size", "moe_status_str")
 
 
 class MoeCfg(C.Structure):
@@ -91,7 +91,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     L.moe_stream_read.argtypes = [vp, sz, vp, sz, vp]
     L.moe_mfma_rate.argtypes = [C.c_int, C.c_int, vp, sz, C.POINTER(C.c_double), vp]
     L.moe_encode_e4m3.argtypes = [vp, sz, vp, vp]
-    L.moe_route.argtypes = [cfgp, vp, vp, vp, vp, vp]
+    L.moe_route_workspace_size.argtypes = [cfgp, C.POINTER(sz)]
+    L.moe_route.argtypes = [cfgp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_status_str.argtypes = [C.c_int]
     L.moe_status_str.restype = C.c_char_p
     for n in EXPORTS:
@@ -308,17 +309,28 @@ def moe_mfma_rate(wfmt: int, iters: int, sink: torch.Tensor) -> float:
     return flops.value
 
 
+def moe_route_workspace_size(cfg: Cfg) -> int:
+    n = C.c_size_t(0)
+    c = cfg.c()
+    _check("moe_route_workspace_size", load().moe_route_workspace_size(C.byref(c), C.byref(n)))
+    return int(n.value)
+
+
 def moe_route(cfg: Cfg, x: torch.Tensor, gate_w: torch.Tensor, ids: Optional[torch.Tensor] = None,
-              weights: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+              weights: Optional[torch.Tensor] = None,
+              ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Router: bf16 x [T,H] and gate rows [E,H] -> (topk_ids int32 [T,topk],
     topk_weights fp32 [T,topk]), the layer's routing inputs."""
     if ids is None:
         ids = torch.empty(cfg.T, cfg.topk, dtype=torch.int32, device=x.device)
     if weights is None:
         weights = torch.empty(cfg.T, cfg.topk, dtype=torch.float32, device=x.device)
+    if ws is None:
+        n = moe_route_workspace_size(cfg)
+        ws = torch.empty(n, dtype=torch.uint8, device=x.device) if n else None
     c = cfg.c()
     _check("moe_route", load().moe_route(C.byref(c), _ptr(_u16(x)), _ptr(_u16(gate_w)), _ptr(ids), _ptr(weights),
-                                         _stream()))
+                                         _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
     return ids, weights
 
 

@@ -486,14 +486,26 @@ int moe_mfma_rate(int wfmt, int iters, void* sink, size_t sink_bytes, double* fl
   return hip_status(launch_mfma_rate(wfmt, iters, static_cast<float*>(sink), flops, static_cast<hipStream_t>(stream)));
 }
 
-int moe_route(const moe_cfg* cfg, const uint16_t* x, const uint16_t* gate_w, int32_t* topk_ids, float* topk_weights,
-              void* stream) {
-  const bool has_rows = cfg && cfg->T > 0;
-  const int rc = check_args(cfg, {{x, has_rows}, {gate_w, true}, {topk_ids, has_rows}, {topk_weights, has_rows}});
+int moe_route_workspace_size(const moe_cfg* cfg, size_t* bytes) {
+  if (!cfg || !bytes) return MOE_ERR_NULL_ARG;
+  const int rc = check_shape(cfg);
   if (rc) return rc;
   if (cfg->E > 256) return MOE_ERR_UNSUPPORTED;
+  *bytes = route_workspace_bytes(cfg->T, cfg->H, cfg->E);
+  return MOE_OK;
+}
+
+int moe_route(const moe_cfg* cfg, const uint16_t* x, const uint16_t* gate_w, int32_t* topk_ids, float* topk_weights,
+              void* ws, size_t ws_bytes, void* stream) {
+  const bool has_rows = cfg && cfg->T > 0;
+  const size_t need = has_rows ? route_workspace_bytes(cfg->T, cfg->H, cfg->E) : 0;
+  const int rc = check_args(cfg, {{x, has_rows}, {gate_w, true}, {topk_ids, has_rows}, {topk_weights, has_rows},
+                                  {ws, need > 0}});
+  if (rc) return rc;
+  if (cfg->E > 256) return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   return hip_status(launch_route_gemm(cfg->T, cfg->H, cfg->E, cfg->topk, x, gate_w, topk_ids, topk_weights,
-                                      static_cast<hipStream_t>(stream)));
+                                      static_cast<float*>(ws), static_cast<hipStream_t>(stream)));
 }
 
 int moe_encode_e4m3(const float* v, size_t n, uint8_t* codes, void* stream) {

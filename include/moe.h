@@ -210,9 +210,16 @@ int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, co
  * Uses cfg's T, H, E and topk (the rest must still be valid); E <= 256
  * (MOE_ERR_UNSUPPORTED otherwise).  Logits are summed in fp32, so two
  * experts whose exact logits differ by less than that rounding may come
- * out in either order.  Errors as for every entry point. */
+ * out in either order.
+ *   ws: device scratch of at least moe_route_workspace_size(cfg) bytes
+ *   (contents on entry ignored; may be NULL when that size is 0).  Up to 512
+ *   tokens the gate rows are spread over many workgroups whose partial
+ *   logits meet in ws, as the layer's workspace is sized on the host
+ *   (FusedDeepMoE W4A8 workspace computation); above, ws is not used.
+ * Errors as for every entry point (MOE_ERR_WORKSPACE: ws_bytes too small). */
+int moe_route_workspace_size(const moe_cfg* cfg, size_t* bytes);
 int moe_route(const moe_cfg* cfg, const uint16_t* x, const uint16_t* gate_w, int32_t* topk_ids, float* topk_weights,
-              void* stream);
+              void* ws, size_t ws_bytes, void* stream);
 
 /* moe_layer for callers that cannot allocate device memory (code under
  * graph capture, tight serving loops, harnesses that forbid allocation):

@@ -266,10 +266,46 @@ def test_static_entry_point_host_checks(lib):
 def test_route_argument_errors(lib):
     c = cfg()
     cc = c.c()
-    call = lambda cfgp, x, wg, ids, w: moe.raw_call("moe_route", cfgp, x, wg, ids, w, None)
+    call = lambda cfgp, x, wg, ids, w: moe.raw_call("moe_route", cfgp, x, wg, ids, w, FAKE, C.c_size_t(1 << 30), None)
     assert call(None, FAKE, FAKE, FAKE, FAKE) == moe.MOE_ERR_NULL_ARG
     assert call(C.byref(cc), FAKE, None, FAKE, FAKE) == moe.MOE_ERR_NULL_ARG
     assert call(C.byref(cc), FAKE, FAKE, FAKE, None) == moe.MOE_ERR_NULL_ARG
     assert call(C.byref(cc), FAKE + 2, FAKE, FAKE, FAKE) == moe.MOE_ERR_MISALIGNED
     assert call(C.byref(cfg(topk=0).c()), FAKE, FAKE, FAKE, FAKE) == moe.MOE_ERR_BAD_SHAPE
     assert call(C.byref(cfg(E=300, topk=8).c()), FAKE, FAKE, FAKE, FAKE) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_route_workspace(lib):
+    n = C.c_size_t(0)
+    size = lambda c: (moe.raw_call("moe_route_workspace_size", C.byref(c.c()), C.byref(n)), n.value)
+    # few tokens need scratch for the partial logits, many none
+    rc, a = size(cfg(T=1, H=4096, E=64, topk=8))
+    assert rc == moe.MOE_OK and a > 0 and a % 4 == 0
+    assert size(cfg(T=512, H=4096, E=64, topk=8))[1] > 0
+    assert size(cfg(T=513, H=4096, E=64, topk=8)) == (moe.MOE_OK, 0)
+    assert size(cfg(T=0)) == (moe.MOE_OK, 0)
+    assert size(cfg(E=300, topk=8))[0] == moe.MOE_ERR_UNSUPPORTED
+    assert size(cfg(topk=0))[0] == moe.MOE_ERR_BAD_SHAPE
+    assert moe.raw_call("moe_route_workspace_size", None, C.byref(n)) == moe.MOE_ERR_NULL_ARG
+    cc = cfg(T=4, H=256, E=8, topk=2).c()
+    P = lambda v: None if v is None else C.c_void_p(v)
+    call = lambda ws, nb: moe.raw_call("moe_route", C.byref(cc), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(ws),
+                                       C.c_size_t(nb), None)
+    assert call(None, 0) == moe.MOE_ERR_NULL_ARG              # needed but missing
+    need = size(cfg(T=4, H=256, E=8, topk=2))[1]
+    assert call(FAKE, need - 4) == moe.MOE_ERR_WORKSPACE
+    assert call(FAKE + 4, need) == moe.MOE_ERR_MISALIGNED
+
+
+def test_binding_declares_every_parameter(lib):
+    """Each exported call's ctypes argtypes has exactly the header's parameter
+    count: an undeclared trailing parameter would be passed as a 32-bit int
+    (a truncated stream or size), which crashes the host inside the call."""
+    import re
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    L = moe.load()
+    for n in moe.EXPORTS:
+        m = re.search(r"\b" + n + r"\(([^;]*?)\);", src, re.S)
+        assert m, n
+        nargs = len([a for a in m.group(1).split(",") if a.strip()])
+        assert len(getattr(L, n).argtypes or []) == nargs, n

@@ -70,8 +70,11 @@ def check_router(x, wg, k, ids, w):
 
 
 CASES = [
-    ("decode_fp8", 1), ("decode_fp8", 37), ("decode_fp8", 256),
-    ("prefill_mxfp4", 64), ("prefill_mxfp4", 4096),        # E = 256, H = 7168; the two-tile kernel at T = 4096
+    # up to 512 tokens: partial logits of many workgroups, then the selection kernel
+    ("decode_fp8", 1), ("decode_fp8", 37), ("decode_fp8", 256), ("decode_fp8", 512), ("prefill_mxfp4", 64),
+    # one kernel: 16 waves per 16-token tile (E <= 64: one expert tile per wave; E = 256: four), and the
+    # two-tile kernel at T = 4096
+    ("decode_fp8", 600), ("prefill_mxfp4", 1000), ("prefill_mxfp4", 4096),
 ]
 
 
@@ -92,9 +95,10 @@ def test_route_matches_oracle(name, T):
     assert same >= (T if T < 10 else 0.9 * T)
 
 
-@pytest.mark.parametrize("H,E,k,T", [(512, 72, 16, 33), (256, 8, 2, 19), (256, 12, 12, 5), (128, 256, 32, 50)])
+@pytest.mark.parametrize("H,E,k,T", [(512, 72, 16, 33), (256, 8, 2, 19), (256, 12, 12, 5), (128, 256, 32, 50),
+                                     (512, 72, 16, 700), (384, 40, 6, 530)])
 def test_route_odd_shapes(H, E, k, T):
-    """E not a multiple of 16, k = E, k = 32, tiny E."""
+    """E not a multiple of 16, k = E, k = 32, tiny E; both kernel paths."""
     moe = M()
     g = torch.Generator(device=DEV).manual_seed(H + E + k)
     x = torch.randn(T, H, generator=g, device=DEV).to(torch.bfloat16)
@@ -162,3 +166,25 @@ def test_route_T0_and_rejects_large_E():
         moe.moe_route(big, torch.zeros(4, 256, dtype=torch.bfloat16, device=DEV),
                       torch.zeros(300, 256, dtype=torch.bfloat16, device=DEV))
     assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("T", [1, 200, 700])
+def test_route_deterministic_with_poisoned_workspace(T):
+    """Repeated calls, the workspace refilled with garbage in between, give
+    bit-identical ids and weights (the partial logits are summed in a fixed
+    order, whatever the workspace held)."""
+    moe = M()
+    wl = synth.WORKLOADS["decode_fp8"]
+    wg = synth.gen_gate(wl, seed=3, device=DEV)
+    x = synth.gen_x(T, wl.H, 3, wl.wid, device=DEV)
+    cfg = moe.Cfg.for_workload(wl, T)
+    n = moe.moe_route_workspace_size(cfg)
+    assert (n > 0) == (T <= 512)
+    ws = torch.empty(max(n, 16), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xFF)
+    ids0, w0 = moe.moe_route(cfg, x, wg, ws=ws)
+    ids0, w0 = ids0.clone(), w0.clone()
+    ws.fill_(0x7F)
+    ids1, w1 = moe.moe_route(cfg, x, wg, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids0, ids1) and torch.equal(w0.view(torch.int32), w1.view(torch.int32))
