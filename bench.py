@@ -110,6 +110,16 @@ class Sweep:
                 out=torch.empty(T, wl.H, dtype=torch.bfloat16, device=dev),
                 wbytes=synth.weight_bytes_touched(wl, w_rm, ids), touched=synth.touched_experts(ids, wl.E),
                 flops=synth.layer_flops(wl, T, ids), graph=None)
+            # the persistent one-launch layer, where the shape allows it
+            status = torch.zeros(1, dtype=torch.int32, device=dev)
+            c = self.cases[T]
+            try:
+                moe.moe_layer_persistent(cfg, x, ids, tw, self.w, ws=c["ws"], out=c["out"], status=status)
+                c["pers"] = status
+            except moe.MoeError as err:
+                if err.status != moe.MOE_ERR_UNSUPPORTED:
+                    raise
+                c["pers"] = None
 
     def gemm1_bytes(self, T):
         """Algorithmic bytes of one GEMM1 launch: W1 codes + scales of every
@@ -175,6 +185,15 @@ def main():
                 if rec is not None:
                     rec[n]["layer"][T].append((a, b))
                     rec[n]["warm"][T].append((d, e))
+                if c["pers"] is not None:
+                    flush.sum(dtype=torch.int64)
+                    f, h = ev(), ev()
+                    f.record(stream)
+                    moe.moe_layer_persistent(c["cfg"], c["x"], c["ids"], c["tw"], sw.w, ws=c["ws"], out=c["out"],
+                                             status=c["pers"])
+                    h.record(stream)
+                    if rec is not None:
+                        rec[n]["pers"][T].append((f, h))
             # stage-by-stage pass at the roofline point: each kernel bracketed by events
             c = sw.cases[sw.RT]
             flush.sum(dtype=torch.int64)
@@ -193,8 +212,8 @@ def main():
 
     for _ in range(args.warmup):
         one_step(None)
-    rec = {n: {"layer": {T: [] for T in sw.Ts}, "warm": {T: [] for T in sw.Ts}, "stages": []}
-           for n, sw in sweeps.items()}
+    rec = {n: {"layer": {T: [] for T in sw.Ts}, "warm": {T: [] for T in sw.Ts}, "pers": {T: [] for T in sw.Ts},
+               "stages": []} for n, sw in sweeps.items()}
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for _ in range(args.steps):
@@ -273,6 +292,11 @@ def summarize(sw, rec, graph_us):
             "hbm_frac": round(c["wbytes"] / med / 1e3 / HBM_PEAK_GBS, 4),
             "TFLOPs": round(c["flops"] / med / 1e6, 2),
         }
+        if rec["pers"][T]:
+            assert int(c["pers"].item()) == 0, "persistent layer: a wait expired"
+            pl = float(np.median(np.array([ms(p) for p in rec["pers"][T]]) * 1e3))
+            sweep[str(T)]["persistent_latency_us_median"] = round(pl, 2)
+            sweep[str(T)]["persistent_hbm_frac"] = round(c["wbytes"] / pl / 1e3 / HBM_PEAK_GBS, 4)
         if T in graph_us:
             g = graph_us[T]
             sweep[str(T)]["graph_latency_us_median"] = round(g, 2)

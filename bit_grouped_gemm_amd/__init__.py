@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
     moe_combine(cfg, y, expand_idx, offsets, topk_weights) -> out
     moe_layer(cfg, x, topk_ids, topk_weights, weights, ws=None, out=None) -> out
     moe_layer_static(cfg, x, topk_ids, topk_weights, weights, out=None) -> out   (no workspace)
+    moe_layer_persistent(cfg, x, topk_ids, topk_weights, weights, ws=None, out=None, status=None) -> out
+                                                                   (decode shapes: one launch)
     moe_prepack_weights(cfg, weights) -> TiledWeights
     moe_route(cfg, x, gate_w) -> (topk_ids, topk_weights)   (the router in front of the layer)
     moe_encode_e4m3(v) -> codes   (diagnostic: the quantisers' fp32 -> e4m3 conversion)
@@ -45,7 +47,8 @@ WFMT_FP8_BLOCK = 0
 WFMT_MXFP4 = 1
 
 EXPORTS = ("moe_workspace_size", "moe_permute", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm2",
-           "moe_combine", "moe_layer", "moe_layer_static", "moe_prepack_weights", "moe_stream_read",
+           "moe_combine", "moe_layer", "moe_layer_static", "moe_layer_persistent", "moe_prepack_weights",
+           "moe_stream_read",
            "moe_mfma_rate", "moe_encode_e4m3", "moe_route", "moe_route_workspace_size", "moe_status_str")
 
 
@@ -87,6 +90,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     L.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
     L.moe_layer.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp]
     L.moe_layer_static.argtypes = [cfgp, vp, vp, vp, wp, vp, vp]
+    L.moe_layer_persistent.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp, vp]
     L.moe_prepack_weights.argtypes = [cfgp, wp, wp, vp]
     L.moe_stream_read.argtypes = [vp, sz, vp, sz, vp]
     L.moe_mfma_rate.argtypes = [C.c_int, C.c_int, vp, sz, C.POINTER(C.c_double), vp]
@@ -257,6 +261,21 @@ def moe_layer_static(cfg: Cfg, x, topk_ids, topk_weights, weights,
     c, w = cfg.c(), weights_struct(weights)
     _check("moe_layer_static", load().moe_layer_static(C.byref(c), _ptr(_u16(x)), _ptr(topk_ids), _ptr(topk_weights),
                                                        C.byref(w), _ptr(_u16(out)), _stream()))
+    return out
+
+
+def moe_layer_persistent(cfg: Cfg, x, topk_ids, topk_weights, weights, ws: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_layer as one persistent launch (decode shapes; raises with
+    MOE_ERR_UNSUPPORTED otherwise).  `status`, an int32 device tensor of one
+    element, receives the number of expired waits (0 in a correct run)."""
+    if out is None:
+        out = torch.empty(cfg.T, cfg.H, dtype=torch.bfloat16, device=x.device)
+    ws = workspace(cfg, x.device) if ws is None else ws
+    c, w = cfg.c(), weights_struct(weights)
+    _check("moe_layer_persistent",
+           load().moe_layer_persistent(C.byref(c), _ptr(_u16(x)), _ptr(topk_ids), _ptr(topk_weights), C.byref(w),
+                                       _ptr(_u16(out)), _ptr(ws), ws.numel(), _ptr(status), _stream()))
     return out
 
 

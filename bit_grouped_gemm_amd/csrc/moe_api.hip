@@ -149,10 +149,12 @@ WsLayout make_ws_layout(const Shape& s) {
   L.part1 = take(s.g1_split > 1 ? 4 * size_t(s.g1_split) * R * 2 * s.I : 0);
   L.part2 = take(s.g2_split > 1 ? 4 * size_t(s.g2_split) * R * s.H : 0);
   L.chunk_cnt = take(s.perm_chunks > 1 ? 4 * size_t(s.perm_chunks) * s.E : 0);
-  // the two counter arrays are adjacent so one clear covers both
+  // the counter arrays (split-K arrivals, then the persistent layer's
+  // control block) are adjacent so one clear covers them all
   L.cnt1 = o;
   L.cnt2 = L.cnt1 + 4 * size_t(s.g1_items) * s.g1_tiles;
-  o = align256(L.cnt2 + 4 * size_t(s.g2_items) * s.g2_tiles);
+  L.pctl = align256(L.cnt2 + 4 * size_t(s.g2_items) * s.g2_tiles);
+  o = align256(L.pctl + 4 * (size_t(kPersistCtlHead) + 2 * size_t(s.g1_items)));
   L.total = o;
   return L;
 }
@@ -244,45 +246,52 @@ int check_args(const moe_cfg* c, PtrList ps, const moe_weights* w = nullptr, boo
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// The layer's buffers inside a scratch region `b` of at least L.total bytes.
+LayerBufs layer_bufs(const WsLayout& L, char* b) {
+  LayerBufs r{};
+  r.counts = reinterpret_cast<int32_t*>(b + L.counts);
+  r.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  r.expand_idx = reinterpret_cast<int32_t*>(b + L.expand_idx);
+  r.row_token = reinterpret_cast<int32_t*>(b + L.row_token);
+  r.xq = reinterpret_cast<uint8_t*>(b + L.xq);
+  r.xs = reinterpret_cast<float*>(b + L.xs);
+  r.hq = reinterpret_cast<uint8_t*>(b + L.hq);
+  r.hs = reinterpret_cast<float*>(b + L.hs);
+  // GEMM2 rows stay inside the layer as bf16 (half the bytes of the fp32
+  // rows the stage export returns); the combine accumulates them in fp32
+  r.yb = reinterpret_cast<uint16_t*>(b + L.y);
+  r.part1 = reinterpret_cast<float*>(b + L.part1);
+  r.part2 = reinterpret_cast<float*>(b + L.part2);
+  r.cnt1 = reinterpret_cast<int32_t*>(b + L.cnt1);
+  r.cnt2 = reinterpret_cast<int32_t*>(b + L.cnt2);
+  // the routing kernel zeroes every split-K arrival counter of the call
+  r.clear = r.cnt1;
+  r.nclear = int((L.total - L.cnt1) / 4);
+  return r;
+}
+
 // The layer's launch sequence over a scratch region `b` of at least L.total
 // bytes (a caller's workspace, or this GPU's static scratch array).
 int enqueue_layer(const Shape& s, const WsLayout& L, const uint16_t* x, const int32_t* topk_ids,
                   const float* topk_weights, const moe_weights* w, uint16_t* out, char* b, hipStream_t st) {
   int rc;
-  int32_t* counts = reinterpret_cast<int32_t*>(b + L.counts);
-  int32_t* offsets = reinterpret_cast<int32_t*>(b + L.offsets);
-  int32_t* eidx = reinterpret_cast<int32_t*>(b + L.expand_idx);
-  int32_t* rtok = reinterpret_cast<int32_t*>(b + L.row_token);
-  uint8_t* xq = reinterpret_cast<uint8_t*>(b + L.xq);
-  float* xs = reinterpret_cast<float*>(b + L.xs);
-  uint8_t* hq = reinterpret_cast<uint8_t*>(b + L.hq);
-  float* hs = reinterpret_cast<float*>(b + L.hs);
-  // GEMM2 rows stay inside the layer as bf16 (half the bytes of the fp32
-  // rows the stage export returns); the combine accumulates them in fp32
-  uint16_t* yb = reinterpret_cast<uint16_t*>(b + L.y);
-  int32_t* cnt1 = reinterpret_cast<int32_t*>(b + L.cnt1);
-  int32_t* cnt2 = reinterpret_cast<int32_t*>(b + L.cnt2);
-  // the routing kernel zeroes every split-K arrival counter of the call
-  const int nclear = int((L.total - L.cnt1) / 4);
+  const LayerBufs B = layer_bufs(L, b);
   int32_t* chunk_cnt = reinterpret_cast<int32_t*>(b + L.chunk_cnt);
-  if ((rc = hip_status(launch_route_quant(s, x, topk_ids, counts, offsets, eidx, rtok, xq, xs, cnt1, nclear,
-                                          chunk_cnt, st))))
+  if ((rc = hip_status(launch_route_quant(s, x, topk_ids, B.counts, B.offsets, B.expand_idx, B.row_token, B.xq,
+                                          B.xs, B.clear, B.nclear, chunk_cnt, st))))
     return rc;
   if (s.T == 0) return MOE_OK;
   const WeightPtrs w1{static_cast<const uint8_t*>(w->w1), w->w1s, static_cast<const uint8_t*>(w->sw1), w->sw1s};
   const WeightPtrs w2{static_cast<const uint8_t*>(w->w2), w->w2s, static_cast<const uint8_t*>(w->sw2), w->sw2s};
   if (s.big) {
-    if ((rc = hip_status(launch_gemm1_big(s, xq, xs, rtok, offsets, w1, hq, hs, 1, st)))) return rc;
-    if ((rc = hip_status(launch_gemm2_big(s, hq, hs, offsets, w2, nullptr, yb, 1, st)))) return rc;
+    if ((rc = hip_status(launch_gemm1_big(s, B.xq, B.xs, B.row_token, B.offsets, w1, B.hq, B.hs, 1, st)))) return rc;
+    if ((rc = hip_status(launch_gemm2_big(s, B.hq, B.hs, B.offsets, w2, nullptr, B.yb, 1, st)))) return rc;
   } else {
-    if ((rc = hip_status(launch_gemm1(s, xq, xs, rtok, offsets, w1, hq, hs,
-                                      reinterpret_cast<float*>(b + L.part1), cnt1, st))))
+    if ((rc = hip_status(launch_gemm1(s, B.xq, B.xs, B.row_token, B.offsets, w1, B.hq, B.hs, B.part1, B.cnt1, st))))
       return rc;
-    if ((rc = hip_status(launch_gemm2(s, hq, hs, offsets, w2, nullptr, yb, reinterpret_cast<float*>(b + L.part2),
-                                      cnt2, st))))
-      return rc;
+    if ((rc = hip_status(launch_gemm2(s, B.hq, B.hs, B.offsets, w2, nullptr, B.yb, B.part2, B.cnt2, st)))) return rc;
   }
-  return hip_status(launch_combine(s, nullptr, yb, eidx, offsets, topk_weights, out, st));
+  return hip_status(launch_combine(s, nullptr, B.yb, B.expand_idx, B.offsets, topk_weights, out, st));
 }
 
 // Scratch of moe_layer_static: one file-scope device array, which every GPU
@@ -433,6 +442,28 @@ int moe_layer_static(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_
   char* base = nullptr;
   if ((rc = static_scratch(&base))) return rc;
   return enqueue_layer(s, L, x, topk_ids, topk_weights, w, out, base, static_cast<hipStream_t>(stream));
+}
+
+int moe_layer_persistent(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
+                         const moe_weights* w, uint16_t* out, void* ws, size_t ws_bytes, int32_t* status,
+                         void* stream) {
+  const bool has_rows = cfg && cfg->T > 0;
+  int rc = check_args(cfg, {{x, has_rows}, {topk_ids, has_rows}, {topk_weights, has_rows}, {out, has_rows},
+                            {ws, true}}, w, true);
+  if (rc) return rc;
+  const Shape s = shape_of(cfg);
+  const WsLayout L = make_ws_layout(s);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (s.T == 0) return MOE_OK;
+  if (!persistent_supported(s)) return MOE_ERR_UNSUPPORTED;
+  char* base = static_cast<char*>(ws);
+  const LayerBufs b = layer_bufs(L, base);
+  const WeightPtrs w1{static_cast<const uint8_t*>(w->w1), w->w1s, static_cast<const uint8_t*>(w->sw1), w->sw1s};
+  const WeightPtrs w2{static_cast<const uint8_t*>(w->w2), w->w2s, static_cast<const uint8_t*>(w->sw2), w->sw2s};
+  return hip_status(launch_layer_persistent(s, x, topk_ids, topk_weights, w1, w2, b,
+                                            reinterpret_cast<int32_t*>(base + L.chunk_cnt), out,
+                                            reinterpret_cast<int32_t*>(base + L.pctl), status,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_weights* packed, void* stream) {

@@ -21,6 +21,9 @@
 // decode), so weight rows sit on the 16-row MFMA side and stream straight
 // from HBM into registers, while the few tokens of an expert form the
 // 16-column side.
+#include <algorithm>
+#include <mutex>
+
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -48,6 +51,7 @@ struct RouteParams {
   int chunk, nchunks;  // slots per chunk; nchunks == 1: one block places every slot
   int T, H, k, E, G, shared;
   int af;              // 1: MXFP4 activations (e2m1 codes, e8m0 per 32) instead of e4m3 per G
+  int32_t* zero1;      // optional: one more word block 0 zeroes (the persistent layer's status)
 };
 
 // Place slots [c0, c1) (chunk b of nb): expert histogram of the chunk, the
@@ -176,6 +180,7 @@ __device__ void permute_chunk(const RouteParams& p, int b, int nb, int c0, int c
   const int cap = n + (p.shared ? p.T : 0);
   for (int r = R + tid; r < cap; r += kThreads) p.row_token[r] = -1;
   for (int q = tid; q < p.nclear; q += kThreads) p.clear[q] = 0;
+  if (tid == 0 && p.zero1) *p.zero1 = 0;
 }
 
 // chunked mode, first pass: expert counts of chunk b into p.chunk_cnt[b][:]
@@ -239,14 +244,16 @@ __device__ void quant_block(const RouteParams& p, int blk) {
   }
 }
 
-// blocks [0, nlead) route (the whole permute, or the chunk counts), the
+// units [0, nlead) route (the whole permute, or the chunk counts), the
 // rest quantise
-__global__ __launch_bounds__(kThreads) void k_route_quant(RouteParams p) {
+__device__ __forceinline__ void route_quant_unit(const RouteParams& p, int b) {
   const int nlead = p.nchunks == 1 ? 1 : p.nchunks;
-  if (int(blockIdx.x) >= nlead) quant_block(p, blockIdx.x - nlead);
+  if (b >= nlead) quant_block(p, b - nlead);
   else if (p.nchunks == 1) permute_chunk(p, 0, 1, 0, p.T * p.k);
-  else count_chunk(p, blockIdx.x);
+  else count_chunk(p, b);
 }
+
+__global__ __launch_bounds__(kThreads) void k_route_quant(RouteParams p) { route_quant_unit(p, blockIdx.x); }
 
 // chunked mode, second pass: block b places chunk b's slots
 __global__ __launch_bounds__(kThreads) void k_permute_rank(RouteParams p) {
@@ -332,6 +339,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
 // scale loads: nt (non-temporal: each weight byte is read once per layer, so
 // its lines are not kept in the caches)
 constexpr int kNt = 2;
+constexpr int kSc1 = 16;  // cache-policy operand of the buffer intrinsics: sc1 (device-coherent)
+
+// Results that one workgroup writes and another, possibly on another XCD
+// (each XCD has its own L2), reads inside the same launch -- the persistent
+// layer's h and y rows -- travel through device-coherent (sc1) stores and
+// loads, which do not stop at a non-coherent L2; CO selects that form.
+template <bool CO>
+__device__ __forceinline__ void st_u32(uint32_t* p, uint32_t v) {
+  if (CO) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool CO>
+__device__ __forceinline__ void st_f32(float* p, float v) {
+  if (CO) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool CO>
+__device__ __forceinline__ float ld_f32(const float* p) {
+  if (CO) return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+template <bool CO>
+__device__ __forceinline__ void st_bf16x4(uint16_t* dst, const v4f& v) {
+  if (!CO) {
+    store_bf16x4(dst, v);
+    return;
+  }
+  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+  st_u32<true>(d, f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16));
+  st_u32<true>(d + 1, f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16));
+}
 
 template <int NJ, int NTT>
 struct KSrc {
@@ -343,7 +381,7 @@ struct KSrc {
   int wstep, sstep, astep;  // bytes per K step: weight tiles, scale tiles, activation scales
 };
 
-template <int WF, int NJ, int NTT, int B32>
+template <int WF, int NJ, int NTT, int B32, bool CO>
 __device__ __forceinline__ void load_frag(Frag<WF, NJ, NTT>& f, const KSrc<NJ, NTT>& src,
                                           const float* const (&wsc)[NJ], int ks) {
   const int kw = ks * src.wstep, ksc = ks * src.sstep, ka = ks * 128, kx = ks * src.astep;
@@ -361,14 +399,14 @@ __device__ __forceinline__ void load_frag(Frag<WF, NJ, NTT>& f, const KSrc<NJ, N
   }
 #pragma unroll
   for (int t = 0; t < NTT; ++t) {
-    const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(src.ar, src.bo[t], ka, 0);
-    const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(src.ar, src.bo[t] + 64, ka, 0);
+    const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(src.ar, src.bo[t], ka, CO ? kSc1 : 0);
+    const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(src.ar, src.bo[t] + 64, ka, CO ? kSc1 : 0);
     f.b[t] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
-    if (!B32) f.xsv[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(src.xr, src.xo[t], kx, 0));
+    if (!B32) f.xsv[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(src.xr, src.xo[t], kx, CO ? kSc1 : 0));
   }
 }
 
-template <int WF, int NJ, int NTT, int B32>
+template <int WF, int NJ, int NTT, int B32, bool CO>
 __device__ __forceinline__ void mma_frag(v4f (&acc)[NJ][NTT], const Frag<WF, NJ, NTT>& f,
                                          const float* const (&wsc)[NJ], const float* const (&bsc)[NTT],
                                          int ks, int g) {
@@ -383,7 +421,7 @@ __device__ __forceinline__ void mma_frag(v4f (&acc)[NJ][NTT], const Frag<WF, NJ,
 #pragma unroll
         for (int t = 0; t < NTT; ++t) {
           const v4f d = mfma_scaled<kFmtE4M3, kFmtE4M3>(am, f.b[t], kUnitScale, kUnitScale);
-          acc[j][t] += d * (ws * bsc[t][ks * 4 + sb]);
+          acc[j][t] += d * (ws * ld_f32<CO>(&bsc[t][ks * 4 + sb]));
         }
       }
     }
@@ -414,21 +452,21 @@ __device__ __forceinline__ void mma_frag(v4f (&acc)[NJ][NTT], const Frag<WF, NJ,
 // The loads are unconditional (past the end they repeat the last step and
 // hit in cache) so the compiler can count outstanding loads exactly and
 // wait only for the stage about to be used; only the MFMAs are predicated.
-template <int WF, int NJ, int NTT, int B32, int ST>
+template <int WF, int NJ, int NTT, int B32, int ST, bool CO = false>
 __device__ __forceinline__ void kloop(v4f (&acc)[NJ][NTT], const KSrc<NJ, NTT>& src, const float* const (&wsc)[NJ],
                                       const float* const (&bsc)[NTT], int ks0, int ks1, int g) {
   Frag<WF, NJ, NTT> f[ST];
 #pragma unroll
   for (int s = 0; s < ST - 1; ++s) {
-    load_frag<WF, NJ, NTT, B32>(f[s], src, wsc, min(ks0 + s, ks1 - 1));
+    load_frag<WF, NJ, NTT, B32, CO>(f[s], src, wsc, min(ks0 + s, ks1 - 1));
     __builtin_amdgcn_sched_barrier(0);  // keep each stage's loads together, in stage order
   }
   for (int ks = ks0; ks < ks1; ks += ST) {
 #pragma unroll
     for (int s = 0; s < ST; ++s) {
-      load_frag<WF, NJ, NTT, B32>(f[(s + ST - 1) % ST], src, wsc, min(ks + s + ST - 1, ks1 - 1));
+      load_frag<WF, NJ, NTT, B32, CO>(f[(s + ST - 1) % ST], src, wsc, min(ks + s + ST - 1, ks1 - 1));
       __builtin_amdgcn_sched_barrier(0);
-      if (ks + s < ks1) mma_frag<WF, NJ, NTT, B32>(acc, f[s], wsc, bsc, ks + s, g);
+      if (ks + s < ks1) mma_frag<WF, NJ, NTT, B32, CO>(acc, f[s], wsc, bsc, ks + s, g);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -465,8 +503,6 @@ struct GemmParams {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const float* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7FFFFFFF, 0x00020000);
 }
-constexpr int kSc1 = 16;  // cache-policy operand of the buffer intrinsics: sc1
-
 __device__ __forceinline__ void st_coherent(__amdgpu_buffer_rsrc_t r, long elem, const v4f& v) {
   const v4u u = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
   __builtin_amdgcn_raw_buffer_store_b128(u, r, int(elem * 4), 0, kSc1);
@@ -495,7 +531,7 @@ __device__ __forceinline__ bool arrive_last(int32_t* counter, int S, int* s_flag
 // n0+32w+16j+(0..15) and j = 2,3 the up rows I+n0+32w+16(j-2)+(0..15), so
 // the gate and up values of one h element land in the same lane.
 // ---------------------------------------------------------------------
-template <int NTT>
+template <int NTT, bool CO>
 __device__ __forceinline__ void swiglu_requant_store(const v4f (&acc)[4][NTT], const GemmParams& p, int row0,
                                                      int ne, int pass, int n0, float (*s_red)[4][16]) {
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 15, g = lane >> 4;
@@ -535,13 +571,13 @@ __device__ __forceinline__ void swiglu_requant_store(const v4f (&acc)[4][NTT], c
     for (int jt = 0; jt < 2; ++jt) {
       const float* hv = h[t] + jt * 4;
       const uint32_t word = enc_e4m3x4(hv[0] * mult, hv[1] * mult, hv[2] * mult, hv[3] * mult);
-      *reinterpret_cast<uint32_t*>(p.hq + r * p.I + n0 + 32 * w + 16 * jt + 4 * g) = word;
+      st_u32<CO>(reinterpret_cast<uint32_t*>(p.hq + r * p.I + n0 + 32 * w + 16 * jt + 4 * g), word);
     }
     if (g == 0) {
       if (p.G == 128) {
-        if (w == 0) p.hs[r * (p.I / 128) + n0 / 128] = 1.0f / mult;
+        if (w == 0) st_f32<CO>(p.hs + r * (p.I / 128) + n0 / 128, 1.0f / mult);
       } else {
-        p.hs[r * (p.I / 32) + (n0 + 32 * w) / 32] = 1.0f / mult;
+        st_f32<CO>(p.hs + r * (p.I / 32) + (n0 + 32 * w) / 32, 1.0f / mult);
       }
     }
   }
@@ -551,16 +587,21 @@ __device__ __forceinline__ void swiglu_requant_store(const v4f (&acc)[4][NTT], c
 // workgroups per CU, which runs a 64-expert T = 64 layer's 768 units in one
 // round instead of one and a half), one token tile at 128 (four per CU); the
 // compiler fits both without spills.
-template <int WF, int NTT, int B32>
-__global__ __launch_bounds__(kThreads, B32 ? 1 : NTT == 2 ? 3 : NTT == 1 ? 4 : 1) void k_gemm1(GemmParams p) {
+template <int NTT>
+constexpr int gemm1_occupancy(int b32) { return b32 ? 1 : NTT == 2 ? 3 : NTT == 1 ? 4 : 1; }
+
+// Unit u of GEMM1.  Returns true (in every thread) when this workgroup
+// stored a finished 128-column slice of h: the only split (S == 1) or the
+// last to arrive.
+template <int WF, int NTT, int B32, bool CO = false>
+__device__ __forceinline__ bool gemm1_unit(const GemmParams& p, int u) {
   __shared__ int s_wsum[4], s_res[2], s_flag;
   __shared__ float s_red[NTT][4][16];
   const int S = p.S, nt = p.ntiles;
-  const int u = blockIdx.x;
   const int split = u % S, tile = (u / S) % nt, item = u / (S * nt);
   int pass0 = 0;
   const int e = nth_item(p.offsets, p.ngroups, item, 16 * NTT, &pass0, s_wsum, s_res);
-  if (e < 0) return;
+  if (e < 0) return false;
   const int row0 = p.offsets[e], ne = p.offsets[e + 1] - row0;
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 15, g = lane >> 4;
   const int H = p.H, I = p.I, n0 = tile * 128;
@@ -611,7 +652,8 @@ __global__ __launch_bounds__(kThreads, B32 ? 1 : NTT == 2 ? 3 : NTT == 1 ? 4 : 1
       for (int t = 0; t < NTT; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     kloop<WF, 4, NTT, B32, kStages>(acc, src, wsc, bsc, ks0, ks1, g);
     if (S == 1) {
-      swiglu_requant_store<NTT>(acc, p, row0, ne, pass, n0, s_red);
+      swiglu_requant_store<NTT, CO>(acc, p, row0, ne, pass, n0, s_red);
+      return true;
     } else {
 #pragma unroll
       for (int t = 0; t < NTT; ++t) {
@@ -626,8 +668,7 @@ __global__ __launch_bounds__(kThreads, B32 ? 1 : NTT == 2 ? 3 : NTT == 1 ? 4 : 1
       }
     }
   }
-  if (S == 1) return;
-  if (!arrive_last(p.cnt + item * nt + tile, S, &s_flag)) return;
+  if (!arrive_last(p.cnt + item * nt + tile, S, &s_flag)) return false;
   {
     const int pass = pass0;
     v4f acc[4][NTT];
@@ -643,8 +684,14 @@ __global__ __launch_bounds__(kThreads, B32 ? 1 : NTT == 2 ? 3 : NTT == 1 ? 4 : 1
         acc[j][t] = s;
       }
     }
-    swiglu_requant_store<NTT>(acc, p, row0, ne, pass, n0, s_red);
+    swiglu_requant_store<NTT, CO>(acc, p, row0, ne, pass, n0, s_red);
   }
+  return true;
+}
+
+template <int WF, int NTT, int B32>
+__global__ __launch_bounds__(kThreads, gemm1_occupancy<NTT>(B32)) void k_gemm1(GemmParams p) {
+  gemm1_unit<WF, NTT, B32>(p, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------
@@ -653,15 +700,23 @@ __global__ __launch_bounds__(kThreads, B32 ? 1 : NTT == 2 ? 3 : NTT == 1 ? 4 : 1
 // units: twice the weight bytes in flight per wave; NJ = 8 for MXFP4, whose
 // tiles carry half the bytes).
 // ---------------------------------------------------------------------
-template <int WF, int NTT, int B32, int NJ>
-__global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
+// Unit u of GEMM2.  `ready(item)` is called (block-wide) once the unit's
+// work item is known to hold rows; it returns when the item's h rows may be
+// read, false if they never will be (the unit is then skipped).
+struct Always {
+  __device__ bool operator()(int) const { return true; }
+};
+
+// Returns the unit's work item, or -1 when the item holds no rows.
+template <int WF, int NTT, int B32, int NJ, bool CO, class Ready>
+__device__ __forceinline__ int gemm2_unit(const GemmParams& p, int u, const Ready& ready) {
   __shared__ int s_wsum[4], s_res[2], s_flag;
   const int S = p.S, nt = p.ntiles;
-  const int u = blockIdx.x;
   const int split = u % S, tile = (u / S) % nt, item = u / (S * nt);
   int pass0 = 0;
   const int e = nth_item(p.offsets, p.ngroups, item, 16 * NTT, &pass0, s_wsum, s_res);
-  if (e < 0) return;
+  if (e < 0) return -1;
+  if (!ready(item)) return item;
   const int row0 = p.offsets[e], ne = p.offsets[e + 1] - row0;
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, m = lane & 15, g = lane >> 4;
   constexpr int kRows = 64 * NJ;  // output rows of a unit
@@ -709,7 +764,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int t = 0; t < NTT; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    kloop<WF, NJ, NTT, B32, kStages>(acc, src, wsc, bsc, ks0, ks1, g);
+    kloop<WF, NJ, NTT, B32, kStages, CO>(acc, src, wsc, bsc, ks0, ks1, g);
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
       const int idx = pass * 16 * NTT + t * 16 + m;
@@ -719,7 +774,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
       for (int j = 0; j < NJ; ++j) {
         const int col = 16 * NJ * w + 16 * j + 4 * g;
         if (S == 1) {
-          if (p.yb) store_bf16x4(p.yb + r * H + n0 + col, acc[j][t]);
+          if (p.yb) st_bf16x4<CO>(p.yb + r * H + n0 + col, acc[j][t]);
           else *reinterpret_cast<v4f*>(p.y + r * H + n0 + col) = acc[j][t];
         }
         else
@@ -727,8 +782,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
       }
     }
   }
-  if (S == 1) return;
-  if (!arrive_last(p.cnt + item * nt + tile, S, &s_flag)) return;
+  if (S == 1) return item;
+  if (!arrive_last(p.cnt + item * nt + tile, S, &s_flag)) return item;
   // reduce the S partial sums in split order: kRows columns x the pass's rows
   constexpr int kQ = kRows / 4;  // 4-column pieces per row
   const int r0 = pass0 * 16 * NTT, nr = min(ne - r0, 16 * NTT);
@@ -738,9 +793,15 @@ __global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
     v4f s = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int sp = 0; sp < S; ++sp)
       s += ld_coherent(prs, ((long(sp) * nt + tile) * p.rows_cap + r) * kRows + col);
-    if (p.yb) store_bf16x4(p.yb + r * H + n0 + col, s);
+    if (p.yb) st_bf16x4<CO>(p.yb + r * H + n0 + col, s);
     else *reinterpret_cast<v4f*>(p.y + r * H + n0 + col) = s;
   }
+  return item;
+}
+
+template <int WF, int NTT, int B32, int NJ>
+__global__ __launch_bounds__(kThreads) void k_gemm2(GemmParams p) {
+  gemm2_unit<WF, NTT, B32, NJ, false>(p, blockIdx.x, Always{});
 }
 
 // =====================================================================
@@ -764,11 +825,12 @@ struct CombineParams {
 // leaves the ascending-order fp32 sum unchanged.
 template <int NV> struct Row { v4f h[NV / 4]; };
 
-template <int NV>
+template <int NV, bool CO>
 __device__ __forceinline__ Row<NV> load_row(const CombineParams& p, long r, int c) {
   Row<NV> v;
   if (NV == 8) {
-    const v4u u = *reinterpret_cast<const v4u*>(p.yb + r * p.H + c);
+    const v4u u = CO ? __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(p.yb), int((r * p.H + c) * 2), 0, kSc1)
+                     : *reinterpret_cast<const v4u*>(p.yb + r * p.H + c);
 #pragma unroll
     for (int h = 0; h < NV / 4; ++h)
       v.h[h] = v4f{bf16_to_f32(u[2 * h] & 0xFFFFu), bf16_to_f32(u[2 * h] >> 16), bf16_to_f32(u[2 * h + 1] & 0xFFFFu),
@@ -779,12 +841,13 @@ __device__ __forceinline__ Row<NV> load_row(const CombineParams& p, long r, int 
   return v;
 }
 
-template <int NV>
-__global__ __launch_bounds__(kThreads) void k_combine(CombineParams p) {
+// unit b = (token b / nchunk, channel chunk b % nchunk)
+template <int NV, bool CO = false>
+__device__ __forceinline__ void combine_unit(const CombineParams& p, int b) {
   constexpr int kChunk = kThreads * NV;
   const int nchunk = (p.H + kChunk - 1) / kChunk;
-  const long t = blockIdx.x / nchunk;
-  const int c = (blockIdx.x % nchunk) * kChunk + threadIdx.x * NV;
+  const long t = b / nchunk;
+  const int c = (b % nchunk) * kChunk + threadIdx.x * NV;
   const int k = p.k;
   const int* ids = p.expand_idx + t * k;
   const float* tw = p.tw + t * k;
@@ -805,7 +868,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineParams p) {
         const int j = j0 + jj;
         const int r = j < k ? ids[j] : -1;
         wj[jj] = r >= 0 ? tw[j] : 0.0f;
-        v[jj] = load_row<NV>(p, r >= 0 ? r : pad, c);
+        v[jj] = load_row<NV, CO>(p, r >= 0 ? r : pad, c);
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj)
@@ -813,7 +876,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineParams p) {
         for (int h = 0; h < NV / 4; ++h) acc.h[h] += wj[jj] * v[jj].h[h];
     }
     if (srow >= 0) {
-      const Row<NV> v = load_row<NV>(p, srow, c);
+      const Row<NV> v = load_row<NV, CO>(p, srow, c);
 #pragma unroll
       for (int h = 0; h < NV / 4; ++h) acc.h[h] += v.h[h];
     }
@@ -828,14 +891,217 @@ __global__ __launch_bounds__(kThreads) void k_combine(CombineParams p) {
   else *reinterpret_cast<uint2*>(p.out + t * p.H + c) = uint2{o[0], o[1]};
 }
 
+template <int NV>
+__global__ __launch_bounds__(kThreads) void k_combine(CombineParams p) { combine_unit<NV>(p, blockIdx.x); }
+
+// =====================================================================
+// persistent decode layer: GEMM1, GEMM2 and the combine in one launch
+// =====================================================================
+// After the routing and quantisation launch, a grid of as many workgroups
+// as fit on the chip at once works through the units of GEMM1, then
+// GEMM2, then the combine (each numbered as in its own launch; together
+// the tickets 0, 1, ...): workgroup b takes tickets b, b + grid, b + 2 grid,
+// ... in that order, so no shared counter is touched to hand out work.  A
+// unit waits only for units of lower tickets: a GEMM2 unit for the GEMM1
+// slices of its work item, a combine unit for the GEMM2 units of the work
+// items holding its token's rows.  With every workgroup running at once
+// (the grid is sized so), the lowest unfinished ticket always has its
+// inputs ready, so the launch always finishes.  The waits are bounded all
+// the same (a GPU shared with other work may not hold the whole grid): one
+// that expires is counted in the control block and in the caller's status
+// word, makes every later wait give up at once, and its unit is skipped.
+// The h and y rows cross XCDs inside the launch, so they are written and
+// read with device-coherent (sc1) accesses; a producing workgroup waits for
+// its stores to complete before one device-scope increment of its work
+// item's counter counts it in.  The control block lives in the workspace
+// and is zeroed by the routing launch.
+struct PersistParams {
+  GemmParams g1, g2;
+  CombineParams c;
+  const int32_t* ids;  // topk ids [T][k] (the combine finds its rows' work items)
+  int32_t* ctl;     // control block: kPersistCtlHead ints, then per work item the GEMM1 and the GEMM2 counters
+  int32_t* status;  // optional: expired waits (zeroed by the routing launch)
+  int n1, n2, nC;   // units of each step
+  int items;        // work items of either GEMM (the same passes)
+  int spin_limit;   // polls per wait before it expires
+};
+
+constexpr int kCtlExpired = 0;
+static_assert(kCtlExpired < kPersistCtlHead, "control block head");
+
+// The workgroup's stores have completed; then it counts itself in once.
+__device__ __forceinline__ void count_in(int32_t* c) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until *c >= target (block-wide answer): false if the wait expired
+// or an earlier one did.
+__device__ __forceinline__ bool wait_count(const int32_t* c, int target, int32_t* expired, int32_t* status,
+                                           int limit) {
+  __shared__ int s_ok;
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    for (int n = 0; __hip_atomic_load(const_cast<int32_t*>(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target;
+         ++n) {
+      if (__hip_atomic_load(expired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+        ok = 0;
+        break;
+      }
+      if (n >= limit) {
+        __hip_atomic_fetch_add(expired, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (status) __hip_atomic_fetch_add(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
+    }
+    s_ok = ok;
+  }
+  __syncthreads();
+  const bool ok = s_ok != 0;
+  __syncthreads();  // s_ok is rewritten by the next wait
+  return ok;
+}
+
+// The combine unit's wait: every work item holding one of token t's rows
+// (its routed slots, and the shared expert's row) has all its GEMM2 units
+// counted in.  An item is (group, pass of R rows); items are numbered group
+// by group, so a row's item is the item count of the groups before its
+// group plus its pass.
+__device__ bool wait_token_rows(const CombineParams& c, const int32_t* ids, int t, int R, const int32_t* items2,
+                                int per_item, int32_t* expired, int32_t* status, int limit) {
+  __shared__ int s_base[1024 + 2];  // items of groups [0, g), g <= E + shared <= 1025
+  __shared__ int s_wsum[4];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int ngroups = c.E + c.shared;
+  const int gpt = (ngroups + kThreads - 1) / kThreads;
+  int local = 0;
+  for (int q = 0; q < gpt; ++q) {
+    const int g = tid * gpt + q;
+    if (g < ngroups) local += (c.offsets[g + 1] - c.offsets[g] + R - 1) / R;
+  }
+  int incl = local;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) s_wsum[w] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int q = 0; q < w; ++q) run += s_wsum[q];
+  for (int q = 0; q < gpt; ++q) {
+    const int g = tid * gpt + q;
+    if (g < ngroups) {
+      s_base[g] = run;
+      run += (c.offsets[g + 1] - c.offsets[g] + R - 1) / R;
+    }
+  }
+  __syncthreads();
+  // wave 0 polls the (at most k + 1 <= 33) counters side by side, lane j
+  // the item of slot j (the shared row in lane k)
+  __shared__ int s_ok;
+  if (w == 0) {
+    int item = -1;
+    if (lane < c.k) {
+      const int r = c.expand_idx[long(t) * c.k + lane];
+      if (r >= 0) {
+        const int g = ids[long(t) * c.k + lane];
+        item = s_base[g] + (r - c.offsets[g]) / R;
+      }
+    } else if (lane == c.k && c.shared) {
+      item = s_base[c.E] + t / R;
+    }
+    int ok = 1;
+    for (int n = 0;; ++n) {
+      const bool wait = item >= 0 &&
+                        __hip_atomic_load(const_cast<int32_t*>(items2) + item, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) < per_item;
+      if (__ballot(wait) == 0) break;
+      int stop = 0;
+      if (lane == 0) {
+        if (__hip_atomic_load(expired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+          stop = 1;
+        } else if (n >= limit) {
+          __hip_atomic_fetch_add(expired, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (status) __hip_atomic_fetch_add(status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          stop = 1;
+        }
+      }
+      if (__shfl(stop, 0, 64)) {
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
+    }
+    if (lane == 0) s_ok = ok;
+  }
+  __syncthreads();
+  const bool ok = s_ok != 0;
+  __syncthreads();
+  return ok;
+}
+
+// The launch's arguments, read through a pointer the compiler cannot see
+// through: each unit loads the part it needs when it starts, instead of
+// every step's arguments staying live in scalar registers over the loop
+// (which spills them).
+typedef const PersistParams __attribute__((address_space(4)))* PersistArgs;
+__device__ __forceinline__ const PersistParams* persist_args() {
+  PersistArgs a = (PersistArgs)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(a));
+  return (const PersistParams*)a;
+}
+
+// Workgroups per CU the persistent kernel is compiled for: GEMM1's, or two
+// (one with two token tiles) when GEMM2 takes eight weight tiles per wave.
+template <int NTT, int B32, int NJ>
+constexpr int persist_occupancy() {
+  return NJ == 8 ? (NTT == 1 ? 2 : 1) : gemm1_occupancy<NTT>(B32);
+}
+
+template <int WF, int NTT, int B32, int NJ>
+__global__ __launch_bounds__(kThreads, (persist_occupancy<NTT, B32, NJ>())) void k_layer_persistent(PersistParams p) {
+  int32_t* const ctl = p.ctl;
+  int32_t* const expired = ctl + kCtlExpired;
+  int32_t* const items1 = ctl + kPersistCtlHead;
+  int32_t* const items2 = items1 + p.items;
+  int32_t* const status = p.status;
+  const int lim = p.spin_limit;
+  const int e2 = p.n1, e3 = e2 + p.n2, total = e3 + p.nC;
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    __syncthreads();  // the previous unit is done with its LDS
+    if (t < e2) {
+      const GemmParams g1 = persist_args()->g1;
+      if (gemm1_unit<WF, NTT, B32, true>(g1, t)) count_in(items1 + t / (g1.S * g1.ntiles));
+    } else if (t < e3) {
+      const int nt1 = persist_args()->g1.ntiles;
+      const GemmParams g2 = persist_args()->g2;
+      const int item = gemm2_unit<WF, NTT, B32, NJ, true>(
+          g2, t - e2, [=](int it) { return wait_count(items1 + it, nt1, expired, status, lim); });
+      if (item >= 0) count_in(items2 + item);
+    } else {
+      const CombineParams c = persist_args()->c;
+      const GemmParams& g2 = persist_args()->g2;
+      const int nchunk = (c.H + kThreads * 8 - 1) / (kThreads * 8);
+      const int u = t - e3;
+      if (wait_token_rows(c, persist_args()->ids, u / nchunk, 16 * NTT, items2, g2.S * g2.ntiles, expired, status,
+                          lim))
+        combine_unit<8, true>(c, u);
+    }
+  }
+}
+
 // =====================================================================
 // host launchers
 // =====================================================================
 hipError_t launch_route_quant(const Shape& s, const uint16_t* x, const int32_t* ids, int32_t* counts,
                               int32_t* offsets, int32_t* expand_idx, int32_t* row_token, uint8_t* xq,
-                              float* xs, int32_t* clear, int nclear, int32_t* chunk_cnt, hipStream_t st) {
+                              float* xs, int32_t* clear, int nclear, int32_t* chunk_cnt, hipStream_t st,
+                              int32_t* zero1) {
   RouteParams p{x, ids, counts, offsets, expand_idx, row_token, xq, xs, reinterpret_cast<uint8_t*>(xs), clear, nclear,
-                chunk_cnt, s.perm_chunk, s.perm_chunks, s.T, s.H, s.k, s.E, s.G, s.shared, s.af};
+                chunk_cnt, s.perm_chunk, s.perm_chunks, s.T, s.H, s.k, s.E, s.G, s.shared, s.af, zero1};
   const long items = long(s.T) * (s.H / 8);
   const long nq = (items + kThreads - 1) / kThreads;
   const int nlead = s.perm_chunks == 1 ? 1 : s.perm_chunks;
@@ -928,6 +1194,98 @@ hipError_t launch_combine(const Shape& s, const float* y, const uint16_t* yb, co
   if (yb) hipLaunchKernelGGL(k_combine<8>, dim3(unsigned(grid)), dim3(kThreads), 0, st, p);
   else hipLaunchKernelGGL(k_combine<4>, dim3(unsigned(grid)), dim3(kThreads), 0, st, p);
   return hipGetLastError();
+}
+
+// Workgroups of one persistent launch: as many as fit on the device at once
+// (the kernel's occupancy times the CU count), looked up once per device
+// and kernel.
+static int resident_grid(const void* fn) {
+  struct Entry { int dev; const void* fn; int grid; };
+  static Entry cache[256];
+  static int n = 0;
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < n; ++i)
+    if (cache[i].dev == dev && cache[i].fn == fn) return cache[i].grid;
+  int ncu = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess) return -1;
+  const int grid = std::max(1, ncu * std::max(1, per_cu));
+  if (n < 256) cache[n++] = Entry{dev, fn, grid};
+  return grid;
+}
+
+template <int WF, int NTT, int B32, int NJ>
+static hipError_t launch_persistent_inst(const PersistParams& p, int total, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&k_layer_persistent<WF, NTT, B32, NJ>);
+  const int grid = resident_grid(fn);
+  if (grid < 0) return hipErrorInvalidDevice;
+  hipLaunchKernelGGL((k_layer_persistent<WF, NTT, B32, NJ>), dim3(unsigned(std::min(grid, total))), dim3(kThreads),
+                     0, st, p);
+  return hipGetLastError();
+}
+
+bool persistent_supported(const Shape& s) {
+  return s.T > 0 && !s.big && s.af == 0 && s.g1_ntt == s.g2_ntt && s.g1_items <= kPersistMaxItems &&
+         (s.wfmt == 1 || s.g2_nj <= 4);
+}
+
+hipError_t launch_layer_persistent(const Shape& s, const uint16_t* x, const int32_t* ids, const float* tw,
+                                   WeightPtrs w1, WeightPtrs w2, const LayerBufs& b, int32_t* chunk_cnt,
+                                   uint16_t* out, int32_t* ctl, int32_t* status, hipStream_t st) {
+  if (!persistent_supported(s)) return hipErrorInvalidValue;
+  // routing and quantisation; also zeroes the control block (inside the
+  // cleared counter range) and the status word
+  const hipError_t e = launch_route_quant(s, x, ids, b.counts, b.offsets, b.expand_idx, b.row_token, b.xq, b.xs,
+                                          b.clear, b.nclear, chunk_cnt, st, status);
+  if (e != hipSuccess) return e;
+  PersistParams p{};
+  GemmParams& g1 = p.g1;
+  g1.act = b.xq; g1.act_s = b.xs; g1.row_token = b.row_token; g1.offsets = b.offsets;
+  g1.w = w1.w; g1.ws = w1.ws; g1.sw = w1.sw; g1.sws = w1.sws;
+  g1.hq = b.hq; g1.hs = b.hs; g1.part = b.part1; g1.cnt = b.cnt1;
+  g1.H = s.H; g1.I = s.I; g1.E = s.E; g1.G = s.G; g1.wblk = s.wblk; g1.ngroups = s.ngroups;
+  g1.S = s.g1_split; g1.ntiles = s.g1_tiles; g1.rows_cap = s.rows_cap;
+  GemmParams& g2 = p.g2;
+  g2.act = b.hq; g2.act_s = b.hs; g2.offsets = b.offsets;
+  g2.w = w2.w; g2.ws = w2.ws; g2.sw = w2.sw; g2.sws = w2.sws;
+  g2.yb = b.yb; g2.part = b.part2; g2.cnt = b.cnt2;
+  g2.H = s.H; g2.I = s.I; g2.E = s.E; g2.G = s.G; g2.wblk = s.wblk; g2.ngroups = s.ngroups;
+  g2.S = s.g2_split; g2.ntiles = s.g2_tiles; g2.rows_cap = s.rows_cap;
+  p.c = CombineParams{nullptr, b.yb, b.expand_idx, b.offsets, tw, out, s.H, s.k, s.E, s.shared};
+  p.ids = ids;
+  p.ctl = ctl;
+  p.status = status;
+  p.items = s.g1_items;
+  p.n1 = s.g1_items * s.g1_tiles * s.g1_split;
+  p.n2 = s.g2_items * s.g2_tiles * s.g2_split;
+  p.nC = s.T * ((s.H + kThreads * 8 - 1) / (kThreads * 8));
+  p.spin_limit = 1 << 20;
+  const int total = p.n1 + p.n2 + p.nC;
+  const bool b32 = s.wfmt == 0 && s.wblk == 32;
+#define MOE_P(WF, NTT, B32)                                                                       \
+  do {                                                                                            \
+    if (s.g2_nj == 2) return launch_persistent_inst<WF, NTT, B32, 2>(p, total, st);              \
+    if (s.g2_nj == 4) return launch_persistent_inst<WF, NTT, B32, 4>(p, total, st);              \
+    if (WF == 1) return launch_persistent_inst<1, NTT, 0, 8>(p, total, st);                      \
+  } while (0)
+  if (s.wfmt == 1) {
+    if (s.g1_ntt == 1) MOE_P(1, 1, 0);
+    else if (s.g1_ntt == 2) MOE_P(1, 2, 0);
+    else MOE_P(1, 4, 0);
+  } else if (b32) {
+    if (s.g1_ntt == 1) MOE_P(0, 1, 1);
+    else if (s.g1_ntt == 2) MOE_P(0, 2, 1);
+    else MOE_P(0, 4, 1);
+  } else {
+    if (s.g1_ntt == 1) MOE_P(0, 1, 0);
+    else if (s.g1_ntt == 2) MOE_P(0, 2, 0);
+    else MOE_P(0, 4, 0);
+  }
+#undef MOE_P
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

@@ -41,6 +41,7 @@ struct WsLayout {
   size_t xq, xs, hq, hs, y;                       // layer-internal activations
   size_t part1, part2;                            // split-K partial sums (fp32)
   size_t cnt1, cnt2;                              // split-K arrival counters (int32), per work item and tile
+  size_t pctl;                                    // persistent layer's control block (int32)
   size_t chunk_cnt;                               // permute per-chunk expert counts (int32)
   size_t total;
 };
@@ -55,9 +56,11 @@ struct WeightPtrs {
   const void* sws;
 };
 
+// clear: nclear ints zeroed by the routing block; zero1: one more int (or null)
 hipError_t launch_route_quant(const Shape& s, const uint16_t* x, const int32_t* ids, int32_t* counts,
                               int32_t* offsets, int32_t* expand_idx, int32_t* row_token, uint8_t* xq,
-                              float* xs, int32_t* clear, int nclear, int32_t* chunk_cnt, hipStream_t st);
+                              float* xs, int32_t* clear, int nclear, int32_t* chunk_cnt, hipStream_t st,
+                              int32_t* zero1 = nullptr);
 
 hipError_t launch_clear(int32_t* p, int n, hipStream_t st);
 
@@ -92,6 +95,34 @@ hipError_t launch_route_gemm(int T, int H, int E, int k, const uint16_t* x, cons
 
 hipError_t launch_tile_weights(int wfmt, int mats, int N, int K, const uint8_t* w, const uint8_t* s, uint8_t* w_tiled,
                                uint8_t* s_tiled, hipStream_t st);
+
+// The persistent decode layer (routing launch, then GEMM1, GEMM2 and the
+// combine in one launch).  Its control block, in the workspace, holds
+// kPersistCtlHead ints, then per work item a GEMM1 and a GEMM2 counter; the
+// routing launch zeroes it.
+constexpr int kPersistCtlHead = 128;
+constexpr int kPersistMaxItems = 1 << 20;
+
+// The layer's buffers inside a workspace (see WsLayout).
+struct LayerBufs {
+  int32_t *counts, *offsets, *expand_idx, *row_token;
+  uint8_t* xq;
+  float* xs;
+  uint8_t* hq;
+  float* hs;
+  uint16_t* yb;
+  float *part1, *part2;
+  int32_t *cnt1, *cnt2;
+  int32_t* clear;  // the split-K counters the routing unit zeroes (nclear ints)
+  int nclear;
+};
+
+// Shapes the persistent layer runs: the decode kernels (not the many-row
+// ones), FP8 activations.
+bool persistent_supported(const Shape& s);
+hipError_t launch_layer_persistent(const Shape& s, const uint16_t* x, const int32_t* ids, const float* tw,
+                                   WeightPtrs w1, WeightPtrs w2, const LayerBufs& b, int32_t* chunk_cnt,
+                                   uint16_t* out, int32_t* ctl, int32_t* status, hipStream_t st);
 
 // y: GEMM2 output rows in fp32, or yb in bf16 (the layer's internal form; y unused then)
 hipError_t launch_combine(const Shape& s, const float* y, const uint16_t* yb, const int32_t* expand_idx, const int32_t* offsets,

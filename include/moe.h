@@ -196,6 +196,34 @@ int moe_combine(const moe_cfg* cfg, const float* y, const int32_t* expand_idx, c
 int moe_layer(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids, const float* topk_weights,
               const moe_weights* w, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Steps 1-8 with GEMM1, GEMM2 and the combine in ONE persistent launch
+ * (after the routing and quantisation launch), for decode shapes: the
+ * layer's chain of launches collapsed into one kernel whose dependent steps
+ * run on device-side counters (the GC-MoE abstract runs its decode layer as
+ * a CUDA graph of three nodes; the FusedDeepMoE family analysis keeps the
+ * GMM1 -> SwiGLU -> GMM2 -> combine chain inside one operator, unified
+ * execution flow figure).  A grid of about as many workgroups as fit on the
+ * GPU takes GEMM1's, GEMM2's and the combine's units in that order from one
+ * ticket counter; a unit waits only for units of earlier tickets (a GEMM2
+ * unit for its work item's GEMM1 slices, the combine for GEMM2), so the
+ * launch always finishes.  The h and y rows pass between workgroups through
+ * device-coherent loads and stores.  Same arithmetic as moe_layer: the
+ * output is bit-identical to moe_layer's for the same inputs.
+ * Arguments as moe_layer (ws of at least moe_workspace_size(cfg) bytes; its
+ * counters are zeroed by the routing launch), plus
+ *   status  int32 device pointer or NULL: set to the number of waits that
+ *           expired (each wait gives up after about a second, its unit is
+ *           skipped and every later wait gives up at once; 0 in every
+ *           correct run -- a nonzero value means the output is not valid).
+ * Shapes: those moe_layer runs on its decode kernels (few rows per expert)
+ * with FP8 activations; others return MOE_ERR_UNSUPPORTED (host check,
+ * before any launch).  T == 0 returns MOE_OK without a launch.  Like
+ * moe_layer, calls on one workspace must not overlap; the call allocates
+ * nothing and enqueues only kernels (it can be captured in a graph). */
+int moe_layer_persistent(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_ids,
+                         const float* topk_weights, const moe_weights* w, uint16_t* out, void* ws,
+                         size_t ws_bytes, int32_t* status, void* stream);
+
 /* The router in front of the layer, one kernel (the routing GEMM and the
  * routing selection fused, as the DeepGEMM 26/09 news page describes its
  * Mega Gate): for every token t,

@@ -309,3 +309,29 @@ def test_binding_declares_every_parameter(lib):
         assert m, n
         nargs = len([a for a in m.group(1).split(",") if a.strip()])
         assert len(getattr(L, n).argtypes or []) == nargs, n
+
+
+def test_persistent_layer_host_checks(lib):
+    """moe_layer_persistent checks moe_layer's arguments, then refuses on the
+    host the shapes it does not run (many-row kernels, MXFP4 activations)
+    with MOE_ERR_UNSUPPORTED; T = 0 is a no-op."""
+    P = lambda v: None if v is None else C.c_void_p(v)
+
+    def call(c, x=FAKE, nbytes=None, w=None):
+        cc = c.c()
+        n = ws_size(c)[1] if nbytes is None else nbytes
+        w = _w() if w is None else w
+        return moe.raw_call("moe_layer_persistent", C.byref(cc), P(x), P(FAKE), P(FAKE), C.byref(w), P(FAKE),
+                            P(FAKE), C.c_size_t(n), None, None)
+
+    c = cfg(T=4, H=512, I=256, E=8, topk=2, wblk=128, act_group=128)
+    assert call(c, x=None) == moe.MOE_ERR_NULL_ARG
+    assert call(c, x=FAKE + 2) == moe.MOE_ERR_MISALIGNED
+    assert call(c, nbytes=ws_size(c)[1] - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(c, w=_w(prepacked=0)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(cfg(T=0, H=512, I=256, E=8, topk=2, wblk=128, act_group=128), x=None) == moe.MOE_OK
+    # many rows per expert: the many-row kernels, not this launch
+    assert call(cfg(T=700, H=512, I=256, E=4, topk=2, wblk=128, act_group=128)) == moe.MOE_ERR_UNSUPPORTED
+    # 4-bit activations run the many-row kernels at every T
+    a4 = cfg(T=4, H=512, I=256, E=8, topk=2, wfmt=1, wblk=32, act_group=32, act_fmt=1)
+    assert call(a4) == moe.MOE_ERR_UNSUPPORTED
