@@ -37,7 +37,8 @@ class Cfg(C.Structure):
 
 
 class WSet(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in ("w1", "w1s", "w2", "w2s", "sw1", "sw1s", "sw2", "sw2s")]
+    _fields_ = [(n, C.c_void_p) for n in ("w1", "w1s", "w2", "w2s", "sw1", "sw1s", "sw2", "sw2s",
+                                          "w1g", "w2g", "sw1g", "sw2g")]
 
 
 def lib() -> C.CDLL:
@@ -213,6 +214,10 @@ class Layer:
             _np(weights.sw2, np.uint8) if weights.sw2 is not None else None,
             _np(weights.sw2s, f32) if weights.sw2s is not None else None,
         ]
+        # NVFP4: the fp32 scale of every expert matrix
+        for n in ("w1g", "w2g", "sw1g", "sw2g"):
+            g = getattr(weights, n, None)
+            self._keep.append(None if g is None else _np(g, np.float32))
         self.wset = WSet(*[_p(a) for a in self._keep])
 
     @classmethod

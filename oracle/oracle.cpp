@@ -39,6 +39,12 @@
 //   e2m1: bias 1, magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}
 //   e8m0: 2^(c-127), c = 255 is NaN
 //
+// NVFP4 weights (wfmt 2; the pages name the format beside MXFP4 without
+// defining it, so this is the published two-level definition): e2m1 codes
+// packed two per byte (even K in the low nibble), one e4m3 scale per 16
+// consecutive K of a row, and one fp32 scale per expert matrix; the weight
+// is code * block scale * matrix scale.
+//
 // Activation formats (act_fmt): 0 = the FP8 rule above (e4m3 codes, one fp32
 // scale per G channels); 1 = MXFP4 activations, the 4-bit-activation variant
 // the FusedDeepMoE page describes for W4A8 (here e2m1 codes with one e8m0
@@ -232,6 +238,10 @@ struct WSet {
   const void* sw1s;
   const uint8_t* sw2;
   const void* sw2s;
+  const float* w1g;  // NVFP4: one fp32 scale per expert matrix ([E]; the shared expert's [1])
+  const float* w2g;
+  const float* sw1g;
+  const float* sw2g;
 };
 
 // Decoded value of every code, filled once from the decoders above (the
@@ -267,10 +277,15 @@ double wval(const Cfg& c, const WSet& w, int which, int e, int64_t n, int64_t kk
     if (g_mutation == 2 && kb == 0) return code;  // planted: drop the first K-block scale
     return code * double(s[(ee * (N / b) + n / b) * (K / b) + kb]);
   }
-  // MXFP4: packed e2m1 (even K in the low nibble) + e8m0 per 32 along K
+  // MXFP4 / NVFP4: packed e2m1 (even K in the low nibble)
   const uint8_t byte = codes[(ee * N + n) * (K / 2) + kk / 2];
   const uint8_t nib = (kk & 1) ? (byte >> 4) : (byte & 15);
   const uint8_t* s = static_cast<const uint8_t*>(sc);
+  if (c.wfmt == 2) {  // NVFP4: e4m3 per 16 along K, times the matrix's fp32 scale
+    const float* g = which == 1 ? (sh ? w.sw1g : w.w1g) : (sh ? w.sw2g : w.w2g);
+    return tab.e2m1[nib] * tab.e4m3[s[(ee * N + n) * (K / 16) + kk / 16]] * double(g[ee]);
+  }
+  // MXFP4: e8m0 per 32 along K
   return tab.e2m1[nib] * tab.e8m0[s[(ee * N + n) * (K / 32) + kk / 32]];
 }
 

@@ -19,6 +19,11 @@ Weight quantisation for the generator (inputs arrive already quantised):
     with one e8m0 power-of-two scale per 32 elements along K, using the
     Microscaling rule X = 2^(floor(log2 amax) - 2) and round-to-nearest-even
     with saturation at +-6.
+  * NVFP4: e2m1 codes packed the same way, one e4m3 scale per 16 elements
+    along K and one fp32 scale per expert matrix: matrix scale S = amax /
+    (448 * 6), block scale = e4m3(block amax / 6 / S) by PyTorch's cast,
+    codes = e2m1 of w / (block scale * S), round-to-nearest-even with
+    saturation at +-6 (a block whose scale is 0 gets zero codes).
 
 Random streams: every tensor draws from its own torch.Generator on the
 target device, seeded from (seed, workload, tensor id, expert).  A stream is
@@ -34,6 +39,7 @@ import torch
 
 FMT_FP8 = 0
 FMT_MXFP4 = 1
+FMT_NVFP4 = 2
 
 
 @dataclasses.dataclass(frozen=True)
@@ -44,8 +50,8 @@ class Workload:
     E: int
     topk: int
     I: int
-    wfmt: int            # FMT_FP8 or FMT_MXFP4
-    wblk: int            # FP8: b x b scale block edge; MXFP4: 32 along K
+    wfmt: int            # FMT_FP8, FMT_MXFP4 or FMT_NVFP4
+    wblk: int            # FP8: b x b scale block edge; MXFP4: 32 along K; NVFP4: 16 along K
     act_group: int       # activation / requantisation group along K
     routing: str         # "uniform" or "zipf"
     shared: bool         # one always-on shared expert with weight 1
@@ -69,6 +75,10 @@ WORKLOADS: Dict[str, Workload] = {
     "decode_mxfp4": Workload("decode_mxfp4", H=4096, E=64, topk=8, I=1536, wfmt=FMT_MXFP4, wblk=32,
                              act_group=128, routing="uniform", shared=False,
                              tokens=(1, 8, 32, 64, 128, 256), wid=2),
+    # decode NVFP4: same shapes and routing (e4m3 scale per 16, fp32 scale per matrix)
+    "decode_nvfp4": Workload("decode_nvfp4", H=4096, E=64, topk=8, I=1536, wfmt=FMT_NVFP4, wblk=16,
+                             act_group=128, routing="uniform", shared=False,
+                             tokens=(1, 8, 32, 64, 128, 256), wid=6),
     # large decode FP8, Zipf(1.2) routing, one shared expert
     "decode_fp8_zipf_shared": Workload("decode_fp8_zipf_shared", H=7168, E=256, topk=8, I=2048,
                                        wfmt=FMT_FP8, wblk=128, act_group=128, routing="zipf",
@@ -180,25 +190,60 @@ def _quant_mxfp4(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     return packed, code.to(torch.uint8)
 
 
+def _e2m1_rne(v: torch.Tensor) -> torch.Tensor:
+    """e2m1 codes (int32, sign in bit 3) of v, round to nearest even, saturating at +-6."""
+    a = v.abs()
+    nib = torch.zeros_like(a, dtype=torch.int32)
+    for i, mid in enumerate(_E2M1_MIDS):
+        nib += (a > mid).to(torch.int32)
+        if i % 2 == 1:                           # tie at an odd lower code goes up to the even one
+            nib += (a == mid).to(torch.int32)
+    return nib | (torch.signbit(v).to(torch.int32) << 3)
+
+
+def _quant_nvfp4(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """fp32 [N,K] -> (packed e2m1 uint8 [N,K/2], e4m3 block scales uint8 [N,K/16],
+    fp32 matrix scale [1])."""
+    N, K = w.shape
+    S = (w.abs().amax() / (_FP8_MAX * 6.0)).clamp_min(2.0 ** -100).reshape(1)
+    blk = w.reshape(N, K // 16, 16)
+    bs = (blk.abs().amax(dim=2) / 6.0 / S).clamp(max=_FP8_MAX).to(torch.float8_e4m3fn)
+    den = bs.to(torch.float32) * S
+    zero = den == 0
+    v = blk / torch.where(zero, torch.ones_like(den), den)[:, :, None]
+    nib = torch.where(zero[:, :, None], torch.zeros_like(v, dtype=torch.int32), _e2m1_rne(v)).reshape(N, K)
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).to(torch.uint8)
+    return packed, bs.view(torch.uint8), S
+
+
 def _gen_matrix_set(n_exp: int, N: int, K: int, wfmt: int, wblk: int, seed: int, wid: int,
-                    tid: int, device) -> Tuple[torch.Tensor, torch.Tensor]:
+                    tid: int, device):
+    """(codes, scales, matrix scales or None) of n_exp quantised [N,K] matrices."""
+    gsc = None
     if wfmt == FMT_FP8:
         codes = torch.empty(n_exp, N, K, dtype=torch.uint8, device=device)
         scales = torch.empty(n_exp, N // wblk, K // wblk, dtype=torch.float32, device=device)
-    else:
+    elif wfmt == FMT_MXFP4:
         codes = torch.empty(n_exp, N, K // 2, dtype=torch.uint8, device=device)
         scales = torch.empty(n_exp, N, K // 32, dtype=torch.uint8, device=device)
+    else:
+        codes = torch.empty(n_exp, N, K // 2, dtype=torch.uint8, device=device)
+        scales = torch.empty(n_exp, N, K // 16, dtype=torch.uint8, device=device)
+        gsc = torch.empty(n_exp, dtype=torch.float32, device=device)
     for e in range(n_exp):
         g = _gen(device, stream_seed(seed, wid, tid, e))
         w = torch.randn(N, K, generator=g, device=device, dtype=torch.float32) * 0.02
         if wfmt == FMT_FP8:
             q, s = _quant_fp8_blocks(w, wblk)
-        else:
+        elif wfmt == FMT_MXFP4:
             q, s = _quant_mxfp4(w)
+        else:
+            q, s, S = _quant_nvfp4(w)
+            gsc[e:e + 1].copy_(S)
         codes[e].copy_(q)
         scales[e].copy_(s)
         del w, q, s
-    return codes, scales
+    return codes, scales, gsc
 
 
 @dataclasses.dataclass
@@ -209,6 +254,8 @@ class Weights:
            w1s fp32 [E,2I/b,H/b]; w2 uint8 [E,H,I], w2s fp32 [E,H/b,I/b].
     MXFP4: w1 uint8 [E,2I,H/2], w1s uint8 e8m0 [E,2I,H/32];
            w2 uint8 [E,H,I/2],  w2s uint8 e8m0 [E,H,I/32].
+    NVFP4: w1 uint8 [E,2I,H/2], w1s uint8 e4m3 [E,2I,H/16], w1g fp32 [E];
+           w2 uint8 [E,H,I/2],  w2s uint8 e4m3 [E,H,I/16],  w2g fp32 [E].
     Shared expert (optional): the same with a leading dimension of 1.
     """
     w1: torch.Tensor
@@ -219,6 +266,10 @@ class Weights:
     sw1s: Optional[torch.Tensor] = None
     sw2: Optional[torch.Tensor] = None
     sw2s: Optional[torch.Tensor] = None
+    w1g: Optional[torch.Tensor] = None
+    w2g: Optional[torch.Tensor] = None
+    sw1g: Optional[torch.Tensor] = None
+    sw2g: Optional[torch.Tensor] = None
 
     def to(self, device) -> "Weights":
         f = lambda t: None if t is None else t.to(device)
@@ -226,24 +277,26 @@ class Weights:
 
     def nbytes_expert(self) -> int:
         """Bytes of one routed expert (codes + scales, W1 and W2)."""
-        return sum(t[0].numel() * t.element_size() for t in (self.w1, self.w1s, self.w2, self.w2s))
+        ts = [self.w1, self.w1s, self.w2, self.w2s] + [t for t in (self.w1g, self.w2g) if t is not None]
+        return sum(t[0].numel() * t.element_size() for t in ts)
 
     def nbytes_shared(self) -> int:
         if self.sw1 is None:
             return 0
-        return sum(t.numel() * t.element_size() for t in (self.sw1, self.sw1s, self.sw2, self.sw2s))
+        ts = [self.sw1, self.sw1s, self.sw2, self.sw2s] + [t for t in (self.sw1g, self.sw2g) if t is not None]
+        return sum(t.numel() * t.element_size() for t in ts)
 
 
 def gen_weights(wl: Workload, seed: int = 0, device="cpu") -> Weights:
     """Quantised expert weights for a workload (independent of T)."""
-    w1, w1s = _gen_matrix_set(wl.E, 2 * wl.I, wl.H, wl.wfmt, wl.wblk, seed, wl.wid, _TID_W1, device)
-    w2, w2s = _gen_matrix_set(wl.E, wl.H, wl.I, wl.wfmt, wl.wblk, seed, wl.wid, _TID_W2, device)
-    out = Weights(w1, w1s, w2, w2s)
+    w1, w1s, w1g = _gen_matrix_set(wl.E, 2 * wl.I, wl.H, wl.wfmt, wl.wblk, seed, wl.wid, _TID_W1, device)
+    w2, w2s, w2g = _gen_matrix_set(wl.E, wl.H, wl.I, wl.wfmt, wl.wblk, seed, wl.wid, _TID_W2, device)
+    out = Weights(w1, w1s, w2, w2s, w1g=w1g, w2g=w2g)
     if wl.shared:
-        out.sw1, out.sw1s = _gen_matrix_set(1, 2 * wl.I, wl.H, wl.wfmt, wl.wblk, seed, wl.wid,
-                                            _TID_SW1, device)
-        out.sw2, out.sw2s = _gen_matrix_set(1, wl.H, wl.I, wl.wfmt, wl.wblk, seed, wl.wid,
-                                            _TID_SW2, device)
+        out.sw1, out.sw1s, out.sw1g = _gen_matrix_set(1, 2 * wl.I, wl.H, wl.wfmt, wl.wblk, seed, wl.wid,
+                                                      _TID_SW1, device)
+        out.sw2, out.sw2s, out.sw2g = _gen_matrix_set(1, wl.H, wl.I, wl.wfmt, wl.wblk, seed, wl.wid,
+                                                      _TID_SW2, device)
     return out
 
 
