@@ -431,7 +431,7 @@ def prefill(moe, synth, torch, dev, reps, name="prefill_mxfp4"):
     g1_flops = 2.0 * R * (2 * wl.I) * wl.H
     g1_tf = g1_flops / (stages["gemm1_swiglu"] * 1e-6) / 1e12
     tf = flops / (med * 1e-6) / 1e12
-    meas = mfma_rate_tflops(moe, torch, dev, 2 if a4 else 1)
+    meas = mfma_rate_tflops(moe, torch, dev, moe.RATE_E2M1_E2M1 if a4 else 1)
     # floor of the layer on HBM: every weight byte + x in + out, at the peak
     act_bytes = 2 * 2 * T * wl.H
     hbm_floor_us = (wbytes_all + act_bytes) / (HBM_PEAK_GBS * 1e9) * 1e6

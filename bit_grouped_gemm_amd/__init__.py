@@ -45,6 +45,8 @@ MOE_ERR_HIP = 6
 
 WFMT_FP8_BLOCK = 0
 WFMT_MXFP4 = 1
+WFMT_NVFP4 = 2
+RATE_E2M1_E2M1 = 16  # moe_mfma_rate's e2m1 x e2m1 operand pair
 
 EXPORTS = ("moe_workspace_size", "moe_permute", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm2",
            "moe_combine", "moe_layer", "moe_layer_static", "moe_layer_persistent", "moe_prepack_weights",
@@ -59,7 +61,7 @@ class MoeCfg(C.Structure):
 
 class MoeWeights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("w1", "w1s", "w2", "w2s", "sw1", "sw1s", "sw2", "sw2s")] + \
-        [("prepacked", C.c_int32)]
+        [("prepacked", C.c_int32)] + [(n, C.c_void_p) for n in ("w1g", "w2g", "sw1g", "sw2g")]
 
 
 class MoeError(RuntimeError):
@@ -167,11 +169,12 @@ def _check(fn: str, rc: int) -> None:
 
 
 def weights_struct(w) -> MoeWeights:
-    """moe_weights from an object with w1, w1s, w2, w2s[, sw1, sw1s, sw2, sw2s] tensors
-    and an optional `prepacked` flag (absent: 0, the canonical row-major layout)."""
+    """moe_weights from an object with w1, w1s, w2, w2s[, sw1, sw1s, sw2, sw2s] tensors,
+    NVFP4's matrix scales w1g, w2g[, sw1g, sw2g] and an optional `prepacked` flag
+    (absent: 0, the canonical row-major layout)."""
     g = lambda n: _ptr(getattr(w, n, None))
     return MoeWeights(g("w1"), g("w1s"), g("w2"), g("w2s"), g("sw1"), g("sw1s"), g("sw2"), g("sw2s"),
-                      int(getattr(w, "prepacked", 0)))
+                      int(getattr(w, "prepacked", 0)), g("w1g"), g("w2g"), g("sw1g"), g("sw2g"))
 
 
 def _u16(x: torch.Tensor) -> torch.Tensor:
@@ -291,12 +294,18 @@ class TiledWeights:
     sw2: Optional[torch.Tensor] = None
     sw2s: Optional[torch.Tensor] = None
     prepacked: int = 1
+    w1g: Optional[torch.Tensor] = None   # NVFP4: fp32 matrix scales (row-major, unchanged)
+    w2g: Optional[torch.Tensor] = None
+    sw1g: Optional[torch.Tensor] = None
+    sw2g: Optional[torch.Tensor] = None
 
 
 def moe_prepack_weights(cfg: Cfg, weights) -> TiledWeights:
     """Tiled copies of a layer's canonical row-major weights (w1, w1s, w2, w2s
     and, when cfg.has_shared, sw1..sw2s): the one-time step at weight load."""
     names = ["w1", "w1s", "w2", "w2s"] + (["sw1", "sw1s", "sw2", "sw2s"] if cfg.has_shared else [])
+    if cfg.wfmt == WFMT_NVFP4:
+        names += ["w1g", "w2g"] + (["sw1g", "sw2g"] if cfg.has_shared else [])
     out = TiledWeights(**{n: torch.empty_like(getattr(weights, n)) for n in names})
     c, src, dst = cfg.c(), weights_struct(weights), weights_struct(out)
     dst.prepacked = 0

@@ -106,6 +106,7 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   s.big = (G == 128 && (wfmt == 1 || wblk == 128) && H % 256 == 0 && H <= 8192 && I <= 8192 &&
            avg_rows >= min_rows) ? 1 : 0;
   if (af == 1) s.big = 1;  // 4-bit activations run the many-row kernels at every T
+  if (wfmt == 2) s.big = 0;  // NVFP4 runs the decode kernels at every T
   // 64 rows per pass while nearly every group fits (mean + 3 sd of a
   // Poisson count), which leaves LDS for a deeper ring; 160 beyond
   s.big_cap = avg_rows + 3.0 * std::sqrt(avg_rows) + 1.0 <= 64.0 ? 64 : 160;
@@ -186,6 +187,9 @@ int check_shape(const moe_cfg* c) {
   } else if (c->wfmt == MOE_WFMT_MXFP4) {
     if (c->wblk != 32) return MOE_ERR_BAD_SHAPE;
     if (c->act_fmt == MOE_AFMT_FP8 && c->act_group != 128) return MOE_ERR_UNSUPPORTED;
+  } else if (c->wfmt == MOE_WFMT_NVFP4) {
+    if (c->wblk != 16) return MOE_ERR_BAD_SHAPE;
+    if (c->act_fmt != MOE_AFMT_FP8 || c->act_group != 128) return MOE_ERR_UNSUPPORTED;
   } else {
     return MOE_ERR_UNSUPPORTED;
   }
@@ -216,6 +220,10 @@ using PtrList = std::initializer_list<std::pair<const void*, bool>>;  // (pointe
 int weights_null(const moe_cfg* c, const moe_weights* w) {
   if (!w || !w->w1 || !w->w1s || !w->w2 || !w->w2s) return MOE_ERR_NULL_ARG;
   if (c->has_shared == 1 && (!w->sw1 || !w->sw1s || !w->sw2 || !w->sw2s)) return MOE_ERR_NULL_ARG;
+  if (c->wfmt == MOE_WFMT_NVFP4) {  // the matrix scales
+    if (!w->w1g || !w->w2g) return MOE_ERR_NULL_ARG;
+    if (c->has_shared == 1 && (!w->sw1g || !w->sw2g)) return MOE_ERR_NULL_ARG;
+  }
   return MOE_OK;
 }
 
@@ -225,6 +233,11 @@ int weights_layout(const moe_cfg* c, const moe_weights* w, int tiled) {
   const void* ps[8] = {w->w1, w->w1s, w->w2, w->w2s, w->sw1, w->sw1s, w->sw2, w->sw2s};
   for (int i = 0; i < (c->has_shared ? 8 : 4); ++i)
     if (misaligned(ps[i])) return MOE_ERR_MISALIGNED;
+  if (c->wfmt == MOE_WFMT_NVFP4) {  // fp32 matrix scales: 4-byte aligned
+    const float* gs[4] = {w->w1g, w->w2g, w->sw1g, w->sw2g};
+    for (int i = 0; i < (c->has_shared ? 4 : 2); ++i)
+      if (reinterpret_cast<uintptr_t>(gs[i]) & 3u) return MOE_ERR_MISALIGNED;
+  }
   if (w->prepacked != 0 && w->prepacked != 1) return MOE_ERR_UNSUPPORTED;
   if (tiled >= 0 && w->prepacked != tiled) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -245,6 +258,16 @@ int check_args(const moe_cfg* c, PtrList ps, const moe_weights* w = nullptr, boo
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// The GEMMs' view of the weights: GEMM1's gate|up tensors, GEMM2's down tensors.
+WeightPtrs w1_ptrs(const moe_weights* w) {
+  return WeightPtrs{static_cast<const uint8_t*>(w->w1), w->w1s, static_cast<const uint8_t*>(w->sw1), w->sw1s,
+                    w->w1g, w->sw1g};
+}
+WeightPtrs w2_ptrs(const moe_weights* w) {
+  return WeightPtrs{static_cast<const uint8_t*>(w->w2), w->w2s, static_cast<const uint8_t*>(w->sw2), w->sw2s,
+                    w->w2g, w->sw2g};
+}
 
 // The layer's buffers inside a scratch region `b` of at least L.total bytes.
 LayerBufs layer_bufs(const WsLayout& L, char* b) {
@@ -281,8 +304,7 @@ int enqueue_layer(const Shape& s, const WsLayout& L, const uint16_t* x, const in
                                           B.xs, B.clear, B.nclear, chunk_cnt, st))))
     return rc;
   if (s.T == 0) return MOE_OK;
-  const WeightPtrs w1{static_cast<const uint8_t*>(w->w1), w->w1s, static_cast<const uint8_t*>(w->sw1), w->sw1s};
-  const WeightPtrs w2{static_cast<const uint8_t*>(w->w2), w->w2s, static_cast<const uint8_t*>(w->sw2), w->sw2s};
+  const WeightPtrs w1 = w1_ptrs(w), w2 = w2_ptrs(w);
   if (s.big) {
     if ((rc = hip_status(launch_gemm1_big(s, B.xq, B.xs, B.row_token, B.offsets, w1, B.hq, B.hs, 1, st)))) return rc;
     if ((rc = hip_status(launch_gemm2_big(s, B.hq, B.hs, B.offsets, w2, nullptr, B.yb, 1, st)))) return rc;
@@ -367,16 +389,14 @@ int moe_grouped_gemm1_swiglu(const moe_cfg* cfg, const uint8_t* xq, const float*
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (s.big)
     return hip_status(launch_gemm1_big(s, xq, xs, row_token, offsets,
-                                       WeightPtrs{static_cast<const uint8_t*>(w->w1), w->w1s,
-                                                  static_cast<const uint8_t*>(w->sw1), w->sw1s},
+                                       w1_ptrs(w),
                                        hq, hs, 1, st));
   int32_t* cnt = reinterpret_cast<int32_t*>(base + L.cnt1);
   if (s.g1_split > 1) {
     if ((rc = hip_status(launch_clear(cnt, s.g1_items * s.g1_tiles, st)))) return rc;
   }
   return hip_status(launch_gemm1(s, xq, xs, row_token, offsets,
-                                 WeightPtrs{static_cast<const uint8_t*>(w->w1), w->w1s,
-                                            static_cast<const uint8_t*>(w->sw1), w->sw1s},
+                                 w1_ptrs(w),
                                  hq, hs, reinterpret_cast<float*>(base + L.part1), cnt, st));
 }
 
@@ -393,16 +413,14 @@ int moe_grouped_gemm2(const moe_cfg* cfg, const uint8_t* hq, const float* hs, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (s.big)
     return hip_status(launch_gemm2_big(s, hq, hs, offsets,
-                                       WeightPtrs{static_cast<const uint8_t*>(w->w2), w->w2s,
-                                                  static_cast<const uint8_t*>(w->sw2), w->sw2s},
+                                       w2_ptrs(w),
                                        y, nullptr, 1, st));
   int32_t* cnt = reinterpret_cast<int32_t*>(base + L.cnt2);
   if (s.g2_split > 1) {
     if ((rc = hip_status(launch_clear(cnt, s.g2_items * s.g2_tiles, st)))) return rc;
   }
   return hip_status(launch_gemm2(s, hq, hs, offsets,
-                                 WeightPtrs{static_cast<const uint8_t*>(w->w2), w->w2s,
-                                            static_cast<const uint8_t*>(w->sw2), w->sw2s},
+                                 w2_ptrs(w),
                                  y, nullptr, reinterpret_cast<float*>(base + L.part2), cnt, st));
 }
 
@@ -458,8 +476,7 @@ int moe_layer_persistent(const moe_cfg* cfg, const uint16_t* x, const int32_t* t
   if (!persistent_supported(s)) return MOE_ERR_UNSUPPORTED;
   char* base = static_cast<char*>(ws);
   const LayerBufs b = layer_bufs(L, base);
-  const WeightPtrs w1{static_cast<const uint8_t*>(w->w1), w->w1s, static_cast<const uint8_t*>(w->sw1), w->sw1s};
-  const WeightPtrs w2{static_cast<const uint8_t*>(w->w2), w->w2s, static_cast<const uint8_t*>(w->sw2), w->sw2s};
+  const WeightPtrs w1 = w1_ptrs(w), w2 = w2_ptrs(w);
   return hip_status(launch_layer_persistent(s, x, topk_ids, topk_weights, w1, w2, b,
                                             reinterpret_cast<int32_t*>(base + L.chunk_cnt), out,
                                             reinterpret_cast<int32_t*>(base + L.pctl), status,
@@ -473,7 +490,7 @@ int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_we
   if ((rc = check_shape(cfg))) return rc;
   if ((rc = weights_layout(cfg, canonical, 0)) || (rc = weights_layout(cfg, packed, -1))) return rc;
   const moe_cfg& c = *cfg;
-  const bool mx = c.wfmt == MOE_WFMT_MXFP4;
+  const bool mx = c.wfmt != MOE_WFMT_FP8_BLOCK;  // scales re-laid out (MXFP4, NVFP4)
   const hipStream_t st = static_cast<hipStream_t>(stream);
   // (codes, scales, matrices, rows N, reduction K) of each tensor pair
   struct Pair { const void *w, *s; void *wt, *stl; int mats, N, K; };
@@ -494,6 +511,16 @@ int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_we
     if (!mx && q.s != q.stl) {  // e4m3 block scales keep their layout
       const size_t sb = size_t(q.mats) * (q.N / c.wblk) * (q.K / c.wblk) * sizeof(float);
       if ((rc = hip_status(hipMemcpyAsync(q.stl, q.s, sb, hipMemcpyDeviceToDevice, st)))) return rc;
+    }
+  }
+  if (c.wfmt == MOE_WFMT_NVFP4) {  // the matrix scales keep their layout
+    const float* gsrc[4] = {canonical->w1g, canonical->w2g, canonical->sw1g, canonical->sw2g};
+    const float* gdst[4] = {packed->w1g, packed->w2g, packed->sw1g, packed->sw2g};
+    for (int i = 0; i < np; ++i) {
+      const size_t gb = size_t(i < 2 ? c.E : 1) * sizeof(float);
+      if (gsrc[i] != gdst[i] &&
+          (rc = hip_status(hipMemcpyAsync(const_cast<float*>(gdst[i]), gsrc[i], gb, hipMemcpyDeviceToDevice, st))))
+        return rc;
     }
   }
   packed->prepacked = 1;

@@ -166,9 +166,11 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, const v4f& v) {
 // at l * 16; e4m3 tiles carry the K bytes 64..127 of the step in a second
 // kilobyte.  MXFP4 scales: 64 bytes per tile, byte l = e8m0 of row
 // 16 rt + l % 16 and 32-block l / 16 of the step -- the scale operand of
-// MFMA lane l.
+// MFMA lane l.  NVFP4 (WF 2) codes tile as MXFP4's; its e4m3 scales take
+// 128 bytes per tile, byte 8 m + j = row 16 rt + m, 16-block 8 ks + j.
 template <int WF> constexpr int kTileBytes = WF == 0 ? 2048 : 1024;
 constexpr int kTileScaleBytes = 64;
+constexpr int kTileScaleBytes16 = 128;
 
 // this lane's operand from a weight tile (tile_lane = tile base + 16 * lane)
 template <int WF>

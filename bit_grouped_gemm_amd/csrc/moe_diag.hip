@@ -119,7 +119,7 @@ hipError_t launch_mfma_rate(int wfmt, int iters, float* sink, double* flops, hip
   else if (wfmt == 1)
     hipLaunchKernelGGL((k_mfma_rate<kFmtE2M1, kFmtE4M3>), dim3(unsigned(grid)), dim3(kStreamThreads), 0, st,
                        0x22222222u, 0x38383838u, iters, sink);
-  else
+  else  // e2m1 x e2m1 (MOE_RATE_E2M1_E2M1)
     hipLaunchKernelGGL((k_mfma_rate<kFmtE2M1, kFmtE2M1>), dim3(unsigned(grid)), dim3(kStreamThreads), 0, st,
                        0x22222222u, 0x22222222u, iters, sink);
   return hipGetLastError();

@@ -315,6 +315,27 @@ __device__ int nth_item(const int32_t* offsets, int ngroups, int item, int R, in
   return s_res[0];
 }
 
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+// Eight e2m1 codes (one word, low nibble first = lower K) as f16 (exact).
+__device__ __forceinline__ h8v cvt_e2m1x8_f16(uint32_t w) {
+  const h2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  const h2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  const h2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  const h2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  return h8v{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Eight e4m3 codes (two words, byte order = K order) as f16 (exact).
+__device__ __forceinline__ h8v cvt_e4m3x8_f16(int w0, int w1) {
+  const h2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(uint32_t(w0), 1.0f, false);
+  const h2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(uint32_t(w0), 1.0f, true);
+  const h2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(uint32_t(w1), 1.0f, false);
+  const h2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(uint32_t(w1), 1.0f, true);
+  return h8v{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // Operands of one 128-K step for a wave: NJ weight tiles of 16 rows and NTT
 // token tiles of 16 columns.
 template <int WF, int NJ, int NTT>
@@ -322,7 +343,7 @@ struct Frag {
   v8i a[NJ];
   v8i b[NTT];
   float wsc[NJ];   // e4m3 weights, 128-blocks: wave-uniform weight scale
-  int wsb[NJ];     // MXFP4: this lane's e8m0 byte (row m, 32-block g)
+  int wsb[NJ];     // MXFP4: this lane's e8m0 byte (row m, 32-block g); NVFP4: its two e4m3 bytes
   float xsv[NTT];  // activation scale of this lane's token column
 };
 
@@ -375,8 +396,8 @@ template <int NJ, int NTT>
 struct KSrc {
   __amdgpu_buffer_rsrc_t wr, sr, ar, xr;
   int wo[NJ];   // weight tile j: the tile's offset + 16 lane
-  int so[NJ];   // MXFP4: scale byte of tile j (the tile's 64 bytes + lane)
-  int bo[NTT];  // token column t: its code row + 16 g
+  int so[NJ];   // MXFP4: scale byte of tile j (the tile's 64 bytes + lane); NVFP4: row m's bytes 2g, 2g+1
+  int bo[NTT];  // token column t: its code row + 16 g (NVFP4: + 32 g)
   int xo[NTT];  // token column t: its scale row, in bytes
   int wstep, sstep, astep;  // bytes per K step: weight tiles, scale tiles, activation scales
 };
@@ -394,13 +415,16 @@ __device__ __forceinline__ void load_frag(Frag<WF, NJ, NTT>& f, const KSrc<NJ, N
       if (!B32) f.wsc[j] = wsc[j][ks];
     } else {
       f.a[j] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), 0, 0, 0, 0};
-      f.wsb[j] = __builtin_amdgcn_raw_buffer_load_b8(src.sr, src.so[j], ksc, kNt);
+      if (WF == 1) f.wsb[j] = __builtin_amdgcn_raw_buffer_load_b8(src.sr, src.so[j], ksc, kNt);
+      else f.wsb[j] = __builtin_amdgcn_raw_buffer_load_b16(src.sr, src.so[j], ksc, kNt);  // NVFP4: 16-blocks 2g, 2g+1
     }
   }
 #pragma unroll
   for (int t = 0; t < NTT; ++t) {
+    // e4m3 operand order: bytes 16 g .. and 64 + 16 g ..; NVFP4's f16 path:
+    // the lane's 32 consecutive K, 32 g ..
     const v4u lo = __builtin_amdgcn_raw_buffer_load_b128(src.ar, src.bo[t], ka, CO ? kSc1 : 0);
-    const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(src.ar, src.bo[t] + 64, ka, CO ? kSc1 : 0);
+    const v4u hi = __builtin_amdgcn_raw_buffer_load_b128(src.ar, src.bo[t] + (WF == 2 ? 16 : 64), ka, CO ? kSc1 : 0);
     f.b[t] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
     if (!B32) f.xsv[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(src.xr, src.xo[t], kx, CO ? kSc1 : 0));
   }
@@ -424,6 +448,33 @@ __device__ __forceinline__ void mma_frag(v4f (&acc)[NJ][NTT], const Frag<WF, NJ,
           acc[j][t] += d * (ws * ld_f32<CO>(&bsc[t][ks * 4 + sb]));
         }
       }
+    }
+  } else if (WF == 2) {
+    // NVFP4 through the fp16 MFMA (16x16x32): lane (row or column 16-slot,
+    // group g) holds K 32 g .. 32 g + 31 of the step for both operands, the
+    // q-th instruction taking K 32 g + 8 q .. + 7, so the two operands agree
+    // on every K.  Weights: e2m1 -> f16, times the e4m3 block scale as f16
+    // (the product has at most 6 significant bits and stays in f16's normal
+    // range, so it is exact); activations: e4m3 -> f16 (exact).  The
+    // matrix scale is applied once after the K loop.
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) {
+      h8v bq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bq[q] = cvt_e4m3x8_f16(f.b[t][2 * q], f.b[t][2 * q + 1]);
+      v4f d[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const h2v sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(uint32_t(f.wsb[j]), 1.0f, false);
+        d[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const h8v a = cvt_e2m1x8_f16(uint32_t(f.a[j][q])) * (q < 2 ? sc[0] : sc[1]);
+          d[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[q], d[j], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j][t] += d[j] * f.xsv[t];
     }
   } else {
     // one token tile at a time: the NJ products land in separate registers
@@ -481,6 +532,8 @@ struct GemmParams {
   const void* ws;
   const uint8_t* sw;
   const void* sws;
+  const float* wg;           // NVFP4: fp32 scale per routed expert matrix [E]
+  const float* swg;          // and the shared expert's [1]
   uint8_t* hq;               // GEMM1 outputs
   float* hs;
   float* y;                  // GEMM2 output (fp32), or
@@ -587,8 +640,12 @@ __device__ __forceinline__ void swiglu_requant_store(const v4f (&acc)[4][NTT], c
 // workgroups per CU, which runs a 64-expert T = 64 layer's 768 units in one
 // round instead of one and a half), one token tile at 128 (four per CU); the
 // compiler fits both without spills.
+// (NVFP4's f16 operands take more registers: two workgroups per CU with
+// two token tiles, where the K loop would otherwise spill)
 template <int NTT>
-constexpr int gemm1_occupancy(int b32) { return b32 ? 1 : NTT == 2 ? 3 : NTT == 1 ? 4 : 1; }
+constexpr int gemm1_occupancy(int b32, int wf = 0) {
+  return b32 ? 1 : NTT == 2 ? (wf == 2 ? 2 : 3) : NTT == 1 ? 4 : 1;
+}
 
 // Unit u of GEMM1.  Returns true (in every thread) when this workgroup
 // stored a finished 128-column slice of h: the only split (S == 1) or the
@@ -611,18 +668,19 @@ __device__ __forceinline__ bool gemm1_unit(const GemmParams& p, int u) {
   const long kbytes = WF == 0 ? H : H / 2;
   KSrc<4, NTT> src;
   src.wr = buf_rsrc((shared ? p.sw : p.w) + ee * 2L * I * kbytes);
-  src.sr = buf_rsrc(static_cast<const uint8_t*>(shared ? p.sws : p.ws) + (WF == 1 ? ee * 2L * I * (H / 32) : 0));
+  src.sr = buf_rsrc(static_cast<const uint8_t*>(shared ? p.sws : p.ws) +
+                    (WF == 1 ? ee * 2L * I * (H / 32) : WF == 2 ? ee * 2L * I * (H / 16) : 0));
   src.ar = buf_rsrc(p.act);
   src.xr = buf_rsrc(p.act_s);
   src.wstep = (2 * I / 16) * kTileBytes<WF>;
-  src.sstep = (2 * I / 16) * kTileScaleBytes;
+  src.sstep = (2 * I / 16) * (WF == 2 ? kTileScaleBytes16 : kTileScaleBytes);
   src.astep = 4;
   const float* wsc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int rb = (j < 2) ? (n0 + 32 * w + 16 * j) : (I + n0 + 32 * w + 16 * (j - 2));
     src.wo[j] = (rb / 16) * kTileBytes<WF> + lane * 16;
-    src.so[j] = (rb / 16) * kTileScaleBytes + lane;
+    src.so[j] = WF == 2 ? (rb / 16) * kTileScaleBytes16 + 8 * m + 2 * g : (rb / 16) * kTileScaleBytes + lane;
     wsc[j] = nullptr;
     if (WF == 0) {
       const int b = p.wblk;
@@ -641,7 +699,7 @@ __device__ __forceinline__ bool gemm1_unit(const GemmParams& p, int u) {
     for (int t = 0; t < NTT; ++t) {
       const int idx = min(pass * 16 * NTT + t * 16 + m, ne - 1);
       const int tok = p.row_token[row0 + idx];
-      src.bo[t] = tok * H + 16 * g;
+      src.bo[t] = tok * H + (WF == 2 ? 32 : 16) * g;
       src.xo[t] = tok * (H / p.G) * 4;
       bsc[t] = p.act_s + long(tok) * (H / p.G);
     }
@@ -651,6 +709,13 @@ __device__ __forceinline__ bool gemm1_unit(const GemmParams& p, int u) {
 #pragma unroll
       for (int t = 0; t < NTT; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     kloop<WF, 4, NTT, B32, kStages>(acc, src, wsc, bsc, ks0, ks1, g);
+    if (WF == 2) {  // NVFP4: the matrix scale
+      const float gs = shared ? p.swg[0] : p.wg[ee];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int t = 0; t < NTT; ++t) acc[j][t] *= gs;
+    }
     if (S == 1) {
       swiglu_requant_store<NTT, CO>(acc, p, row0, ne, pass, n0, s_red);
       return true;
@@ -690,7 +755,7 @@ __device__ __forceinline__ bool gemm1_unit(const GemmParams& p, int u) {
 }
 
 template <int WF, int NTT, int B32>
-__global__ __launch_bounds__(kThreads, gemm1_occupancy<NTT>(B32)) void k_gemm1(GemmParams p) {
+__global__ __launch_bounds__(kThreads, gemm1_occupancy<NTT>(B32, WF)) void k_gemm1(GemmParams p) {
   gemm1_unit<WF, NTT, B32>(p, blockIdx.x);
 }
 
@@ -727,18 +792,19 @@ __device__ __forceinline__ int gemm2_unit(const GemmParams& p, int u, const Read
   const long kbytes = WF == 0 ? I : I / 2;
   KSrc<NJ, NTT> src;
   src.wr = buf_rsrc((shared ? p.sw : p.w) + ee * long(H) * kbytes);
-  src.sr = buf_rsrc(static_cast<const uint8_t*>(shared ? p.sws : p.ws) + (WF == 1 ? ee * long(H) * (I / 32) : 0));
+  src.sr = buf_rsrc(static_cast<const uint8_t*>(shared ? p.sws : p.ws) +
+                    (WF == 1 ? ee * long(H) * (I / 32) : WF == 2 ? ee * long(H) * (I / 16) : 0));
   src.ar = buf_rsrc(p.act);
   src.xr = buf_rsrc(p.act_s);
   src.wstep = (H / 16) * kTileBytes<WF>;
-  src.sstep = (H / 16) * kTileScaleBytes;
+  src.sstep = (H / 16) * (WF == 2 ? kTileScaleBytes16 : kTileScaleBytes);
   src.astep = 4;
   const float* wsc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int rb = n0 + 16 * NJ * w + 16 * j;
     src.wo[j] = (rb / 16) * kTileBytes<WF> + lane * 16;
-    src.so[j] = (rb / 16) * kTileScaleBytes + lane;
+    src.so[j] = WF == 2 ? (rb / 16) * kTileScaleBytes16 + 8 * m + 2 * g : (rb / 16) * kTileScaleBytes + lane;
     wsc[j] = nullptr;
     if (WF == 0) {
       const int b = p.wblk;
@@ -755,7 +821,7 @@ __device__ __forceinline__ int gemm2_unit(const GemmParams& p, int u, const Read
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
       const int r = row0 + min(pass * 16 * NTT + t * 16 + m, ne - 1);
-      src.bo[t] = r * I + 16 * g;
+      src.bo[t] = r * I + (WF == 2 ? 32 : 16) * g;
       src.xo[t] = r * (I / p.G) * 4;
       bsc[t] = p.act_s + long(r) * (I / p.G);
     }
@@ -765,6 +831,13 @@ __device__ __forceinline__ int gemm2_unit(const GemmParams& p, int u, const Read
 #pragma unroll
       for (int t = 0; t < NTT; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     kloop<WF, NJ, NTT, B32, kStages, CO>(acc, src, wsc, bsc, ks0, ks1, g);
+    if (WF == 2) {  // NVFP4: the matrix scale
+      const float gs = shared ? p.swg[0] : p.wg[ee];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int t = 0; t < NTT; ++t) acc[j][t] *= gs;
+    }
 #pragma unroll
     for (int t = 0; t < NTT; ++t) {
       const int idx = pass * 16 * NTT + t * 16 + m;
@@ -1128,6 +1201,10 @@ hipError_t launch_clear(int32_t* ptr, int n, hipStream_t st) {
       if (ntt == 1) hipLaunchKernelGGL((NAME<0, 1, 1>), dim3(grid), dim3(kThreads), 0, st, p); \
       else if (ntt == 2) hipLaunchKernelGGL((NAME<0, 2, 1>), dim3(grid), dim3(kThreads), 0, st, p); \
       else hipLaunchKernelGGL((NAME<0, 4, 1>), dim3(grid), dim3(kThreads), 0, st, p);        \
+    } else if (s.wfmt == 2) {                                                                \
+      if (ntt == 1) hipLaunchKernelGGL((NAME<2, 1, 0>), dim3(grid), dim3(kThreads), 0, st, p); \
+      else if (ntt == 2) hipLaunchKernelGGL((NAME<2, 2, 0>), dim3(grid), dim3(kThreads), 0, st, p); \
+      else hipLaunchKernelGGL((NAME<2, 4, 0>), dim3(grid), dim3(kThreads), 0, st, p);        \
     } else {                                                                                 \
       if (ntt == 1) hipLaunchKernelGGL((NAME<1, 1, 0>), dim3(grid), dim3(kThreads), 0, st, p); \
       else if (ntt == 2) hipLaunchKernelGGL((NAME<1, 2, 0>), dim3(grid), dim3(kThreads), 0, st, p); \
@@ -1142,7 +1219,7 @@ MOE_GEMM_DISPATCH(k_gemm1)
 template <int NJ>
 static hipError_t dispatch_gemm2_nj(const Shape& s, int ntt, unsigned grid, const GemmParams& p, hipStream_t st) {
   const bool b32 = s.wfmt == 0 && s.wblk == 32;
-  const int wf = s.wfmt == 0 ? 0 : 1;
+  const int wf = s.wfmt;
 #define MOE_G2(WF, B32)                                                                                \
   do {                                                                                                 \
     if (ntt == 1) hipLaunchKernelGGL((k_gemm2<WF, 1, B32, NJ>), dim3(grid), dim3(kThreads), 0, st, p);  \
@@ -1151,6 +1228,7 @@ static hipError_t dispatch_gemm2_nj(const Shape& s, int ntt, unsigned grid, cons
   } while (0)
   if (wf == 0 && !b32) MOE_G2(0, 0);
   else if (b32) MOE_G2(0, 1);
+  else if (wf == 2) MOE_G2(2, 0);
   else MOE_G2(1, 0);
 #undef MOE_G2
   return hipGetLastError();
@@ -1161,7 +1239,7 @@ hipError_t launch_gemm1(const Shape& s, const uint8_t* xq, const float* xs, cons
                         int32_t* cnt, hipStream_t st) {
   GemmParams p{};
   p.act = xq; p.act_s = xs; p.row_token = row_token; p.offsets = offsets;
-  p.w = w1.w; p.ws = w1.ws; p.sw = w1.sw; p.sws = w1.sws;
+  p.w = w1.w; p.ws = w1.ws; p.sw = w1.sw; p.sws = w1.sws; p.wg = w1.g; p.swg = w1.sg;
   p.hq = hq; p.hs = hs; p.part = part; p.cnt = cnt;
   p.H = s.H; p.I = s.I; p.E = s.E; p.G = s.G; p.wblk = s.wblk; p.ngroups = s.ngroups;
   p.S = s.g1_split; p.ntiles = s.g1_tiles; p.rows_cap = s.rows_cap;
@@ -1174,7 +1252,7 @@ hipError_t launch_gemm2(const Shape& s, const uint8_t* hq, const float* hs, cons
                         WeightPtrs w2, float* y, uint16_t* yb, float* part, int32_t* cnt, hipStream_t st) {
   GemmParams p{};
   p.act = hq; p.act_s = hs; p.offsets = offsets;
-  p.w = w2.w; p.ws = w2.ws; p.sw = w2.sw; p.sws = w2.sws;
+  p.w = w2.w; p.ws = w2.ws; p.sw = w2.sw; p.sws = w2.sws; p.wg = w2.g; p.swg = w2.sg;
   p.y = y; p.yb = yb; p.part = part; p.cnt = cnt;
   p.H = s.H; p.I = s.I; p.E = s.E; p.G = s.G; p.wblk = s.wblk; p.ngroups = s.ngroups;
   p.S = s.g2_split; p.ntiles = s.g2_tiles; p.rows_cap = s.rows_cap;
@@ -1228,8 +1306,8 @@ static hipError_t launch_persistent_inst(const PersistParams& p, int total, hipS
 }
 
 bool persistent_supported(const Shape& s) {
-  return s.T > 0 && !s.big && s.af == 0 && s.g1_ntt == s.g2_ntt && s.g1_items <= kPersistMaxItems &&
-         (s.wfmt == 1 || s.g2_nj <= 4);
+  return s.T > 0 && !s.big && s.af == 0 && s.wfmt != 2 && s.g1_ntt == s.g2_ntt &&
+         s.g1_items <= kPersistMaxItems && (s.wfmt == 1 || s.g2_nj <= 4);
 }
 
 hipError_t launch_layer_persistent(const Shape& s, const uint16_t* x, const int32_t* ids, const float* tw,
@@ -1244,13 +1322,13 @@ hipError_t launch_layer_persistent(const Shape& s, const uint16_t* x, const int3
   PersistParams p{};
   GemmParams& g1 = p.g1;
   g1.act = b.xq; g1.act_s = b.xs; g1.row_token = b.row_token; g1.offsets = b.offsets;
-  g1.w = w1.w; g1.ws = w1.ws; g1.sw = w1.sw; g1.sws = w1.sws;
+  g1.w = w1.w; g1.ws = w1.ws; g1.sw = w1.sw; g1.sws = w1.sws; g1.wg = w1.g; g1.swg = w1.sg;
   g1.hq = b.hq; g1.hs = b.hs; g1.part = b.part1; g1.cnt = b.cnt1;
   g1.H = s.H; g1.I = s.I; g1.E = s.E; g1.G = s.G; g1.wblk = s.wblk; g1.ngroups = s.ngroups;
   g1.S = s.g1_split; g1.ntiles = s.g1_tiles; g1.rows_cap = s.rows_cap;
   GemmParams& g2 = p.g2;
   g2.act = b.hq; g2.act_s = b.hs; g2.offsets = b.offsets;
-  g2.w = w2.w; g2.ws = w2.ws; g2.sw = w2.sw; g2.sws = w2.sws;
+  g2.w = w2.w; g2.ws = w2.ws; g2.sw = w2.sw; g2.sws = w2.sws; g2.wg = w2.g; g2.swg = w2.sg;
   g2.yb = b.yb; g2.part = b.part2; g2.cnt = b.cnt2;
   g2.H = s.H; g2.I = s.I; g2.E = s.E; g2.G = s.G; g2.wblk = s.wblk; g2.ngroups = s.ngroups;
   g2.S = s.g2_split; g2.ntiles = s.g2_tiles; g2.rows_cap = s.rows_cap;

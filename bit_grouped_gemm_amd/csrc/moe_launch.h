@@ -54,6 +54,8 @@ struct WeightPtrs {
   const void* ws;     // routed scales
   const uint8_t* sw;  // shared expert (or null)
   const void* sws;
+  const float* g = nullptr;   // NVFP4: fp32 scale per routed matrix [E]
+  const float* sg = nullptr;  // and the shared expert's [1]
 };
 
 // clear: nclear ints zeroed by the routing block; zero1: one more int (or null)
@@ -118,7 +120,7 @@ struct LayerBufs {
 };
 
 // Shapes the persistent layer runs: the decode kernels (not the many-row
-// ones), FP8 activations.
+// ones), FP8 activations, FP8 or MXFP4 weights.
 bool persistent_supported(const Shape& s);
 hipError_t launch_layer_persistent(const Shape& s, const uint16_t* x, const int32_t* ids, const float* tw,
                                    WeightPtrs w1, WeightPtrs w2, const LayerBufs& b, int32_t* chunk_cnt,

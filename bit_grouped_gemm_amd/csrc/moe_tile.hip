@@ -8,8 +8,10 @@
 // Tiles are stored k-step major, [mats][K/128][N/16][tile], so the tiles of
 // consecutive rows for one k step are adjacent.  MXFP4 scales follow the
 // same order with 64 bytes per tile, byte l being the e8m0 scale MFMA lane
-// l consumes (row 16 rt + l % 16, 32-block 4 ks + l / 16).  The reorder is a
-// permutation: sizes are those of the row-major tensors.
+// l consumes (row 16 rt + l % 16, 32-block 4 ks + l / 16).  NVFP4 codes
+// tile as MXFP4's; its e4m3 scales take 128 bytes per tile, row m's eight
+// 16-blocks of the step at 8 m.  The reorder is a permutation: sizes are
+// those of the row-major tensors.
 #include "moe_device.h"
 #include "moe_launch.h"
 
@@ -55,6 +57,21 @@ __global__ __launch_bounds__(kTileThreads) void k_tile_scales(const uint8_t* __r
   }
 }
 
+// one thread per scale byte of the tiled NVFP4 scales
+__global__ __launch_bounds__(kTileThreads) void k_tile_scales16(const uint8_t* __restrict__ src,
+                                                               uint8_t* __restrict__ dst, long bytes, int N, int K) {
+  const int nrt = N / 16, nks = K / 128, kb = K / 16;
+  for (long i = long(blockIdx.x) * kTileThreads + threadIdx.x; i < bytes; i += long(gridDim.x) * kTileThreads) {
+    const long tile = i / kTileScaleBytes16;
+    const int within = int(i % kTileScaleBytes16);
+    const int rt = int(tile % nrt);
+    const long rest = tile / nrt;
+    const int ks = int(rest % nks);
+    const long mat = rest / nks;
+    dst[i] = src[(mat * N + long(rt) * 16 + within / 8) * kb + ks * 8 + within % 8];
+  }
+}
+
 unsigned grid_for(long items) {
   const long blocks = (items + kTileThreads - 1) / kTileThreads;
   return unsigned(blocks < 8192 ? blocks : 8192);
@@ -74,6 +91,10 @@ hipError_t launch_tile_weights(int wfmt, int mats, int N, int K, const uint8_t* 
     const long sbytes = long(mats) * N * (K / 32);
     if (sbytes > 0)
       hipLaunchKernelGGL(k_tile_scales, dim3(grid_for(sbytes)), dim3(kTileThreads), 0, st, s, s_tiled, sbytes, N, K);
+  } else if (wfmt == 2) {
+    const long sbytes = long(mats) * N * (K / 16);
+    if (sbytes > 0)
+      hipLaunchKernelGGL(k_tile_scales16, dim3(grid_for(sbytes)), dim3(kTileThreads), 0, st, s, s_tiled, sbytes, N, K);
   }
   return hipGetLastError();
 }

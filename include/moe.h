@@ -63,7 +63,7 @@ enum {
   MOE_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
 };
 
-enum { MOE_WFMT_FP8_BLOCK = 0, MOE_WFMT_MXFP4 = 1 };
+enum { MOE_WFMT_FP8_BLOCK = 0, MOE_WFMT_MXFP4 = 1, MOE_WFMT_NVFP4 = 2 };
 enum { MOE_AFMT_FP8 = 0, MOE_AFMT_MXFP4 = 1 };
 
 /* Layer shape (host struct).
@@ -74,6 +74,13 @@ enum { MOE_AFMT_FP8 = 0, MOE_AFMT_MXFP4 = 1 };
  *   wfmt = MOE_WFMT_MXFP4: e2m1 weights packed two per byte (even K index in
  *          the low nibble) with one e8m0 scale per 32 along K (wblk = 32);
  *          act_group must be 128.
+ *   wfmt = MOE_WFMT_NVFP4: e2m1 weights packed the same way, one e4m3 scale
+ *          per 16 along K (wblk = 16) and one fp32 scale per expert matrix
+ *          (moe_weights' w1g..sw2g): weight = code * block scale * matrix
+ *          scale (the pages name NVFP4 beside MXFP4 in the onnxruntime QMoE
+ *          PR's shared 4-bit expert layouts; this is its published
+ *          two-level definition).  act_group must be 128 and act_fmt FP8;
+ *          every T runs the decode kernels.
  *   has_shared = 1 adds one always-on shared expert (same format and I) to
  *   every token with weight 1 (GC-MoE abstract: shared experts as an
  *   option; FusedDeepMoE shared-expert path: all tokens in one group).
@@ -107,7 +114,9 @@ typedef struct moe_cfg {
  *     [E][2I][H] (rows 0..I-1 gate, I..2I-1 up, K contiguous), w1s float
  *     [E][2I/wblk][H/wblk]; w2 uint8 [E][H][I], w2s float [E][H/wblk][I/wblk].
  *     MXFP4: w1 uint8 [E][2I][H/2], w1s uint8 [E][2I][H/32]; w2 uint8
- *     [E][H][I/2], w2s uint8 [E][H][I/32].
+ *     [E][H][I/2], w2s uint8 [E][H][I/32].  NVFP4: w1 uint8 [E][2I][H/2],
+ *     w1s uint8 e4m3 [E][2I][H/16], w1g float [E]; w2 uint8 [E][H][I/2],
+ *     w2s uint8 e4m3 [E][H][I/16], w2g float [E] (sw1g, sw2g: [1]).
  *   prepacked = 1: the same tensors in the TILED layout written by
  *     moe_prepack_weights (codes and MXFP4 scales re-laid out, e4m3 block
  *     scales unchanged; same sizes).
@@ -117,11 +126,14 @@ typedef struct moe_cfg {
  * (its gmm1_permuted_weight argument) and the onnxruntime QMoE PR marks
  * pre-arranged weights with a weights_prepacked flag.
  * sw1..sw2s: the shared expert with a leading dimension of 1 (may be NULL
- * when has_shared == 0). */
+ * when has_shared == 0).  w1g..sw2g: NVFP4's fp32 matrix scales, 4-byte
+ * aligned (NULL for the other formats; the tiled layout keeps them as they
+ * are). */
 typedef struct moe_weights {
   const void *w1, *w1s, *w2, *w2s;
   const void *sw1, *sw1s, *sw2, *sw2s;
   int32_t prepacked;
+  const float *w1g, *w2g, *sw1g, *sw2g;
 } moe_weights;
 
 /* Bytes of workspace moe_layer and the stage calls need for this shape
@@ -293,8 +305,11 @@ int moe_layer_static(const moe_cfg* cfg, const uint16_t* x, const int32_t* topk_
  * the step's K chunk (128 bytes for e4m3, 64 for e2m1), and for e4m3 byte
  * 1024 + l*16 + i is row-major byte 64 + 16 (l/16) + i of that chunk.
  * MXFP4 scales: 64 bytes per tile in the same order, byte l = scale of row
- * 16 rt + l%16 and 32-block 4 ks + l/16.  e4m3 block scales keep their
- * row-major layout (copied when the packed pointer differs).  Work is
+ * 16 rt + l%16 and 32-block 4 ks + l/16.  NVFP4 codes tile as MXFP4's;
+ * NVFP4 scales: 128 bytes per tile, byte 8 m + j = scale of row 16 rt + m
+ * and 16-block 8 ks + j.  e4m3 block scales of the FP8 format and NVFP4's
+ * matrix scales keep their row-major layout (copied when the packed pointer
+ * differs).  Work is
  * enqueued on `stream` like every other call. */
 int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_weights* packed, void* stream);
 
@@ -322,7 +337,7 @@ int moe_stream_read(const void* buf, size_t bytes, void* sink, size_t sink_bytes
  * call's duration on `stream`.  MOE_ERR_NULL_ARG (sink), MOE_ERR_MISALIGNED,
  * MOE_ERR_UNSUPPORTED (other wfmt), MOE_ERR_BAD_SHAPE (iters) and
  * MOE_ERR_WORKSPACE (sink too small) are host checks. */
-enum { MOE_RATE_E2M1_E2M1 = 2 };
+enum { MOE_RATE_E2M1_E2M1 = 16 };  /* not a weight format: the probe's third operand pair */
 int moe_mfma_rate(int wfmt, int iters, void* sink, size_t sink_bytes, double* flops, void* stream);
 
 /* Diagnostic: the fp32 -> e4m3 conversion every quantiser of the layer

@@ -242,6 +242,7 @@ def test_mfma_rate_argument_errors(lib):
     assert call(0, 16, None, 1 << 12) == moe.MOE_ERR_NULL_ARG
     assert call(0, 16, FAKE + 4, 1 << 12) == moe.MOE_ERR_MISALIGNED
     assert call(3, 16, FAKE, 1 << 12) == moe.MOE_ERR_UNSUPPORTED
+    assert call(2, 16, FAKE, 1 << 12) == moe.MOE_ERR_UNSUPPORTED   # NVFP4 is no probe pair
     assert call(0, 0, FAKE, 1 << 12) == moe.MOE_ERR_BAD_SHAPE
     assert call(1, 65537, FAKE, 1 << 12) == moe.MOE_ERR_BAD_SHAPE
     assert call(1, 16, FAKE, 16) == moe.MOE_ERR_WORKSPACE
@@ -335,3 +336,33 @@ def test_persistent_layer_host_checks(lib):
     # 4-bit activations run the many-row kernels at every T
     a4 = cfg(T=4, H=512, I=256, E=8, topk=2, wfmt=1, wblk=32, act_group=32, act_fmt=1)
     assert call(a4) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_nvfp4_host_checks(lib):
+    """NVFP4 (wfmt 2): wblk 16, FP8 activations in 128-groups; the matrix
+    scales w1g / w2g (and the shared expert's) are required and 4-byte
+    aligned; workspace sizing works like the other formats."""
+    c = cfg(T=4, H=512, I=256, E=8, topk=2, wfmt=2, wblk=16, act_group=128)
+    assert ws_size(c)[0] == moe.MOE_OK
+    assert ws_size(cfg(T=4, H=512, I=256, E=8, topk=2, wfmt=2, wblk=32, act_group=128))[0] == moe.MOE_ERR_BAD_SHAPE
+    assert ws_size(cfg(T=4, H=512, I=256, E=8, topk=2, wfmt=2, wblk=16, act_group=32))[0] == moe.MOE_ERR_UNSUPPORTED
+    a4 = cfg(T=4, H=512, I=256, E=8, topk=2, wfmt=2, wblk=16, act_group=32, act_fmt=1)
+    assert ws_size(a4)[0] == moe.MOE_ERR_UNSUPPORTED
+    cc = c.c()
+    _, n = ws_size(c)
+    call = lambda w: moe.raw_call("moe_layer", C.byref(cc), FAKE, FAKE, FAKE, C.byref(w), FAKE, FAKE,
+                                  C.c_size_t(n), None)
+    assert call(_w(w1g=None, w2g=FAKE)) == moe.MOE_ERR_NULL_ARG
+    assert call(_w(w1g=FAKE, w2g=None)) == moe.MOE_ERR_NULL_ARG
+    assert call(_w(w1g=FAKE + 2, w2g=FAKE)) == moe.MOE_ERR_MISALIGNED
+    # a shared expert needs its two matrix scales too
+    cs = cfg(T=4, H=512, I=256, E=8, topk=2, wfmt=2, wblk=16, act_group=128, has_shared=1)
+    ccs = cs.c()
+    ws_ = _w(w1g=FAKE, w2g=FAKE, sw1=FAKE, sw1s=FAKE, sw2=FAKE, sw2s=FAKE)
+    assert moe.raw_call("moe_layer", C.byref(ccs), FAKE, FAKE, FAKE, C.byref(ws_), FAKE, FAKE,
+                        C.c_size_t(ws_size(cs)[1]), None) == moe.MOE_ERR_NULL_ARG
+    # the other formats ignore the matrix-scale fields
+    c8 = cfg(T=4, H=512, I=256, E=8, topk=2, wblk=128, act_group=128)
+    cc8 = c8.c()
+    assert moe.raw_call("moe_layer", C.byref(cc8), FAKE, FAKE, FAKE, C.byref(_w(w1g=FAKE + 2)), FAKE, FAKE,
+                        C.c_size_t(0), None) == moe.MOE_ERR_WORKSPACE
