@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_fp8", help="the headline decode sweep (sets `value`)")
-    ap.add_argument("--extra", default="decode_mxfp4,decode_fp8_zipf_shared",
+    ap.add_argument("--extra", default="decode_mxfp4,decode_nvfp4,decode_fp8_zipf_shared",
                     help="comma-separated further decode sweeps timed in the same steps ('' for none)")
     ap.add_argument("--tokens", default=None, help="comma-separated T values (default: each workload's sweep)")
     ap.add_argument("--roofline-T", type=int, default=64)
