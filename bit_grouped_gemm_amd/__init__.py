@@ -49,7 +49,8 @@ WFMT_NVFP4 = 2
 RATE_E2M1_E2M1 = 16  # moe_mfma_rate's e2m1 x e2m1 operand pair
 
 EXPORTS = ("moe_workspace_size", "moe_permute", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm2",
-           "moe_combine", "moe_layer", "moe_layer_static", "moe_layer_persistent", "moe_prepack_weights",
+           "moe_combine", "moe_layer", "moe_layer_static", "moe_layer_persistent", "moe_layer_persistent_spin_limit",
+           "moe_prepack_weights",
            "moe_stream_read",
            "moe_mfma_rate", "moe_encode_e4m3", "moe_route", "moe_route_workspace_size", "moe_status_str")
 
@@ -93,6 +94,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     L.moe_layer.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp]
     L.moe_layer_static.argtypes = [cfgp, vp, vp, vp, wp, vp, vp]
     L.moe_layer_persistent.argtypes = [cfgp, vp, vp, vp, wp, vp, vp, sz, vp, vp]
+    L.moe_layer_persistent_spin_limit.argtypes = [C.c_int]
     L.moe_prepack_weights.argtypes = [cfgp, wp, wp, vp]
     L.moe_stream_read.argtypes = [vp, sz, vp, sz, vp]
     L.moe_mfma_rate.argtypes = [C.c_int, C.c_int, vp, sz, C.POINTER(C.c_double), vp]
@@ -280,6 +282,15 @@ def moe_layer_persistent(cfg: Cfg, x, topk_ids, topk_weights, weights, ws: Optio
            load().moe_layer_persistent(C.byref(c), _ptr(_u16(x)), _ptr(topk_ids), _ptr(topk_weights), C.byref(w),
                                        _ptr(_u16(out)), _ptr(ws), ws.numel(), _ptr(status), _stream()))
     return out
+
+
+PERSIST_SPIN_LIMIT = 1 << 20  # moe_layer_persistent's default polls per wait
+
+
+def moe_layer_persistent_spin_limit(polls: int) -> None:
+    """Polls per wait of moe_layer_persistent before it expires (process-wide;
+    0 exercises the expiry path)."""
+    _check("moe_layer_persistent_spin_limit", load().moe_layer_persistent_spin_limit(int(polls)))
 
 
 @dataclasses.dataclass

@@ -483,6 +483,12 @@ int moe_layer_persistent(const moe_cfg* cfg, const uint16_t* x, const int32_t* t
                                             static_cast<hipStream_t>(stream)));
 }
 
+int moe_layer_persistent_spin_limit(int polls) {
+  if (polls < 0) return MOE_ERR_BAD_SHAPE;
+  set_persist_spin_limit(polls);
+  return MOE_OK;
+}
+
 int moe_prepack_weights(const moe_cfg* cfg, const moe_weights* canonical, moe_weights* packed, void* stream) {
   if (!cfg || !canonical || !packed) return MOE_ERR_NULL_ARG;
   int rc;

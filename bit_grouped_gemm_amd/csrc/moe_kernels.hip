@@ -22,6 +22,7 @@
 // from HBM into registers, while the few tokens of an expert form the
 // 16-column side.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "moe_device.h"
@@ -1295,6 +1296,10 @@ static int resident_grid(const void* fn) {
   return grid;
 }
 
+// polls per wait of the persistent layer before the wait expires
+static std::atomic<int> g_spin_limit{kPersistSpinLimit};
+void set_persist_spin_limit(int polls) { g_spin_limit.store(polls); }
+
 template <int WF, int NTT, int B32, int NJ>
 static hipError_t launch_persistent_inst(const PersistParams& p, int total, hipStream_t st) {
   const void* fn = reinterpret_cast<const void*>(&k_layer_persistent<WF, NTT, B32, NJ>);
@@ -1340,7 +1345,7 @@ hipError_t launch_layer_persistent(const Shape& s, const uint16_t* x, const int3
   p.n1 = s.g1_items * s.g1_tiles * s.g1_split;
   p.n2 = s.g2_items * s.g2_tiles * s.g2_split;
   p.nC = s.T * ((s.H + kThreads * 8 - 1) / (kThreads * 8));
-  p.spin_limit = 1 << 20;
+  p.spin_limit = g_spin_limit.load();
   const int total = p.n1 + p.n2 + p.nC;
   const bool b32 = s.wfmt == 0 && s.wblk == 32;
 #define MOE_P(WF, NTT, B32)                                                                       \

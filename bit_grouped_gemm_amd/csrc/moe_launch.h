@@ -104,6 +104,8 @@ hipError_t launch_tile_weights(int wfmt, int mats, int N, int K, const uint8_t* 
 // routing launch zeroes it.
 constexpr int kPersistCtlHead = 128;
 constexpr int kPersistMaxItems = 1 << 20;
+constexpr int kPersistSpinLimit = 1 << 20;  // default polls per wait (about a second)
+void set_persist_spin_limit(int polls);
 
 // The layer's buffers inside a workspace (see WsLayout).
 struct LayerBufs {

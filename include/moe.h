@@ -236,6 +236,13 @@ int moe_layer_persistent(const moe_cfg* cfg, const uint16_t* x, const int32_t* t
                          const float* topk_weights, const moe_weights* w, uint16_t* out, void* ws,
                          size_t ws_bytes, int32_t* status, void* stream);
 
+/* Polls each wait of moe_layer_persistent makes before it expires (default
+ * 2^20, about a second; process-wide, read when a call is enqueued).  A
+ * diagnostic: 0 makes every wait that finds its producer unfinished expire
+ * at once, which exercises the expiry path (status > 0, the launch still
+ * ends) without a slow run.  MOE_ERR_BAD_SHAPE for polls < 0. */
+int moe_layer_persistent_spin_limit(int polls);
+
 /* The router in front of the layer, one kernel (the routing GEMM and the
  * routing selection fused, as the DeepGEMM 26/09 news page describes its
  * Mega Gate): for every token t,

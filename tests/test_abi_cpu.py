@@ -366,3 +366,8 @@ def test_nvfp4_host_checks(lib):
     cc8 = c8.c()
     assert moe.raw_call("moe_layer", C.byref(cc8), FAKE, FAKE, FAKE, C.byref(_w(w1g=FAKE + 2)), FAKE, FAKE,
                         C.c_size_t(0), None) == moe.MOE_ERR_WORKSPACE
+
+
+def test_persistent_spin_limit_host_check(lib):
+    assert moe.raw_call("moe_layer_persistent_spin_limit", -1) == moe.MOE_ERR_BAD_SHAPE
+    assert moe.raw_call("moe_layer_persistent_spin_limit", 1 << 20) == moe.MOE_OK

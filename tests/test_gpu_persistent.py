@@ -220,3 +220,29 @@ def test_persistent_chunked_permute():
     cfg = moe.Cfg.for_workload(wl, T)
     out = persistent(cfg, x, ids, tw, w)
     assert same_bits(out, moe.moe_layer(cfg, x, ids, tw, w))
+
+
+def test_persistent_expired_wait_is_reported_and_the_launch_ends():
+    """Forced from the host: with a spin limit of 0 every wait that finds its
+    producer unfinished expires at once.  The launch still ends (the stream
+    synchronises), the status word reports the expiry, and the next call with
+    the default limit is valid again (the routing launch zeroes the control
+    block)."""
+    moe = M()
+    wl = REDUCED["fp8_b128"]
+    T = 37
+    w, _ = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=60)
+    cfg = moe.Cfg.for_workload(wl, T)
+    ref = moe.moe_layer(cfg, x, ids, tw, w).clone()
+    status = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    _note("persistent spin limit 0")
+    moe.moe_layer_persistent_spin_limit(0)
+    try:
+        moe.moe_layer_persistent(cfg, x, ids, tw, w, status=status)
+        torch.cuda.synchronize()
+    finally:
+        moe.moe_layer_persistent_spin_limit(moe.PERSIST_SPIN_LIMIT)
+    assert int(status.item()) >= 1
+    out = persistent(cfg, x, ids, tw, w)
+    assert same_bits(out, ref)
