@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import synth
-from test_gpu_parity import (gemm1_stage_check, gemm2_stage_check, inputs_for, sample_tokens, tol_check,
-                             weights_for)
+from test_gpu_parity import (extreme_rows, gemm1_stage_check, gemm2_stage_check, inputs_for, sample_tokens,
+                             tol_check, weights_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -150,3 +150,42 @@ def test_nvfp4_persistent_is_refused():
     with pytest.raises(moe.MoeError) as e:
         moe.moe_layer_persistent(moe.Cfg.for_workload(wl, 3), x, ids, tw, w)
     assert e.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_nvfp4_extreme_activation_ranges():
+    """Rows whose 128-groups mix all-zero, subnormal and very large values:
+    the fp16 operands stay in range (codes, not values, are converted) and
+    every token matches the oracle within the bound taken over its row."""
+    moe = M()
+    wl = CASES["nvfp4_shared"]
+    T = 37
+    w, wc = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=21)
+    x = extreme_rows(x, wl.act_group).to(DEV)
+    out = moe.moe_layer(moe.Cfg.for_workload(wl, T), x, ids, tw, w)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    ref = oracle.layer_for(wl, T, wc).layer(x.cpu(), ids.cpu(), tw.cpu())
+    assert np.isfinite(got).all() and np.abs(ref).max() > 1e20
+    err = np.abs(got - ref).max(axis=1)
+    assert np.all(err <= 1e-2 * np.abs(ref).max(axis=1) + 1e-3)
+
+
+def test_nvfp4_one_hot_expert_many_passes_and_masked_slots():
+    """Every token on expert 0 (its rows split into many work items, split K)
+    plus masked slots; and the no-allocation entry point on the same call."""
+    moe = M()
+    wl = CASES["nvfp4_split_shared"]
+    T = 150
+    w, wc = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=33)
+    ids = ids.clone()
+    ids[:, 0] = 0
+    ids[::4, 1] = -1
+    cfg = moe.Cfg.for_workload(wl, T)
+    out = moe.moe_layer(cfg, x, ids, tw, w)
+    out_s = moe.moe_layer_static(cfg, x, ids, tw, w)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_s.view(torch.int16))
+    ref = oracle.layer_for(wl, T, wc).layer(x.cpu(), ids.cpu(), tw.cpu())
+    tol_check(out.float().cpu().numpy(), ref, "nvfp4 one-hot")
