@@ -102,14 +102,15 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   const double groups = std::fmin(double(E), double(T) * k);
   const double avg_rows = groups > 0 ? double(T) * k / groups : 0.0;
   // the big-tile kernels keep a pass's token scales in LDS: K <= 8192 for both GEMMs
-  const double min_rows = wfmt == 1 ? kBigMinAvgRowsFp4 : kBigMinAvgRowsFp8;
-  s.big = (G == 128 && (wfmt == 1 || wblk == 128) && H % 256 == 0 && H <= 8192 && I <= 8192 &&
+  const double min_rows = wfmt != 0 ? kBigMinAvgRowsFp4 : kBigMinAvgRowsFp8;
+  s.big = (G == 128 && (wfmt != 0 || wblk == 128) && H % 256 == 0 && H <= 8192 && I <= 8192 &&
            avg_rows >= min_rows) ? 1 : 0;
   if (af == 1) s.big = 1;  // 4-bit activations run the many-row kernels at every T
-  if (wfmt == 2) s.big = 0;  // NVFP4 runs the decode kernels at every T
   // 64 rows per pass while nearly every group fits (mean + 3 sd of a
   // Poisson count), which leaves LDS for a deeper ring; 160 beyond
   s.big_cap = avg_rows + 3.0 * std::sqrt(avg_rows) + 1.0 <= 64.0 ? 64 : 160;
+  // NVFP4's fp16 operands leave registers for 96 token rows per pass
+  if (wfmt == 2 && s.big_cap == 160) s.big_cap = 96;
   if (s.big) s.g1_split = s.g2_split = 1;
   // permute: one block places up to 4096 slots; beyond that the slots are
   // split into at most 64 chunks of at least 2048, each placed by its own

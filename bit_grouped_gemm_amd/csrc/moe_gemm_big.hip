@@ -36,6 +36,13 @@
 // GEMM1 mode: weight rows are 128 gate + 128 up rows (128 h columns = one
 // requantisation group of 128), epilogue SwiGLU + FP8 requantisation.
 // GEMM2 mode: 256 output rows, epilogue writes y.
+// NVFP4 weights (WF = 2: e2m1 codes, an e4m3 scale per 16 along K, an fp32
+// scale per matrix): code tiles as MXFP4's, 2 KB of e4m3 scale tiles per
+// unit and step; both operands are turned into fp16 in registers (exact) and
+// multiplied on the fp16 MFMA (four 16x16x32 per 16x16x128 block), each
+// step's products promoted with a VALU FMA like e4m3's; 96 token rows per
+// pass at most (the fp16 operands and the step's products leave too few
+// registers for more: 128 spilled inside the K loop and ran no faster).
 // 4-bit activations (AF = 1, MXFP4 weights only): token rows are 64 bytes per
 // K step (e2m1, two per byte) and their scales e8m0 per 32 channels, so the
 // token operand's scale goes into the MFMA's B-operand scale like the
@@ -70,8 +77,9 @@ template <int WF, int CAP, int AF> struct BigGeo {
   static constexpr int kTokTileBytes = AF ? 1024 : 2048;     // 16 rows x 64 B (e2m1) or 128 B (e4m3)
   static constexpr int kTokLoads = AF ? kTokTiles : 2 * kTokTiles;  // 1 KB each: 16 x 64 B or 8 x 128 B
   static constexpr int kTokSlots = (kTokLoads + 7) / 8;      // token-row loads of one wave
-  static constexpr int kWLoads = WF == 1 ? kWTiles : 2 * kWTiles;  // 1 KB each
-  static constexpr int kScLoads = WF == 1 ? 1 : 0;           // 16 tiles x 64 B of e8m0 scales
+  static constexpr int kWLoads = WF != 0 ? kWTiles : 2 * kWTiles;  // 1 KB each
+  // 16 tiles x 64 B of e8m0 scales (MXFP4), or x 128 B of e4m3 scales (NVFP4)
+  static constexpr int kScLoads = WF == 1 ? 1 : WF == 2 ? 2 : 0;
   static constexpr int kL = (kTokLoads + kWLoads + kScLoads + 7) / 8;
   static constexpr int kWOff = kTokTiles * kTokTileBytes;    // token tiles, chunk-swizzled
   static constexpr int kScOff = kWOff + kWLoads * 1024;
@@ -101,6 +109,8 @@ struct BigParams {
   const void* ws;
   const uint8_t* sw;
   const void* sws;
+  const float* wg;   // NVFP4: fp32 scale per routed matrix
+  const float* swg;  // and the shared expert's
   uint8_t* hq;
   float* hs;
   float* y;
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
   const int ka = AF ? K / 2 : K;         // bytes per token row
   const int nks = K / 128;
   const long wstep = long(NR / 16) * kTileBytes<WF>;  // tiled weights: bytes per K step
-  const long sstep = long(NR / 16) * kTileScaleBytes;
+  const long sstep = long(NR / 16) * (WF == 2 ? kTileScaleBytes16 : kTileScaleBytes);
   // this wave's weight tiles among the unit's 16 (GEMM1: tiles 0..7 are gate
   // rows, 8..15 the up rows of the same h columns; GEMM2 rows in order)
   int ja[4];
@@ -287,6 +297,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
   int tab_row = 0;          // this wave's token-scale rows of the pass (lane i: token w + 8 i)
   const float* ws_src = nullptr;  // e4m3: the block-scale row this wave loads (waves 0, 1)
   int ld_row = 0, ld_npass = 0, ld_n0 = 0, ld_ntw = 0;  // first row of the pass, its rows, unit column, tiles
+  float ld_gsc = 1.0f;      // NVFP4: the matrix scale of the pass's expert
   auto setup = [&](int4 ent, int pass) __attribute__((always_inline)) {
     if (!pf_ok) prefetch(ent, pass);
     pf_ok = false;
@@ -300,6 +311,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
     const long ee = shared ? 0 : e;
     const uint8_t* wmat = (shared ? p.sw : p.w) + ee * long(NR) * kb;
     const void* smat = shared ? p.sws : p.ws;
+    if (WF == 2) ld_gsc = shared ? p.swg[0] : p.wg[ee];
     const int n0 = ld_n0;
     // first matrix row of unit weight tile t (0..15)
     auto wtile_row = [&](int t) __attribute__((always_inline)) { return MODE == 0 ? (t < 8 ? n0 + 16 * t : I + n0 + 16 * (t - 8)) : n0 + 16 * t; };
@@ -322,17 +334,26 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
         dst16[j] = i * 1024;
       } else if (i < Geo::kTokLoads + Geo::kWLoads) {
         const int wi = i - Geo::kTokLoads;
-        const int t = WF == 1 ? wi : wi >> 1, half = WF == 1 ? 0 : wi & 1;
+        const int t = WF != 0 ? wi : wi >> 1, half = WF != 0 ? 0 : wi & 1;
         src16[j] = wmat + long(wtile_row(t) / 16) * kTileBytes<WF> + half * 1024 + lane * 16;
         stride16[j] = wstep;
         dst16[j] = Geo::kWOff + wi * 1024;
       } else if (i < Geo::kTokLoads + Geo::kWLoads + Geo::kScLoads) {
-        // the 16 tiles' e8m0 scales: lanes 0..31 the 8 tiles from unit tile 0
-        // (512 adjacent bytes), lanes 32..63 those from unit tile 8
-        const uint8_t* sb = static_cast<const uint8_t*>(smat) + ee * long(NR) * (K / 32);
-        src16[j] = sb + long(wtile_row(lane < 32 ? 0 : 8) / 16) * kTileScaleBytes + (lane & 31) * 16;
+        if (WF == 2) {
+          // NVFP4: load si = 0 the 8 tiles from unit tile 0 (1 KB adjacent),
+          // si = 1 those from unit tile 8
+          const int si = i - Geo::kTokLoads - Geo::kWLoads;
+          const uint8_t* sb = static_cast<const uint8_t*>(smat) + ee * long(NR) * (K / 16);
+          src16[j] = sb + long(wtile_row(8 * si) / 16) * kTileScaleBytes16 + lane * 16;
+          dst16[j] = Geo::kScOff + si * 1024;
+        } else {
+          // the 16 tiles' e8m0 scales: lanes 0..31 the 8 tiles from unit tile 0
+          // (512 adjacent bytes), lanes 32..63 those from unit tile 8
+          const uint8_t* sb = static_cast<const uint8_t*>(smat) + ee * long(NR) * (K / 32);
+          src16[j] = sb + long(wtile_row(lane < 32 ? 0 : 8) / 16) * kTileScaleBytes + (lane & 31) * 16;
+          dst16[j] = Geo::kScOff;
+        }
         stride16[j] = sstep;
-        dst16[j] = Geo::kScOff;
       } else {  // spare slot: one hot line into the sink
         src16[j] = wmat;
         stride16[j] = 0;
@@ -425,6 +446,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
                 "epilogue buffers fit one stage");
   uint8_t* const ebuf = stage_ptr(S - 1);
   int c_row = 0, c_npass = 0, c_n0 = 0, c_ntw = 0;
+  float c_gsc = 1.0f;
   auto epi1 = [&]() __attribute__((always_inline)) {
     if (MODE == 0 && AF) {
       // 4-bit activations: the wave row's 32 h columns of a token are one
@@ -464,6 +486,9 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
         if (WF == 1)
 #pragma unroll
           for (int q = 0; q < 4; ++q) acc[q][tt] *= xsp[tt];
+        if (WF == 2)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q][tt] *= c_gsc;
         float amax = 0.0f;
 #pragma unroll
         for (int q = 0; q < 2; ++q)
@@ -489,7 +514,8 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
         const int t0 = (2 * tt + wc) * 16;
         v4f v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = (WF == 1 && !AF) ? acc[q][tt] * xsp[tt] : acc[q][tt];
+        for (int q = 0; q < 4; ++q)
+          v[q] = (WF == 1 && !AF) ? acc[q][tt] * xsp[tt] : WF == 2 ? acc[q][tt] * c_gsc : acc[q][tt];
         if (p.yb) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -603,6 +629,12 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
           af[q] = v8i{int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
           sa[q] = st[Geo::kScOff + ja[q] * kTileScaleBytes + lane];
           wsv[q] = 1.0f;
+        } else if (WF == 2) {
+          // codes as MXFP4's; the lane's two e4m3 block scales (16-blocks 2g, 2g + 1 of row m)
+          const v4u a = *reinterpret_cast<const v4u*>(st + Geo::kWOff + ja[q] * 1024 + lane * 16);
+          af[q] = v8i{int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
+          sa[q] = *reinterpret_cast<const uint16_t*>(st + Geo::kScOff + ja[q] * kTileScaleBytes16 + 8 * m + 2 * g);
+          wsv[q] = 1.0f;
         } else {
           const v4u lo = *reinterpret_cast<const v4u*>(st + Geo::kWOff + (2 * ja[q]) * 1024 + lane * 16);
           const v4u hi = *reinterpret_cast<const v4u*>(st + Geo::kWOff + (2 * ja[q] + 1) * 1024 + lane * 16);
@@ -623,8 +655,10 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
           bf[tt] = v8i{int(b[0]), int(b[1]), int(b[2]), int(b[3]), 0, 0, 0, 0};
           sb[tt] = int((__float_as_uint(xsv[tt]) >> (8 * g)) & 0xFFu);
         } else {
-          const v4u lo = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, g));
-          const v4u hi = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, 4 + g));
+          // e4m3 operand order: chunks g and 4 + g of the row's 128 bytes;
+          // NVFP4's fp16 path: the lane's 32 consecutive K, chunks 2g, 2g + 1
+          const v4u lo = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, WF == 2 ? 2 * g : g));
+          const v4u hi = *reinterpret_cast<const v4u*>(st + t * 2048 + tok_swz(m, WF == 2 ? 2 * g + 1 : 4 + g));
           bf[tt] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
         }
       }
@@ -647,6 +681,56 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
     // is one) go out into stage iss between the token tiles
     auto MMA = [&](int kn, uint8_t* iss) __attribute__((always_inline)) {
       const bool go = kn < nks;
+      if (WF == 2) {
+        // NVFP4: the step as four K quarters (lane group g: K 32 g + 8 i ..
+        // + 7 of both operands in quarter i), taken for two token tiles at a
+        // time so the step's products fit registers next to the
+        // accumulators: per pair and quarter the weights are turned into
+        // fp16 (code times block scale, exact), each token tile's e4m3 codes
+        // likewise (exact); the pair's products are then promoted with the
+        // token scale.  The loads of step kn go out between the quarters.
+        constexpr int NP = (NT + 1) / 2;  // token-tile pairs
+#pragma unroll
+        for (int h = 0; h < NP; ++h) {
+          v4f d[4][2];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) d[q][0] = d[q][1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            h8v a[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              // converted again for every pair: an opaque copy of the codes
+              // keeps the compiler from holding all four quarters' fp16
+              // weights (64 registers) live across the pairs
+              uint32_t cw = uint32_t(af[q][i]);
+              asm volatile("" : "+v"(cw));
+              const h2v sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(uint32_t(sa[q]), 1.0f, false);
+              a[q] = cvt_e2m1x8_f16(cw) * (i < 2 ? sc[0] : sc[1]);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int tt = 2 * h + u;
+              if (tt >= NT) break;
+              const h8v b = cvt_e4m3x8_f16(bf[tt][2 * i], bf[tt][2 * i + 1]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) d[q][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[q], b, d[q][u], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(kSchedMayCross);
+            if (go) issue_range(kn, iss, (4 * h + i) * L / (4 * NP), (4 * h + i + 1) * L / (4 * NP));
+            __builtin_amdgcn_sched_barrier(kSchedMayCross);
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int tt = 2 * h + u;
+            if (tt >= NT) break;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q][tt] += d[q][u] * xsv[tt];
+          }
+        }
+        if (NT == 0 && go) issue_range(kn, iss, 0, L);
+        return;
+      }
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
         if (AF) {
@@ -738,7 +822,7 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
     // ---- the pass's epilogue first (the accumulators die with it, which
     // leaves the registers to the next pass's set-up), then the next pass's
     // first loads: every stage is free (the last reads were in B(nks - 1))
-    c_row = ld_row; c_npass = ld_npass; c_n0 = ld_n0; c_ntw = ld_ntw;
+    c_row = ld_row; c_npass = ld_npass; c_n0 = ld_n0; c_ntw = ld_ntw; c_gsc = ld_gsc;
     epi1();
     lds_barrier();
     epi2();
@@ -791,6 +875,9 @@ static hipError_t launch_big(const Shape& s, int mode, BigParams& p, hipStream_t
   } else if (s.wfmt == 0) {
     if (s.big_cap == 64) MOE_BIG_LAUNCH(0, 64, 0);
     else MOE_BIG_LAUNCH(0, 160, 0);
+  } else if (s.wfmt == 2) {
+    if (s.big_cap == 64) MOE_BIG_LAUNCH(2, 64, 0);
+    else MOE_BIG_LAUNCH(2, 96, 0);
   } else {
     if (s.big_cap == 64) MOE_BIG_LAUNCH(1, 64, 0);
     else MOE_BIG_LAUNCH(1, 160, 0);
@@ -805,7 +892,7 @@ hipError_t launch_gemm1_big(const Shape& s, const uint8_t* xq, const float* xs, 
                             hipStream_t st) {
   BigParams p{};
   p.act = xq; p.act_s = xs; p.row_token = row_token; p.offsets = offsets;
-  p.w = w1.w; p.ws = w1.ws; p.sw = w1.sw; p.sws = w1.sws;
+  p.w = w1.w; p.ws = w1.ws; p.sw = w1.sw; p.sws = w1.sws; p.wg = w1.g; p.swg = w1.sg;
   p.hq = hq; p.hs = hs;
   p.H = s.H; p.I = s.I; p.E = s.E; p.G = s.G; p.wblk = s.wblk; p.ngroups = s.ngroups;
   p.ntiles = s.I / 128; p.min_rows = min_rows;
@@ -816,7 +903,7 @@ hipError_t launch_gemm2_big(const Shape& s, const uint8_t* hq, const float* hs, 
                             WeightPtrs w2, float* y, uint16_t* yb, int min_rows, hipStream_t st) {
   BigParams p{};
   p.act = hq; p.act_s = hs; p.offsets = offsets;
-  p.w = w2.w; p.ws = w2.ws; p.sw = w2.sw; p.sws = w2.sws;
+  p.w = w2.w; p.ws = w2.ws; p.sw = w2.sw; p.sws = w2.sws; p.wg = w2.g; p.swg = w2.sg;
   p.y = y;
   p.yb = yb;
   p.H = s.H; p.I = s.I; p.E = s.E; p.G = s.G; p.wblk = s.wblk; p.ngroups = s.ngroups;

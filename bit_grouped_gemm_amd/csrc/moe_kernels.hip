@@ -316,27 +316,6 @@ __device__ int nth_item(const int32_t* offsets, int ngroups, int item, int R, in
   return s_res[0];
 }
 
-typedef _Float16 h8v __attribute__((ext_vector_type(8)));
-typedef _Float16 h2v __attribute__((ext_vector_type(2)));
-
-// Eight e2m1 codes (one word, low nibble first = lower K) as f16 (exact).
-__device__ __forceinline__ h8v cvt_e2m1x8_f16(uint32_t w) {
-  const h2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
-  const h2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
-  const h2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
-  const h2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
-  return h8v{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// Eight e4m3 codes (two words, byte order = K order) as f16 (exact).
-__device__ __forceinline__ h8v cvt_e4m3x8_f16(int w0, int w1) {
-  const h2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(uint32_t(w0), 1.0f, false);
-  const h2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(uint32_t(w0), 1.0f, true);
-  const h2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(uint32_t(w1), 1.0f, false);
-  const h2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(uint32_t(w1), 1.0f, true);
-  return h8v{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
 // Operands of one 128-K step for a wave: NJ weight tiles of 16 rows and NTT
 // token tiles of 16 columns.
 template <int WF, int NJ, int NTT>

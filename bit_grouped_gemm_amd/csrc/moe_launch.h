@@ -29,7 +29,7 @@ struct Shape {
   // groups with many rows (prefill, larger decode batches) run the LDS-staged
   // kernels: 256 weight rows x big_cap token rows per pass
   int big;          // 1: both GEMMs use the big-tile kernels
-  int big_cap;      // their token rows per pass: 64 or 160
+  int big_cap;      // their token rows per pass: 64 or 160 (NVFP4: 64 or 96)
   // permute: slots per chunk and chunk count; one chunk = one block places
   // every slot, more = a counting pass then one placing block per chunk
   int perm_chunk, perm_chunks;

@@ -80,7 +80,7 @@ enum { MOE_AFMT_FP8 = 0, MOE_AFMT_MXFP4 = 1 };
  *          scale (the pages name NVFP4 beside MXFP4 in the onnxruntime QMoE
  *          PR's shared 4-bit expert layouts; this is its published
  *          two-level definition).  act_group must be 128 and act_fmt FP8;
- *          every T runs the decode kernels.
+ *          both operands are multiplied as fp16 (exact).
  *   has_shared = 1 adds one always-on shared expert (same format and I) to
  *   every token with weight 1 (GC-MoE abstract: shared experts as an
  *   option; FusedDeepMoE shared-expert path: all tokens in one group).

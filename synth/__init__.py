@@ -87,6 +87,10 @@ WORKLOADS: Dict[str, Workload] = {
     "prefill_mxfp4": Workload("prefill_mxfp4", H=7168, E=256, topk=8, I=2048, wfmt=FMT_MXFP4,
                               wblk=32, act_group=128, routing="uniform", shared=False,
                               tokens=(4096,), wid=4),
+    # prefill NVFP4 weights against e4m3 activations, same shapes and routing
+    "prefill_nvfp4": Workload("prefill_nvfp4", H=7168, E=256, topk=8, I=2048, wfmt=FMT_NVFP4,
+                              wblk=16, act_group=128, routing="uniform", shared=False,
+                              tokens=(4096,), wid=7),
     # the 4-bit-activation variant of the prefill layer: MXFP4 weights and MXFP4
     # activations (e2m1 with an e8m0 scale per 32 channels), same shapes and routing
     "prefill_mxfp4_a4": Workload("prefill_mxfp4_a4", H=7168, E=256, topk=8, I=2048, wfmt=FMT_MXFP4,

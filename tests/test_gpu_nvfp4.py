@@ -1,10 +1,10 @@
 """GPU parity of the NVFP4-weight path (e2m1 codes, an e4m3 scale per 16 along
 K, an fp32 scale per expert matrix) against the CPU oracle.
 
-The decode kernels run it at every T: e2m1 codes and activations are turned
-into fp16 in registers (exact: a code times a block scale has at most six
-significant bits) and multiplied on the fp16 MFMA, the matrix scale applied
-once per output.  Tolerances as for the other formats.
+Both kernel families run it: e2m1 codes and activations are turned into fp16
+in registers (exact: a code times a block scale has at most six significant
+bits) and multiplied on the fp16 MFMA, the matrix scale applied once per
+output.  Tolerances as for the other formats.
 """
 import sys
 
@@ -93,12 +93,16 @@ def test_layer_nvfp4_reduced(name, T):
     tol_check(out.float().cpu().numpy(), ref, f"{name} T={T}")
 
 
-@pytest.mark.parametrize("name,T", [("nvfp4", 37), ("nvfp4_shared", 64), ("nvfp4_split_shared", 5)])
+# T = 200 on "nvfp4" and "nvfp4_split_shared" (50 rows per expert) takes the
+# many-row kernels (128-token passes), the rest the decode kernels
+@pytest.mark.parametrize("name,T", [("nvfp4", 37), ("nvfp4_shared", 64), ("nvfp4_split_shared", 5),
+                                    ("nvfp4", 200), ("nvfp4_split_shared", 200)])
 def test_gemm1_stage_nvfp4(name, T):
     gemm1_stage_check(CASES[name], T, name)
 
 
-@pytest.mark.parametrize("name,T", [("nvfp4", 29), ("nvfp4_shared", 64), ("nvfp4_split_shared", 5)])
+@pytest.mark.parametrize("name,T", [("nvfp4", 29), ("nvfp4_shared", 64), ("nvfp4_split_shared", 5),
+                                    ("nvfp4", 200), ("nvfp4_split_shared", 200)])
 def test_gemm2_stage_nvfp4(name, T):
     gemm2_stage_check(CASES[name], T, name)
 
@@ -189,3 +193,43 @@ def test_nvfp4_one_hot_expert_many_passes_and_masked_slots():
     assert torch.equal(out.view(torch.int16), out_s.view(torch.int16))
     ref = oracle.layer_for(wl, T, wc).layer(x.cpu(), ids.cpu(), tw.cpu())
     tol_check(out.float().cpu().numpy(), ref, "nvfp4 one-hot")
+
+
+def test_layer_nvfp4_prefill_size_sampled():
+    """The prefill shape (T = 4096, H = 7168, E = 256, top-8, I = 2048) with
+    NVFP4 weights, on the many-row kernels: 256 sampled tokens against the
+    oracle."""
+    moe = M()
+    wl = synth.WORKLOADS["prefill_nvfp4"]
+    T = 4096
+    _note("full prefill_nvfp4 T=4096")
+    w, wc = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=0)
+    cfg = moe.Cfg.for_workload(wl, T)
+    out = moe.moe_layer(cfg, x, ids, tw, w, ws=moe.workspace(cfg))
+    torch.cuda.synchronize()
+    toks = sample_tokens(T, T)
+    ref = oracle.layer_for(wl, T, wc).layer(x.cpu(), ids.cpu(), tw.cpu(), toks=toks)
+    tol_check(out.float().cpu().numpy()[toks], ref, f"prefill_nvfp4 sampled {len(toks)}")
+
+
+@pytest.mark.parametrize("T", [200, 700])
+def test_nvfp4_many_row_kernels_deterministic(T):
+    """The many-row kernels' waves share LDS stages and tables: repeated
+    calls with a poisoned workspace are bit-identical (a race would show as
+    differing outputs), and the layer is within the bound of the oracle
+    (T = 700: 175 rows per expert, so the larger groups take two passes)."""
+    moe = M()
+    wl = CASES["nvfp4"]
+    w, wc = weights_for(wl)
+    x, ids, tw = inputs_for(wl, T, seed=44)
+    cfg = moe.Cfg.for_workload(wl, T)
+    ws = moe.workspace(cfg)
+    ws.fill_(0xFF)
+    a = moe.moe_layer(cfg, x, ids, tw, w, ws=ws).clone()
+    ws.fill_(0x00)
+    b = moe.moe_layer(cfg, x, ids, tw, w, ws=ws).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = oracle.layer_for(wl, T, wc).layer(x.cpu(), ids.cpu(), tw.cpu())
+    tol_check(a.float().cpu().numpy(), ref, f"nvfp4 many-row T={T}")
