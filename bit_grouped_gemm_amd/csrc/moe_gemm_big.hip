@@ -128,9 +128,6 @@ __device__ __forceinline__ void dma16(const void* src, uint8_t* lds_base) {
 __device__ __forceinline__ void dma16nt(const void* src, uint8_t* lds_base) {
   __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 2);
 }
-__device__ __forceinline__ void dma4(const void* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, lds_base, 4, 0, 0);
-}
 
 // wait until at most N vector-memory operations of this wave are pending
 // (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, other counters at
@@ -385,17 +382,27 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
   };
   auto stage_ptr = [&](int s) __attribute__((always_inline)) -> uint8_t* { return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3; };
   // first loads of a pass: the token-scale table (one load per token: its
-  // nks scales are contiguous; lanes past them repeat the last), the e4m3
-  // block-scale rows, then steps 0 .. S - 2 into stages 0 .. S - 2.  The
-  // tables are older than every stage load, so the wait for step 0 covers
+  // nks scales are contiguous; lanes past them repeat the last) and the
+  // e4m3 block-scale rows, written to LDS by the waves themselves, then
+  // steps 0 .. S - 2 into stages 0 .. S - 2.  The tables go through
+  // registers, not direct-to-LDS loads: the compiler tracks a direct-to-LDS
+  // load by its LDS target, and a K loop that reads a table so filled got a
+  // wait for every load in flight (the ring's included) on each of its
+  // iterations.  Filled this way, the tables cost one wait per pass, before
+  // the first stage is issued; the first barrier of the K loop publishes
   // them.
   auto prologue = [&]() __attribute__((always_inline)) {
+    float tv[Geo::kTabLoads];
 #pragma unroll
     for (int i = 0; i < Geo::kTabLoads; ++i) {
       const int arow = __builtin_amdgcn_readlane(tab_row, i);
-      dma4(p.act_s + long(arow) * nks + min(lane, nks - 1), reinterpret_cast<uint8_t*>(xs_tab + (w + 8 * i) * kXsRow));
+      tv[i] = p.act_s[long(arow) * nks + min(lane, nks - 1)];
     }
-    if (WF == 0 && w < 2) dma4(ws_src + min(lane, nks - 1), reinterpret_cast<uint8_t*>(ws_tab + w * kXsRow));
+    float wv = 0.0f;
+    if (WF == 0 && w < 2) wv = ws_src[min(lane, nks - 1)];
+#pragma unroll
+    for (int i = 0; i < Geo::kTabLoads; ++i) xs_tab[(w + 8 * i) * kXsRow + lane] = tv[i];
+    if (WF == 0 && w < 2) ws_tab[w * kXsRow + lane] = wv;
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
       if (s < nks) issue_range(s, stage_ptr(s), 0, L);
@@ -622,6 +629,12 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
     v8i bf[NA];
     // the fragments of step k in stage st; MXFP4: rescale to its token scales
     auto READ = [&](const uint8_t* st, int k) __attribute__((always_inline)) {
+      // the step index passes through an empty asm statement, so the table
+      // addresses are formed afresh at each step rather than carried in a
+      // loop register (which the compiler may spill and reload before the
+      // loop, and whose first use in the loop then waits for every load in
+      // flight)
+      asm volatile("" : "+s"(k));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (WF == 1) {
