@@ -227,6 +227,9 @@ def main():
     stream_gbs = stream_read_gbs(moe, flush, stream, ev)
     for r in results.values():
         r["roofline_gemm1"]["frac_of_stream_read"] = round(r["roofline_gemm1"]["achieved"] / stream_gbs, 4)
+        # each layer's weight rate against what a plain read stream reaches on this part
+        for e in r["sweep"].values():
+            e["frac_of_stream_read"] = round(e["weight_GBps"] / stream_gbs, 4)
     hr = head["roofline_gemm1"]
     traffic = load_traffic(args.workload, hr["T"])
     wl = sweeps[args.workload].wl
