@@ -8,9 +8,10 @@
 //   * both operands of a step travel HBM/L2 -> LDS by direct-to-LDS loads
 //     (global_load_lds: 64 lanes x 16 B into 1 KB of LDS per instruction,
 //     no registers held while in flight) through a ring of up to four
-//     stages; a stage holds the step's token rows, weight tiles, MXFP4
-//     scales (or the two e4m3 block scales) and the pass's token scales of
-//     that step, so nothing else is read from memory in the K loop;
+//     stages; a stage holds the step's token rows, weight tiles and MXFP4 or
+//     NVFP4 weight scales, and the pass's token scales (and a unit's e4m3
+//     block scales) sit in per-pass LDS tables, so nothing else is read from
+//     memory in the K loop;
 //   * weights come from the tiled layout (16-row x 128-K tiles in MFMA lane
 //     order, see moe_tile.hip), one contiguous kilobyte per tile and step,
 //     and land in LDS unchanged, so fragment reads are linear ds_read_b128;
@@ -32,7 +33,7 @@
 //     XCDs), so the expert's token rows are fetched into that XCD's L2 once;
 //     each workgroup finds its units' groups once (a table in LDS), loads
 //     the next pass's token-row indices while the current pass runs, and
-//     issues the next pass's first ring stages before its epilogue.
+//     issues the next pass's first ring stages right after its epilogue.
 // GEMM1 mode: weight rows are 128 gate + 128 up rows (128 h columns = one
 // requantisation group of 128), epilogue SwiGLU + FP8 requantisation.
 // GEMM2 mode: 256 output rows, epilogue writes y.
@@ -696,51 +697,39 @@ __global__ __launch_bounds__(kBigThreads) void k_gemm_big(BigParams p) {
       const bool go = kn < nks;
       if (WF == 2) {
         // NVFP4: the step as four K quarters (lane group g: K 32 g + 8 i ..
-        // + 7 of both operands in quarter i), taken for two token tiles at a
-        // time so the step's products fit registers next to the
-        // accumulators: per pair and quarter the weights are turned into
-        // fp16 (code times block scale, exact), each token tile's e4m3 codes
-        // likewise (exact); the pair's products are then promoted with the
-        // token scale.  The loads of step kn go out between the quarters.
-        constexpr int NP = (NT + 1) / 2;  // token-tile pairs
+        // + 7 of both operands in quarter i): per quarter the wave's four
+        // weight tiles are turned into fp16 once (code times block scale,
+        // exact) and multiplied with every token tile, whose e4m3 codes are
+        // turned into fp16 likewise (exact); the step's products, one set
+        // per token tile, are then promoted with the token scale.  The loads
+        // of step kn go out between the quarters.
+        v4f d[4][NA];
 #pragma unroll
-        for (int h = 0; h < NP; ++h) {
-          v4f d[4][2];
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) d[q][0] = d[q][1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          for (int tt = 0; tt < NA; ++tt) d[q][tt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            h8v a[4];
+        for (int i = 0; i < 4; ++i) {
+          h8v a[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              // converted again for every pair: an opaque copy of the codes
-              // keeps the compiler from holding all four quarters' fp16
-              // weights (64 registers) live across the pairs
-              uint32_t cw = uint32_t(af[q][i]);
-              asm volatile("" : "+v"(cw));
-              const h2v sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(uint32_t(sa[q]), 1.0f, false);
-              a[q] = cvt_e2m1x8_f16(cw) * (i < 2 ? sc[0] : sc[1]);
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int tt = 2 * h + u;
-              if (tt >= NT) break;
-              const h8v b = cvt_e4m3x8_f16(bf[tt][2 * i], bf[tt][2 * i + 1]);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) d[q][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[q], b, d[q][u], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(kSchedMayCross);
-            if (go) issue_range(kn, iss, (4 * h + i) * L / (4 * NP), (4 * h + i + 1) * L / (4 * NP));
-            __builtin_amdgcn_sched_barrier(kSchedMayCross);
+          for (int q = 0; q < 4; ++q) {
+            const h2v sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(uint32_t(sa[q]), 1.0f, false);
+            a[q] = cvt_e2m1x8_f16(uint32_t(af[q][i])) * (i < 2 ? sc[0] : sc[1]);
           }
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int tt = 2 * h + u;
-            if (tt >= NT) break;
+          for (int tt = 0; tt < NT; ++tt) {
+            const h8v b = cvt_e4m3x8_f16(bf[tt][2 * i], bf[tt][2 * i + 1]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[q][tt] += d[q][u] * xsv[tt];
+            for (int q = 0; q < 4; ++q) d[q][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[q], b, d[q][tt], 0, 0, 0);
           }
+          __builtin_amdgcn_sched_barrier(kSchedMayCross);
+          if (go) issue_range(kn, iss, i * L / 4, (i + 1) * L / 4);
+          __builtin_amdgcn_sched_barrier(kSchedMayCross);
         }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q][tt] += d[q][tt] * xsv[tt];
         if (NT == 0 && go) issue_range(kn, iss, 0, L);
         return;
       }
