@@ -324,7 +324,7 @@ def summarize(sw, rec, graph_us):
 
 
 def router_section(moe, synth, torch, flush, stream, ev, reps=20):
-    """moe_route (gate GEMM + top-k + softmax; two kernels up to 512 tokens) on the decode FP8
+    """moe_route (gate GEMM with K splits, then the per-token reduction + top-k + softmax) on the decode FP8
     layer's shape (H=4096, E=64, top-8) at T = 1, 64, 256 and the prefill
     shape (H=7168, E=256, top-8) at T = 4096, cold caches: median latency,
     bytes moved (x, gate rows, ids and weights) per second, TFLOP/s."""
@@ -352,6 +352,7 @@ def router_section(moe, synth, torch, flush, stream, ev, reps=20):
         nbytes = 2 * T * wl.H + 2 * wl.E * wl.H + 8 * T * wl.topk
         out[f"H{wl.H}_E{wl.E}_T{T}"] = {"latency_us_median": round(us, 2), "bytes": nbytes,
                                         "GBps": round(nbytes / us / 1e3, 1),
+                                        "hbm_frac": round(nbytes / us / 1e3 / 8000.0, 4),
                                         "TFLOPs": round(2.0 * T * wl.E * wl.H / us / 1e6, 2)}
     return out
 

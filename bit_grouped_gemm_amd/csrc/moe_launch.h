@@ -88,9 +88,9 @@ int mfma_rate_grid();
 hipError_t launch_mfma_rate(int wfmt, int iters, float* sink, double* flops, hipStream_t st);
 hipError_t launch_encode_e4m3(const float* v, long n, uint8_t* codes, hipStream_t st);
 
-// router (moe_router.hip): gate GEMM + top-k + softmax of the selected logits;
-// up to 512 tokens it runs as two kernels over `part`, a scratch of
-// route_workspace_bytes(T, H, E) bytes (0 above: part may be null)
+// router (moe_router.hip): gate GEMM + top-k + softmax of the selected logits,
+// two kernels over `part`, a scratch of route_workspace_bytes(T, H, E) bytes
+// (0 only for T = 0)
 size_t route_workspace_bytes(int T, int H, int E);
 hipError_t launch_route_gemm(int T, int H, int E, int k, const uint16_t* x, const uint16_t* wg, int32_t* ids,
                              float* weights, float* part, hipStream_t st);

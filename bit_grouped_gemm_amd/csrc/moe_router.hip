@@ -1,23 +1,24 @@
-// moe_router.hip -- the router in front of the MoE layer, one kernel: gate
-// GEMM (bf16 MFMA, fp32 accumulation), top-k selection and the softmax of
-// the selected logits.  This is the fusion the DeepGEMM 26/09 news page
-// describes for its Mega Gate (the routing GEMM and the routing operations
-// -- matrix product, selection, data organisation -- in one kernel, so no
-// logits go back to memory and no second launch is needed).
+// moe_router.hip -- the router in front of the MoE layer: gate GEMM (bf16
+// MFMA, fp32 accumulation), top-k selection and the softmax of the selected
+// logits.  The DeepGEMM 26/09 news page describes this fusion for its Mega
+// Gate (the routing GEMM and the routing operations -- matrix product,
+// selection, data organisation -- in one kernel).  Here it is two launches
+// at every T: the GEMM spreads the gate matrix over enough workgroups to
+// fill the chip and writes fp32 partial logits per K split to the caller's
+// workspace; a second kernel sums each token's splits in a fixed order and
+// selects (one workgroup per token), so the result does not depend on
+// timing.  The partials are the price of the split, 4 E bytes per token and
+// split (16.8 MB at 4096 tokens, 256 experts, four splits); one kernel
+// holding a token's whole K cannot fill the CUs below tens of thousands of
+// tokens.
 //
-// Up to 512 tokens (decode) the gate matrix is spread over many workgroups:
-// one wave per (16-token tile, 16-expert tile, K chunk) writes fp32 partial
-// logits to the caller's workspace, and a second kernel sums each token's
-// chunks in a fixed order and selects (one workgroup per token).  Above that one
-// kernel: a workgroup owns NTT tiles of 16 tokens and every expert, its waves
-// forming 4 expert slots x KG K groups (the wave of slot j and group g runs
-// expert tiles j, j + 4, j + 8, j + 12 over its group's share of K, keeping
-// RS register stages of 64 K in flight), with the gate rows on the MFMA's
-// 16-row side and the tokens on its 16-column side; the K groups' partial
-// logits meet in LDS and are summed in group order.  Either way the result
-// does not depend on timing.  The selection: k rounds of a wave-wide argmax
-// (equal logits going to the lower expert id), then the softmax of the k
-// selected logits.
+// Up to 512 tokens (decode) the GEMM is one wave per (16-token tile,
+// 16-expert tile, K chunk), its operands loaded straight into registers.
+// Above, one workgroup per (64-token tile, K split) stages its token rows
+// and every expert's gate rows through LDS (k_route_tile), so each gate row
+// is read once per 64 tokens.  The selection: k rounds of a wave-wide
+// argmax (equal logits going to the lower expert id), then the softmax of
+// the k selected logits.
 
 #include <float.h>
 
@@ -33,14 +34,6 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kRouteThreads = 256;
 constexpr int kMaxExpertTiles = 16;   // E <= 256
 constexpr int kStageK = 64;           // K per pipeline stage: two 16x16x32 MFMA steps
-
-struct RouteGemmParams {
-  const uint16_t* x;   // bf16 [T][H]
-  const uint16_t* wg;  // bf16 [E][H]
-  int32_t* ids;        // [T][k]
-  float* weights;      // [T][k]
-  int T, H, E, k;
-};
 
 // Lane l's operand bytes of one stage: 16 rows (lane % 16) x 64 K, lane
 // group g = l / 16 holding K [16 g, 16 g + 16) of the stage as two 8-element
@@ -99,109 +92,126 @@ __device__ __forceinline__ void select_topk(const float (&v)[4], int E, int k, i
   }
 }
 
-template <int NTT, int KG, int RS, int NTE>
-__global__ __launch_bounds__(256 * KG) void k_route(RouteGemmParams p) {
-  constexpr int kTok = 16 * NTT;
-  constexpr int kPitch = kMaxExpertTiles * 16 + 1;
-  __shared__ float lg[KG][kTok][kPitch];
+// ---- many tokens: one workgroup per (64-token tile, K split) holds every
+// expert.  Each 64-K stage of the tile's token rows and of all expert rows
+// (128 bytes per row) is loaded as whole rows -- eight lanes per row, eight
+// rows per wave and instruction -- into registers two stages ahead, then
+// stored to one of two LDS buffers, 16-byte chunk c of row r at chunk
+// position c ^ (r & 7), so the fragment reads of sixteen rows at one chunk
+// spread over every bank.  Wave w multiplies expert tiles w, w + 4, w + 8,
+// w + 12 by the four token tiles (gate rows on the MFMA's 16-row side,
+// tokens on its 16-column side), and the split's fp32 partial logits go to
+// the workspace ([split][token][expert]), where k_route_select sums them in
+// split order and selects.
+constexpr int kTileTok = 64;                                // tokens per workgroup
+constexpr int kTileRows = kTileTok + kMaxExpertTiles * 16;  // LDS rows per stage (tokens, then experts)
+
+struct RouteTileParams {
+  const uint16_t* x;   // bf16 [T][H]
+  const uint16_t* wg;  // bf16 [E][H]
+  float* part;         // [S][T_pad][E]
+  int T, H, E, steps;  // steps: 64-K stages per split
+  int T_pad;           // tokens rounded up to the tile
+  int splits;          // S
+};
+
+// NTE expert tiles per wave: the workgroup stages 64 token rows and 64 NTE
+// expert rows, NP = 2 + 2 NTE 16-byte loads per thread and stage.  Every load,
+// LDS store and MFMA is unconditional (rows past T or E repeat the last valid
+// row, and their products are never stored), so the compiler counts the
+// loads in flight exactly and waits only for the stage it stores.
+template <int NTE>
+__global__ __launch_bounds__(kRouteThreads, 1) void k_route_tile(RouteTileParams p) {
+  constexpr int NP = 2 + 2 * NTE;
+  __shared__ v4u lds[2][kTileRows * 8];  // two stages, up to 40 KB each
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
-  const int slot = w & 3, kg = w >> 2;
-  const int tok0 = blockIdx.x * kTok;
-  const int H = p.H, E = p.E;
-  const int ET = (E + 15) / 16;
-  // this wave's expert tiles: slot, slot + 4, slot + 8, slot + 12 (those below
-  // ET, at most NTE of them)
-  int nte = 0;
-  const uint16_t* arow[NTE];
+  // work items w = tile + ntiles * split, split-major; workgroup L runs on
+  // XCD L % 8 (the dispatcher deals workgroups to the eight XCDs in turn),
+  // so with n a multiple of 8 XCD x takes the contiguous items [x n / 8,
+  // (x + 1) n / 8): mostly one K split per XCD, whose gate slice then stays
+  // in that XCD's L2
+  const int ntiles = p.T_pad / kTileTok, n = ntiles * p.splits, L = blockIdx.x;
+  const int wi = n % 8 == 0 ? (L % 8) * (n / 8) + L / 8 : L;
+  const int tok0 = (wi % ntiles) * kTileTok, split = wi / ntiles;
+  const int H = p.H, E = p.E, ET = (E + 15) / 16;
+  // piece q of this thread is row (tid + 256 q) / 8, 16-byte chunk (tid + 256 q) % 8
+  const uint16_t* src[NP];
+  int dst[NP];
 #pragma unroll
-  for (int j = 0; j < NTE; ++j) {
-    const int tile = slot + 4 * j;
-    if (tile < ET) nte = j + 1;
-    const int e = min(16 * min(tile, ET - 1) + m, E - 1);
-    arow[j] = p.wg + long(e) * H + 16 * g;
+  for (int q = 0; q < NP; ++q) {
+    const int pc = tid + kRouteThreads * q, r = pc >> 3, c = pc & 7;
+    src[q] = r < kTileTok ? p.x + long(min(tok0 + r, p.T - 1)) * H + 8 * c
+                          : p.wg + long(min(r - kTileTok, E - 1)) * H + 8 * c;
+    dst[q] = r * 8 + (c ^ (r & 7));
   }
-  const uint16_t* brow[NTT];
+  const long k_base = long(split) * p.steps * kStageK;
+  auto gload = [&](v4u (&rg)[NP], int s) __attribute__((always_inline)) {
+    const long k0 = k_base + long(s) * kStageK;
 #pragma unroll
-  for (int t = 0; t < NTT; ++t) brow[t] = p.x + long(min(tok0 + 16 * t + m, p.T - 1)) * H + 16 * g;
-
-  v4f acc[NTE][NTT];
+    for (int q = 0; q < NP; ++q) rg[q] = *reinterpret_cast<const v4u*>(src[q] + k0);
+  };
+  auto swrite = [&](int b, const v4u (&rg)[NP]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NP; ++q) lds[b][dst[q]] = rg[q];
+  };
+  v4f acc[NTE][4];
 #pragma unroll
   for (int j = 0; j < NTE; ++j)
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  auto load = [&](Stage<NTE, NTT>& s, int k0) __attribute__((always_inline)) {
+    for (int t = 0; t < 4; ++t) acc[j][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  // one stage from LDS buffer b: two 32-K MFMA steps; lane group g holds
+  // K [32 h + 8 g, 32 h + 8 g + 8) of step h in chunk 4 h + g, for both
+  // operands (rows 16 t + m and 64 + 16 tile + m both have r & 7 = m & 7)
+  auto compute = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < NTE; ++j)
-      if (j < nte) {
-        s.a[j][0] = *reinterpret_cast<const v4u*>(arow[j] + k0);
-        s.a[j][1] = *reinterpret_cast<const v4u*>(arow[j] + k0 + 8);
-      }
+    for (int h = 0; h < 2; ++h) {
+      const int cpos = (4 * h + g) ^ (m & 7);
+      v4u bt[4];
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) {
-      s.b[t][0] = *reinterpret_cast<const v4u*>(brow[t] + k0);
-      s.b[t][1] = *reinterpret_cast<const v4u*>(brow[t] + k0 + 8);
-    }
-  };
-  auto mma = [&](const Stage<NTE, NTT>& s) __attribute__((always_inline)) {
+      for (int t = 0; t < 4; ++t) bt[t] = lds[b][(16 * t + m) * 8 + cpos];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int j = 0; j < NTE; ++j) {
+        const v4u a = lds[b][(kTileTok + 16 * (w + 4 * j) + m) * 8 + cpos];
 #pragma unroll
-      for (int j = 0; j < NTE; ++j)
-        if (j < nte)
-#pragma unroll
-          for (int t = 0; t < NTT; ++t)
-            acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(s.a[j][h]), as_bf(s.b[t][h]), acc[j][t], 0, 0, 0);
-  };
-  // this group's stages [s0, s1) of the H / 64; RS register stages: the
-  // loads of stages i + 1 .. i + RS - 1 are in flight while stage i multiplies
-  const int nst = H / kStageK;
-  const int s0 = kg * nst / KG, s1 = (kg + 1) * nst / KG, ns = s1 - s0;
-  Stage<NTE, NTT> st[RS];
-#pragma unroll
-  for (int r = 0; r < RS - 1; ++r)
-    if (r < ns) load(st[r], (s0 + r) * kStageK);
-  for (int i = 0; i < ns; i += RS) {
-#pragma unroll
-    for (int r = 0; r < RS; ++r) {
-      if (i + r < ns) {
-        if (i + r + RS - 1 < ns) load(st[(r + RS - 1) % RS], (s0 + i + r + RS - 1) * kStageK);
-        mma(st[r]);
+        for (int t = 0; t < 4; ++t)
+          acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a), as_bf(bt[t]), acc[j][t], 0, 0, 0);
       }
     }
-  }
-  // partial logits to LDS: lane l holds token 16 t + m, experts 16 tile + 4 g + (0..3)
-#pragma unroll
-  for (int j = 0; j < NTE; ++j)
-    if (j < nte)
-#pragma unroll
-      for (int t = 0; t < NTT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lg[kg][16 * t + m][16 * (slot + 4 * j) + 4 * g + i] = acc[j][t][i];
+  };
+  // stage s sits in LDS buffer s % 2 while the registers hold stages s + 1
+  // and s + 2; one barrier per stage.  Past the last stage the loads repeat
+  // it (cache hits, never multiplied), so every iteration issues and stores
+  // the same loads and waits only for the older register stage.
+  const int ns = p.steps;
+  v4u r0[NP], r1[NP];
+  gload(r0, 0);
+  gload(r1, min(1, ns - 1));
+  swrite(0, r0);
   __syncthreads();
-  if (KG > 1) {
-    // the K groups' partial sums, in group order, into group 0's rows
-    for (int idx = tid; idx < kTok * E; idx += 256 * KG) {
-      const int tl = idx / E, e = idx - tl * E;
-      float v = lg[0][tl][e];
-#pragma unroll
-      for (int q = 1; q < KG; ++q) v += lg[q][tl][e];
-      lg[0][tl][e] = v;
-    }
+  for (int s = 0; s < ns; s += 2) {
+    gload(r0, min(s + 2, ns - 1));
+    compute(0);
+    swrite(1, r1);
+    __syncthreads();
+    gload(r1, min(s + 3, ns - 1));
+    if (s + 1 < ns) compute(1);
+    swrite(0, r0);
     __syncthreads();
   }
-
-  // top-k per token: lane l holds experts l, l + 64, l + 128, l + 192
-  for (int tl = w; tl < kTok; tl += 4 * KG) {
-    const int t = tok0 + tl;
-    if (t >= p.T) break;
-    float v[4];
+  // lane l holds token 16 t + m, experts 16 tile + 4 g + (0..3)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      v[q] = e < E ? lg[0][tl][e] : 0.0f;
+  for (int j = 0; j < NTE; ++j) {
+    const int tile = w + 4 * j;
+    if (tile >= ET) continue;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tok = tok0 + 16 * t + m;
+      if (tok >= p.T) continue;
+      float* dstp = p.part + (long(split) * p.T_pad + tok) * E + 16 * tile + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (16 * tile + 4 * g + i < E) dstp[i] = acc[j][t][i];
     }
-    select_topk(v, E, p.k, lane, p.ids + long(t) * p.k, p.weights + long(t) * p.k);
   }
 }
 
@@ -302,52 +312,99 @@ __global__ __launch_bounds__(256) void k_route_select(RouteSelParams p) {
   select_topk(v, p.E, p.k, lane, p.ids + long(t) * p.k, p.weights + long(t) * p.k);
 }
 
+// Many tokens: one wave per token, four tokens per workgroup.  Lane l sums
+// its experts l, l + 64, l + 128, l + 192 over the splits in split order;
+// every load is issued (up to NC splits; past the split count or E they
+// re-read a valid entry and are not added), so a wave has its loads in
+// flight at once.
+constexpr int kSelMaxSplits = 32;
+
+template <int NC>
+__global__ __launch_bounds__(256) void k_route_select_wave(RouteSelParams p) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + w;
+  if (t >= p.T) return;
+  const int nkc = p.nkc, E = p.E;
+  const long pitch = long(p.T_pad) * E;
+  const float* row = p.part + long(t) * E;
+  float x[NC][4];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const float* r = row + min(c, nkc - 1) * pitch;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[c][q] = r[min(lane + 64 * q, E - 1)];
+  }
+  float v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float s = x[0][q];
+#pragma unroll
+    for (int c = 1; c < NC; ++c) s = c < nkc ? s + x[c][q] : s;
+    v[q] = lane + 64 * q < E ? s : 0.0f;
+  }
+  select_topk(v, E, p.k, lane, p.ids + long(t) * p.k, p.weights + long(t) * p.k);
+}
+
 }  // namespace
 
 // K chunks of the few-token path: the largest divisor of the H / 64 stages
 // that keeps the launch within kRouteWaves waves (about two per CU)
 constexpr int kRouteSmallMaxT = 512;
 constexpr long kRouteWaves = 512;
+// K splits of the many-token path: the largest divisor of the H / 64 stages
+// that keeps the launch within kRouteTileWGs workgroups (one per CU)
+constexpr long kRouteTileWGs = 256;
 
-static int route_chunks(int T, int H, int E) {
-  const long units = long((T + 15) / 16) * ((E + 15) / 16);
-  const int stages = H / kStageK;
+static int largest_split(long units, int stages, long cap) {
   int best = 1;
   for (int d = 1; d <= stages; ++d)
-    if (stages % d == 0 && units * d <= kRouteWaves) best = d;
+    if (stages % d == 0 && units * d <= cap) best = d;
   return best;
 }
 
+static int route_chunks(int T, int H, int E) {
+  if (T <= kRouteSmallMaxT) return largest_split(long((T + 15) / 16) * ((E + 15) / 16), H / kStageK, kRouteWaves);
+  const long ntiles = (T + kTileTok - 1) / kTileTok;
+  return largest_split(ntiles, H / kStageK, std::min(kRouteTileWGs, ntiles * kSelMaxSplits));
+}
+
+static long route_t_pad(int T) {
+  const int tile = T <= kRouteSmallMaxT ? 16 : kTileTok;
+  return long(T + tile - 1) / tile * tile;
+}
+
 size_t route_workspace_bytes(int T, int H, int E) {
-  if (T == 0 || T > kRouteSmallMaxT) return 0;
-  const long T_pad = (T + 15) / 16 * 16;
-  return size_t(route_chunks(T, H, E)) * T_pad * E * 4;
+  if (T == 0) return 0;
+  return size_t(route_chunks(T, H, E)) * route_t_pad(T) * E * 4;
 }
 
 hipError_t launch_route_gemm(int T, int H, int E, int k, const uint16_t* x, const uint16_t* wg, int32_t* ids,
                              float* weights, float* part, hipStream_t st) {
   if (T == 0) return hipSuccess;
+  const int nkc = route_chunks(T, H, E);
+  const int T_pad = int(route_t_pad(T));
+  const int steps = H / kStageK / nkc;
   if (T <= kRouteSmallMaxT) {
-    const int nkc = route_chunks(T, H, E);
-    const int T_pad = (T + 15) / 16 * 16;
-    RoutePartParams pp{x, wg, part, T, H, E, H / kStageK / nkc, T_pad};
+    RoutePartParams pp{x, wg, part, T, H, E, steps, T_pad};
     hipLaunchKernelGGL(k_route_part, dim3(unsigned(T_pad / 16), unsigned((E + 15) / 16), unsigned(nkc)), dim3(64), 0,
                        st, pp);
-    RouteSelParams sp{part, ids, weights, T, E, k, nkc, T_pad};
-    hipLaunchKernelGGL(k_route_select, dim3(unsigned(T)), dim3(256), 0, st, sp);
-    return hipGetLastError();
-  }
-  RouteGemmParams p{x, wg, ids, weights, T, H, E, k};
-  // two token tiles per workgroup once there are enough tokens to fill the
-  // CUs with them (half the gate-row reads per token); below that 16 waves
-  // per 16-token tile, split four ways along K, with six register stages
-  // when each wave holds one expert tile (E <= 64) and two otherwise
-  if (T >= 4096) {
-    hipLaunchKernelGGL((k_route<2, 1, 2, 4>), dim3(unsigned((T + 31) / 32)), dim3(kRouteThreads), 0, st, p);
-  } else if (E <= 64) {
-    hipLaunchKernelGGL((k_route<1, 4, 6, 1>), dim3(unsigned((T + 15) / 16)), dim3(4 * kRouteThreads), 0, st, p);
   } else {
-    hipLaunchKernelGGL((k_route<1, 4, 2, 4>), dim3(unsigned((T + 15) / 16)), dim3(4 * kRouteThreads), 0, st, p);
+    RouteTileParams tp{x, wg, part, T, H, E, steps, T_pad, nkc};
+    const dim3 grid(unsigned(T_pad / kTileTok * nkc));
+    const int nte = ((E + 15) / 16 + 3) / 4;  // expert tiles per wave
+    if (nte == 1) hipLaunchKernelGGL(k_route_tile<1>, grid, dim3(kRouteThreads), 0, st, tp);
+    else if (nte == 2) hipLaunchKernelGGL(k_route_tile<2>, grid, dim3(kRouteThreads), 0, st, tp);
+    else if (nte == 3) hipLaunchKernelGGL(k_route_tile<3>, grid, dim3(kRouteThreads), 0, st, tp);
+    else hipLaunchKernelGGL(k_route_tile<4>, grid, dim3(kRouteThreads), 0, st, tp);
+  }
+  RouteSelParams sp{part, ids, weights, T, E, k, nkc, T_pad};
+  if (T <= kRouteSmallMaxT) hipLaunchKernelGGL(k_route_select, dim3(unsigned(T)), dim3(256), 0, st, sp);
+  else {
+    const dim3 grid(unsigned((T + 3) / 4));
+    if (nkc <= 4) hipLaunchKernelGGL(k_route_select_wave<4>, grid, dim3(256), 0, st, sp);
+    else if (nkc <= 8) hipLaunchKernelGGL(k_route_select_wave<8>, grid, dim3(256), 0, st, sp);
+    else if (nkc <= 16) hipLaunchKernelGGL(k_route_select_wave<16>, grid, dim3(256), 0, st, sp);
+    else hipLaunchKernelGGL(k_route_select_wave<kSelMaxSplits>, grid, dim3(256), 0, st, sp);
   }
   return hipGetLastError();
 }

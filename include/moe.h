@@ -243,9 +243,10 @@ int moe_layer_persistent(const moe_cfg* cfg, const uint16_t* x, const int32_t* t
  * ends) without a slow run.  MOE_ERR_BAD_SHAPE for polls < 0. */
 int moe_layer_persistent_spin_limit(int polls);
 
-/* The router in front of the layer, one kernel (the routing GEMM and the
- * routing selection fused, as the DeepGEMM 26/09 news page describes its
- * Mega Gate): for every token t,
+/* The router in front of the layer: the routing GEMM and the routing
+ * selection, which the DeepGEMM 26/09 news page fuses into one kernel for its
+ * Mega Gate (here two launches, the GEMM's fp32 partial logits meeting in
+ * ws): for every token t,
  *   logit[e] = sum_h x[t][h] * gate_w[e][h]    (bf16 products, fp32 sums)
  *   topk_ids[t][0..topk) = the topk experts with the largest logits, in
  *     descending order, equal logits going to the lower expert id
@@ -259,10 +260,11 @@ int moe_layer_persistent_spin_limit(int polls);
  * experts whose exact logits differ by less than that rounding may come
  * out in either order.
  *   ws: device scratch of at least moe_route_workspace_size(cfg) bytes
- *   (contents on entry ignored; may be NULL when that size is 0).  Up to 512
- *   tokens the gate rows are spread over many workgroups whose partial
- *   logits meet in ws, as the layer's workspace is sized on the host
- *   (FusedDeepMoE W4A8 workspace computation); above, ws is not used.
+ *   (contents on entry ignored; may be NULL when that size is 0, i.e. T = 0).
+ *   The gate GEMM is split along K over enough workgroups to fill the GPU;
+ *   the splits' fp32 partial logits meet in ws, sized on the host as the
+ *   layer's workspace is (FusedDeepMoE W4A8 workspace computation):
+ *   splits x T (rounded up to 16, or to 64 above 512 tokens) x E x 4 bytes.
  * Errors as for every entry point (MOE_ERR_WORKSPACE: ws_bytes too small). */
 int moe_route_workspace_size(const moe_cfg* cfg, size_t* bytes);
 int moe_route(const moe_cfg* cfg, const uint16_t* x, const uint16_t* gate_w, int32_t* topk_ids, float* topk_weights,

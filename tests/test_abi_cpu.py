@@ -279,11 +279,17 @@ def test_route_argument_errors(lib):
 def test_route_workspace(lib):
     n = C.c_size_t(0)
     size = lambda c: (moe.raw_call("moe_route_workspace_size", C.byref(c.c()), C.byref(n)), n.value)
-    # few tokens need scratch for the partial logits, many none
+    # every T > 0 needs scratch for the K splits' partial logits: splits x T
+    # (rounded up to 16, or 64 above 512 tokens) x E fp32 values, the splits
+    # dividing H / 64
     rc, a = size(cfg(T=1, H=4096, E=64, topk=8))
-    assert rc == moe.MOE_OK and a > 0 and a % 4 == 0
-    assert size(cfg(T=512, H=4096, E=64, topk=8))[1] > 0
-    assert size(cfg(T=513, H=4096, E=64, topk=8)) == (moe.MOE_OK, 0)
+    assert rc == moe.MOE_OK and a > 0 and a % (16 * 64 * 4) == 0 and (4096 // 64) % (a // (16 * 64 * 4)) == 0
+    b = size(cfg(T=512, H=4096, E=64, topk=8))[1]
+    assert b > 0 and b % (512 * 64 * 4) == 0
+    c = size(cfg(T=513, H=4096, E=64, topk=8))[1]
+    assert c > 0 and c % (576 * 64 * 4) == 0 and (4096 // 64) % (c // (576 * 64 * 4)) == 0
+    d = size(cfg(T=4096, H=7168, E=256, topk=8))[1]
+    assert d % (4096 * 256 * 4) == 0 and (7168 // 64) % (d // (4096 * 256 * 4)) == 0
     assert size(cfg(T=0)) == (moe.MOE_OK, 0)
     assert size(cfg(E=300, topk=8))[0] == moe.MOE_ERR_UNSUPPORTED
     assert size(cfg(topk=0))[0] == moe.MOE_ERR_BAD_SHAPE
