@@ -48,16 +48,40 @@ struct Stage {
 
 __device__ __forceinline__ v8bf as_bf(const v4u& u) { return __builtin_bit_cast(v8bf, u); }
 
-// (value, expert id) order of the selection: larger logit first, the lower
-// id first among equal logits
-__device__ __forceinline__ bool beats(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+// Wave-wide reductions through DPP moves (register to register, no LDS
+// round trip): within each 16-lane row by the quad permutations (lane xor 1,
+// xor 2), the half-row mirror (lane i and 7 - i) and the row mirror (i and
+// 15 - i), then the four rows' results read out of lanes 0, 16, 32, 48 and
+// combined in row order.  The result is the same in every lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f32(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
 
 // The selection of one token by one wave: lane l holds the logits of experts
-// l, l + 64, l + 128, l + 192 (entries past E ignored); k rounds of a
-// wave-wide argmax over (logit, -id), lane j keeping the j-th pick, then the
-// softmax of the k picks.  Writes ids[0..k) and weights[0..k).
+// l, l + 64, l + 128, l + 192 (entries past E ignored).  Each of k rounds
+// takes the largest remaining logit (a wave-wide max) and, among the entries
+// equal to it, the lowest expert id: ids run q-major (64 q + lane), so that is
+// the lowest set lane of the first non-empty ballot in q order.  Lane j keeps
+// the j-th pick; then the softmax of the k picks.  Writes ids[0..k) and
+// weights[0..k).
 __device__ __forceinline__ void select_topk(const float (&v)[4], int E, int k, int lane, int32_t* ids,
                                             float* weights) {
   int taken = 0;
@@ -67,25 +91,26 @@ __device__ __forceinline__ void select_topk(const float (&v)[4], int E, int k, i
   float my_v = 0.0f;  // lane j keeps the j-th selected logit
   int my_i = 0;
   for (int r = 0; r < k; ++r) {
-    float bv = -FLT_MAX;
-    int bi = 0x7FFFFFFF;
+    float lm = -INFINITY;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      if (!(taken & (1 << q)) && beats(v[q], lane + 64 * q, bv, bi)) { bv = v[q]; bi = lane + 64 * q; }
+      if (!(taken & (1 << q))) lm = fmaxf(lm, v[q]);
+    const float top = wave_max_f32(lm);
+    int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    for (int q = 0; q < 4; ++q) {
+      const uint64_t b = __ballot(!(taken & (1 << q)) && v[q] == top);
+      if (b) {
+        bi = 64 * q + __ffsll((unsigned long long)b) - 1;
+        break;
+      }
     }
     if (bi != 0x7FFFFFFF && (bi & 63) == lane) taken |= 1 << (bi >> 6);
-    if (lane == r) { my_v = bv; my_i = bi; }
+    if (lane == r) { my_v = top; my_i = bi; }
   }
-  const float top = __shfl(my_v, 0, 64);
+  const float top = lane_f32(my_v, 0);
   const float ex = lane < k ? expf(my_v - top) : 0.0f;
-  float sum = ex;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) sum += __shfl_xor(sum, o, 64);
+  const float sum = wave_sum_f32(ex);
   if (lane < k) {
     ids[lane] = my_i;
     weights[lane] = ex / sum;
@@ -95,16 +120,18 @@ __device__ __forceinline__ void select_topk(const float (&v)[4], int E, int k, i
 // ---- many tokens: one workgroup per (64-token tile, K split) holds every
 // expert.  Each 64-K stage of the tile's token rows and of all expert rows
 // (128 bytes per row) is loaded as whole rows -- eight lanes per row, eight
-// rows per wave and instruction -- into registers two stages ahead, then
+// rows per wave and instruction -- into a ring of register stages, then
 // stored to one of two LDS buffers, 16-byte chunk c of row r at chunk
-// position c ^ (r & 7), so the fragment reads of sixteen rows at one chunk
-// spread over every bank.  Wave w multiplies expert tiles w, w + 4, w + 8,
+// position c ^ (r & 7), so the fragment reads of eight consecutive rows at
+// one chunk fall on eight different chunk positions (the layout the
+// many-row GEMMs use for their token rows).  Wave w multiplies expert tiles w, w + 4, w + 8,
 // w + 12 by the four token tiles (gate rows on the MFMA's 16-row side,
 // tokens on its 16-column side), and the split's fp32 partial logits go to
 // the workspace ([split][token][expert]), where k_route_select sums them in
 // split order and selects.
 constexpr int kTileTok = 64;                                // tokens per workgroup
 constexpr int kTileRows = kTileTok + kMaxExpertTiles * 16;  // LDS rows per stage (tokens, then experts)
+constexpr int kTileRegStages = 4;                           // register stages of loads in flight
 
 struct RouteTileParams {
   const uint16_t* x;   // bf16 [T][H]
@@ -145,10 +172,14 @@ __global__ __launch_bounds__(kRouteThreads, 1) void k_route_tile(RouteTileParams
     dst[q] = r * 8 + (c ^ (r & 7));
   }
   const long k_base = long(split) * p.steps * kStageK;
+  // token rows are read once (non-temporal, so they do not push the gate
+  // slice out of L2); gate rows are re-read by every token tile of the split
   auto gload = [&](v4u (&rg)[NP], int s) __attribute__((always_inline)) {
     const long k0 = k_base + long(s) * kStageK;
 #pragma unroll
-    for (int q = 0; q < NP; ++q) rg[q] = *reinterpret_cast<const v4u*>(src[q] + k0);
+    for (int q = 0; q < NP; ++q)
+      rg[q] = q < 2 ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(src[q] + k0))
+                    : *reinterpret_cast<const v4u*>(src[q] + k0);
   };
   auto swrite = [&](int b, const v4u (&rg)[NP]) __attribute__((always_inline)) {
 #pragma unroll
@@ -178,25 +209,28 @@ __global__ __launch_bounds__(kRouteThreads, 1) void k_route_tile(RouteTileParams
       }
     }
   };
-  // stage s sits in LDS buffer s % 2 while the registers hold stages s + 1
-  // and s + 2; one barrier per stage.  Past the last stage the loads repeat
-  // it (cache hits, never multiplied), so every iteration issues and stores
-  // the same loads and waits only for the older register stage.
+  // stage s sits in LDS buffer s % 2 while a ring of R register stages
+  // holds stages s + 1 .. s + R (R - 1 stages of loads in flight while a
+  // stage multiplies); one barrier per stage.  Past the last stage the loads
+  // repeat it (cache hits, never multiplied), so every step issues and
+  // stores the same loads and waits only for the oldest register stage.
+  constexpr int R = kTileRegStages;
   const int ns = p.steps;
-  v4u r0[NP], r1[NP];
-  gload(r0, 0);
-  gload(r1, min(1, ns - 1));
-  swrite(0, r0);
+  v4u rg[R][NP];
+#pragma unroll
+  for (int i = 0; i < R; ++i) gload(rg[i], min(i, ns - 1));
+  swrite(0, rg[0]);
   __syncthreads();
-  for (int s = 0; s < ns; s += 2) {
-    gload(r0, min(s + 2, ns - 1));
-    compute(0);
-    swrite(1, r1);
-    __syncthreads();
-    gload(r1, min(s + 3, ns - 1));
-    if (s + 1 < ns) compute(1);
-    swrite(0, r0);
-    __syncthreads();
+  gload(rg[0], min(R, ns - 1));
+  for (int s = 0; s < ns; s += R) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      // stage s + i: in buffer i % 2; rg[(i + 1) % R] holds stage s + i + 1
+      if (s + i < ns) compute(i % 2);
+      swrite((i + 1) % 2, rg[(i + 1) % R]);
+      __syncthreads();
+      gload(rg[(i + 1) % R], min(s + i + 1 + R, ns - 1));
+    }
   }
   // lane l holds token 16 t + m, experts 16 tile + 4 g + (0..3)
 #pragma unroll
@@ -273,9 +307,10 @@ struct RouteSelParams {
   int T, E, k, nkc, T_pad;
 };
 
+template <int NB>
 __global__ __launch_bounds__(256) void k_route_select(RouteSelParams p) {
   // one workgroup per token: wave w sums the chunks [w nkc / 4, (w + 1) nkc / 4)
-  // in sixteen independent partial sums (sixteen loads in flight per lane: the
+  // in NB independent partial sums (NB loads in flight per lane: the
   // partials were written by other XCDs, so each round trip goes past L2),
   // folded pairwise in a fixed order;
   // the four waves' sums meet in LDS in wave order, wave 0 selects
@@ -285,21 +320,24 @@ __global__ __launch_bounds__(256) void k_route_select(RouteSelParams p) {
   const int c0 = w * p.nkc / 4, c1 = (w + 1) * p.nkc / 4;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    if (e >= p.E) continue;
-    float sp[16];
+    const int e = min(lane + 64 * q, p.E - 1);
+    float sp[NB];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) sp[u] = 0.0f;
-    for (int c = c0; c < c1; c += 16) {
+    for (int u = 0; u < NB; ++u) sp[u] = 0.0f;
+    // every load of a round of NB is issued (past c1 they re-read the last
+    // chunk and are not added)
+    for (int c = c0; c < c1; c += NB) {
+      float x[NB];
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (c + u < c1) sp[u] += p.part[(long(c + u) * p.T_pad + t) * p.E + e];
+      for (int u = 0; u < NB; ++u) x[u] = p.part[(long(min(c + u, c1 - 1)) * p.T_pad + t) * p.E + e];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) sp[u] = c + u < c1 ? sp[u] + x[u] : sp[u];
     }
 #pragma unroll
-    for (int h = 8; h >= 1; h >>= 1)
+    for (int h = NB / 2; h >= 1; h >>= 1)
 #pragma unroll
       for (int u = 0; u < h; ++u) sp[u] += sp[u + h];
-    red[w][e] = sp[0];
+    if (lane + 64 * q < p.E) red[w][lane + 64 * q] = sp[0];
   }
   __syncthreads();
   if (w != 0) return;
@@ -398,7 +436,11 @@ hipError_t launch_route_gemm(int T, int H, int E, int k, const uint16_t* x, cons
     else hipLaunchKernelGGL(k_route_tile<4>, grid, dim3(kRouteThreads), 0, st, tp);
   }
   RouteSelParams sp{part, ids, weights, T, E, k, nkc, T_pad};
-  if (T <= kRouteSmallMaxT) hipLaunchKernelGGL(k_route_select, dim3(unsigned(T)), dim3(256), 0, st, sp);
+  if (T <= kRouteSmallMaxT) {
+    // NB partial sums per lane: 4 when no wave has more than 4 chunks
+    if ((nkc + 3) / 4 <= 4) hipLaunchKernelGGL(k_route_select<4>, dim3(unsigned(T)), dim3(256), 0, st, sp);
+    else hipLaunchKernelGGL(k_route_select<16>, dim3(unsigned(T)), dim3(256), 0, st, sp);
+  }
   else {
     const dim3 grid(unsigned((T + 3) / 4));
     if (nkc <= 4) hipLaunchKernelGGL(k_route_select_wave<4>, grid, dim3(256), 0, st, sp);
