@@ -101,6 +101,27 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, kWave));
 }
 
+// Another lane's value within the lane's 16-lane row by a DPP move (CTRL:
+// the DPP control word), register to register.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Max over each aligned group of `lanes` consecutive lanes (4 or 16), in
+// every lane of the group: the quad permutations (lane xor 1, xor 2), then
+// for 16 lanes the half-row mirror (lanes i, 7 - i) and the row mirror
+// (i, 15 - i).  Every lane of the wave must be active.
+__device__ __forceinline__ float group_max_dpp(float v, int lanes) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));  // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));  // quad_perm [2, 3, 0, 1]
+  if (lanes > 4) {
+    v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+    v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+  }
+  return v;
+}
+
 // ------------------------------------------------------------------ MFMA
 // v_mfma_scale_f32_16x16x128_f8f6f4, layout measured on gfx950:
 //   operand lane l: row (A) / column (B) = l % 16, lane group g = l / 16.

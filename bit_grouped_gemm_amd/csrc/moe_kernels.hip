@@ -218,8 +218,8 @@ __device__ void quant_block(const RouteParams& p, int blk) {
     }
     for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(f[q]));
   }
-  const int lanes = p.G / 8;  // 4 or 16, a power of two dividing 64
-  for (int msk = 1; msk < lanes; msk <<= 1) amax = wave_max_xor(amax, msk);
+  const int lanes = p.G / 8;  // 4 or 16: the group's lanes, one aligned run
+  amax = group_max_dpp(amax, lanes);
   if (p.af == 1) {
     // MXFP4: one e8m0 scale per 32 channels (4 lanes), 8 e2m1 codes per thread
     if (item < items) {

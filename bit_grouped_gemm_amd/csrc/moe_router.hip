@@ -53,10 +53,6 @@ __device__ __forceinline__ v8bf as_bf(const v4u& u) { return __builtin_bit_cast(
 // xor 2), the half-row mirror (lane i and 7 - i) and the row mirror (i and
 // 15 - i), then the four rows' results read out of lanes 0, 16, 32, 48 and
 // combined in row order.  The result is the same in every lane.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
 __device__ __forceinline__ float lane_f32(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
