@@ -95,10 +95,18 @@ __device__ void permute_chunk(const RouteParams& p, int b, int nb, int c0, int c
       if (nb == 1) {
         tot[q] = cnt[0][e] + cnt[1][e] + cnt[2][e] + cnt[3][e];
       } else {
-        for (int bb = 0; bb < nb; ++bb) {
-          const int c = p.chunk_cnt[bb * E + e];
-          tot[q] += c;
-          if (bb < b) pre[q] += c;
+        // sixteen chunks' counts loaded at a time (past nb they re-read the
+        // last chunk's and are not added), so their round trips overlap
+        for (int bb0 = 0; bb0 < nb; bb0 += 16) {
+          int cv[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) cv[u] = p.chunk_cnt[min(bb0 + u, nb - 1) * E + e];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const int bb = bb0 + u;
+            tot[q] += bb < nb ? cv[u] : 0;
+            pre[q] += bb < b ? cv[u] : 0;
+          }
         }
       }
     }
