@@ -120,11 +120,12 @@ __device__ __forceinline__ void select_topk(const float (&v)[4], int E, int k, i
 // stored to one of two LDS buffers, 16-byte chunk c of row r at chunk
 // position c ^ (r & 7), so the fragment reads of eight consecutive rows at
 // one chunk fall on eight different chunk positions (the layout the
-// many-row GEMMs use for their token rows).  Wave w multiplies expert tiles w, w + 4, w + 8,
-// w + 12 by the four token tiles (gate rows on the MFMA's 16-row side,
-// tokens on its 16-column side), and the split's fp32 partial logits go to
-// the workspace ([split][token][expert]), where k_route_select sums them in
-// split order and selects.
+// many-row GEMMs use for their token rows).  Of NW waves (4, or 8 from
+// eight expert tiles on), wave w multiplies expert tiles w, w + NW, ... by
+// the four token tiles (gate rows on the MFMA's 16-row side, tokens on its
+// 16-column side), and the split's fp32 partial logits go to the workspace
+// ([split][token][expert]), where k_route_select_wave sums them in split
+// order and selects.
 constexpr int kTileTok = 64;                                // tokens per workgroup
 constexpr int kTileRows = kTileTok + kMaxExpertTiles * 16;  // LDS rows per stage (tokens, then experts)
 constexpr int kTileRegStages = 4;                           // register stages of loads in flight
@@ -143,9 +144,11 @@ struct RouteTileParams {
 // LDS store and MFMA is unconditional (rows past T or E repeat the last valid
 // row, and their products are never stored), so the compiler counts the
 // loads in flight exactly and waits only for the stage it stores.
-template <int NTE>
-__global__ __launch_bounds__(kRouteThreads, 1) void k_route_tile(RouteTileParams p) {
-  constexpr int NP = 2 + 2 * NTE;
+template <int NTE, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_route_tile(RouteTileParams p) {
+  constexpr int kThr = 64 * NW;
+  constexpr int NP = (kTileTok + 16 * NW * NTE) * 8 / kThr;
+  static_assert((kTileTok + 16 * NW * NTE) * 8 % kThr == 0 && kTileTok * 8 % kThr == 0, "whole loads per thread");
   __shared__ v4u lds[2][kTileRows * 8];  // two stages, up to 40 KB each
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, g = lane >> 4;
   // work items w = tile + ntiles * split, split-major; workgroup L runs on
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(kRouteThreads, 1) void k_route_tile(RouteTileParams
   int dst[NP];
 #pragma unroll
   for (int q = 0; q < NP; ++q) {
-    const int pc = tid + kRouteThreads * q, r = pc >> 3, c = pc & 7;
+    const int pc = tid + kThr * q, r = pc >> 3, c = pc & 7;
     src[q] = r < kTileTok ? p.x + long(min(tok0 + r, p.T - 1)) * H + 8 * c
                           : p.wg + long(min(r - kTileTok, E - 1)) * H + 8 * c;
     dst[q] = r * 8 + (c ^ (r & 7));
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(kRouteThreads, 1) void k_route_tile(RouteTileParams
     const long k0 = k_base + long(s) * kStageK;
 #pragma unroll
     for (int q = 0; q < NP; ++q)
-      rg[q] = q < 2 ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(src[q] + k0))
+      rg[q] = q < kTileTok * 8 / kThr ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(src[q] + k0))
                     : *reinterpret_cast<const v4u*>(src[q] + k0);
   };
   auto swrite = [&](int b, const v4u (&rg)[NP]) __attribute__((always_inline)) {
@@ -198,7 +201,7 @@ __global__ __launch_bounds__(kRouteThreads, 1) void k_route_tile(RouteTileParams
       for (int t = 0; t < 4; ++t) bt[t] = lds[b][(16 * t + m) * 8 + cpos];
 #pragma unroll
       for (int j = 0; j < NTE; ++j) {
-        const v4u a = lds[b][(kTileTok + 16 * (w + 4 * j) + m) * 8 + cpos];
+        const v4u a = lds[b][(kTileTok + 16 * (w + NW * j) + m) * 8 + cpos];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(a), as_bf(bt[t]), acc[j][t], 0, 0, 0);
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(kRouteThreads, 1) void k_route_tile(RouteTileParams
   // lane l holds token 16 t + m, experts 16 tile + 4 g + (0..3)
 #pragma unroll
   for (int j = 0; j < NTE; ++j) {
-    const int tile = w + 4 * j;
+    const int tile = w + NW * j;
     if (tile >= ET) continue;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -425,11 +428,12 @@ hipError_t launch_route_gemm(int T, int H, int E, int k, const uint16_t* x, cons
   } else {
     RouteTileParams tp{x, wg, part, T, H, E, steps, T_pad, nkc};
     const dim3 grid(unsigned(T_pad / kTileTok * nkc));
-    const int nte = ((E + 15) / 16 + 3) / 4;  // expert tiles per wave
-    if (nte == 1) hipLaunchKernelGGL(k_route_tile<1>, grid, dim3(kRouteThreads), 0, st, tp);
-    else if (nte == 2) hipLaunchKernelGGL(k_route_tile<2>, grid, dim3(kRouteThreads), 0, st, tp);
-    else if (nte == 3) hipLaunchKernelGGL(k_route_tile<3>, grid, dim3(kRouteThreads), 0, st, tp);
-    else hipLaunchKernelGGL(k_route_tile<4>, grid, dim3(kRouteThreads), 0, st, tp);
+    // eight waves (two per SIMD, so one's LDS reads and barrier waits overlap
+    // the other's MFMAs) once there are eight expert tiles, else four
+    const int et = (E + 15) / 16;
+    if (et > 8) hipLaunchKernelGGL((k_route_tile<2, 8>), grid, dim3(512), 0, st, tp);
+    else if (et > 4) hipLaunchKernelGGL((k_route_tile<1, 8>), grid, dim3(512), 0, st, tp);
+    else hipLaunchKernelGGL((k_route_tile<1, 4>), grid, dim3(256), 0, st, tp);
   }
   RouteSelParams sp{part, ids, weights, T, E, k, nkc, T_pad};
   if (T <= kRouteSmallMaxT) {

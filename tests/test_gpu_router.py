@@ -112,15 +112,21 @@ def test_route_odd_shapes(H, E, k, T):
     check_router(x, wg, k, ids, w)
 
 
-def test_route_exact_ties_go_to_the_lower_id():
+@pytest.mark.parametrize("T,E,dup", [
+    (40, 64, [(2, 50), (9, 10), (30, 31), (31, 63)]),
+    # above 512 tokens (LDS-tiled GEMM, wave-per-token selection); with E = 256
+    # the tied experts sit in different 64-id groups of the selection's ballots
+    (700, 64, [(2, 50), (9, 10), (30, 31), (31, 63)]),
+    (600, 256, [(2, 200), (70, 71), (130, 255), (64, 192)]),
+])
+def test_route_exact_ties_go_to_the_lower_id(T, E, dup):
     """Duplicated gate rows give equal logits on both sides: the lower expert
     id must come first, bit-exact."""
     moe = M()
-    T, H, E, k = 40, 512, 64, 8
+    H, k = 512, 8
     g = torch.Generator(device=DEV).manual_seed(9)
     x = torch.randn(T, H, generator=g, device=DEV).to(torch.bfloat16)
     wg = (torch.randn(E, H, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
-    dup = [(2, 50), (9, 10), (30, 31), (31, 63)]
     for a, b in dup:
         wg[b] = wg[a]
     x[0] = 0.0                                    # every logit 0: ids 0..k-1, weights 1/k
