@@ -10,6 +10,9 @@
 //   moe_bench copy MIB
 //     three device-to-device copies of MIB MiB (the runtime's copy kernel):
 //     a transfer of known size, to scale a profiler's byte counters by
+//   moe_bench route WORKLOAD T REPS
+//     the router (moe_route) on the workload's H, E and top-k: bf16 tokens
+//     ~N(0,1) and gate rows ~N(0, 0.02), REPS timed calls after one untimed
 //   moe_bench WORKLOAD T REPS [stages]
 //     WORKLOAD  decode_fp8 | decode_mxfp4 | decode_fp8_zipf_shared | prefill_mxfp4 |
 //               prefill_mxfp4_a4
@@ -142,15 +145,62 @@ int main(int argc, char** argv) {
     return 0;
   }
   if (argc < 4) {
-    std::fprintf(stderr, "usage: %s WORKLOAD T REPS [stages] | %s copy MIB\n", argv[0], argv[0]);
+    std::fprintf(stderr, "usage: %s WORKLOAD T REPS [stages] | %s route WORKLOAD T REPS | %s copy MIB\n", argv[0],
+                 argv[0], argv[0]);
     return 2;
   }
+  const bool route = std::string(argv[1]) == "route";
+  if (route && argc < 5) return 2;
+  const char* wname = route ? argv[2] : argv[1];
   const Shape* sp = nullptr;
   for (const auto& s : kShapes)
-    if (std::string(argv[1]) == s.name) sp = &s;
+    if (std::string(wname) == s.name) sp = &s;
   if (!sp) {
-    std::fprintf(stderr, "unknown workload %s\n", argv[1]);
+    std::fprintf(stderr, "unknown workload %s\n", wname);
     return 2;
+  }
+  if (route) {
+    const Shape& s = *sp;
+    const int T = std::atoi(argv[3]), reps = std::atoi(argv[4]);
+    if (T < 1 || reps < 1) return 2;
+    moe_cfg cfg{T, s.H, s.I, s.E, s.k, s.wfmt, s.wblk, s.G, s.shared, s.af};
+    uint64_t st = 0x5EED0001ull;
+    std::vector<uint16_t> x(size_t(T) * s.H), g(size_t(s.E) * s.H);
+    for (auto& v : x) v = to_bf16(float(normal(st)));
+    for (auto& v : g) v = to_bf16(float(0.02 * normal(st)));
+    void* dx = upload(x.data(), x.size() * 2);
+    void* dg = upload(g.data(), g.size() * 2);
+    void* ids = nullptr;
+    void* tw = nullptr;
+    HIP_CHECK(hipMalloc(&ids, size_t(T) * s.k * 4));
+    HIP_CHECK(hipMalloc(&tw, size_t(T) * s.k * 4));
+    size_t nws = 0;
+    MOE_CHECK(moe_route_workspace_size(&cfg, &nws));
+    void* ws = nullptr;
+    HIP_CHECK(hipMalloc(&ws, std::max<size_t>(nws, 16)));
+    hipStream_t stream;
+    HIP_CHECK(hipStreamCreate(&stream));
+    auto call = [&] {
+      MOE_CHECK(moe_route(&cfg, static_cast<const uint16_t*>(dx), static_cast<const uint16_t*>(dg),
+                          static_cast<int32_t*>(ids), static_cast<float*>(tw), ws, nws, stream));
+    };
+    call();
+    HIP_CHECK(hipStreamSynchronize(stream));
+    hipEvent_t a, b;
+    HIP_CHECK(hipEventCreate(&a));
+    HIP_CHECK(hipEventCreate(&b));
+    std::vector<double> us;
+    for (int r = 0; r < reps; ++r) {
+      HIP_CHECK(hipEventRecord(a, stream));
+      call();
+      HIP_CHECK(hipEventRecord(b, stream));
+      HIP_CHECK(hipEventSynchronize(b));
+      float ms = 0.0f;
+      HIP_CHECK(hipEventElapsedTime(&ms, a, b));
+      us.push_back(ms * 1e3);
+    }
+    std::printf("route %s T=%d: %.2f us median of %d (warm)\ndone\n", s.name, T, median(us), reps);
+    return 0;
   }
   const Shape& s = *sp;
   const int T = std::atoi(argv[2]), reps = std::atoi(argv[3]);
