@@ -128,7 +128,7 @@ __device__ __forceinline__ void select_topk(const float (&v)[4], int E, int k, i
 // order and selects.
 constexpr int kTileTok = 64;                                // tokens per workgroup
 constexpr int kTileRows = kTileTok + kMaxExpertTiles * 16;  // LDS rows per stage (tokens, then experts)
-constexpr int kTileRegStages = 4;                           // register stages of loads in flight
+constexpr int kTileRegStages = 4;                           // register stages of loads in flight (even)
 
 struct RouteTileParams {
   const uint16_t* x;   // bf16 [T][H]
@@ -214,6 +214,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_route_tile(RouteTileParams p) {
   // repeat it (cache hits, never multiplied), so every step issues and
   // stores the same loads and waits only for the oldest register stage.
   constexpr int R = kTileRegStages;
+  static_assert(R % 2 == 0, "stage s + i sits in buffer i % 2 only when the ring's period is even");
   const int ns = p.steps;
   v4u rg[R][NP];
 #pragma unroll
