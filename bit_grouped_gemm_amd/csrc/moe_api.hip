@@ -113,14 +113,14 @@ Shape make_shape(int T, int H, int I, int E, int k, int wfmt, int wblk, int G, i
   if (wfmt == 2 && s.big_cap == 160) s.big_cap = 96;
   if (s.big) s.g1_split = s.g2_split = 1;
   // permute: one block places up to 4096 slots; beyond that the slots are
-  // split into at most 64 chunks of at least 2048, each placed by its own
+  // split into at most 64 chunks of at least 1024, each placed by its own
   // block after a counting pass
   const long n = long(T) * k;
   if (n <= 4096) {
     s.perm_chunk = int(std::max(n, 1L));
     s.perm_chunks = 1;
   } else {
-    long chunk = std::max(2048L, (n + 63) / 64);
+    long chunk = std::max(1024L, (n + 63) / 64);
     chunk = (chunk + 63) / 64 * 64;
     s.perm_chunk = int(chunk);
     s.perm_chunks = int((n + chunk - 1) / chunk);
