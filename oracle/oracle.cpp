@@ -268,7 +268,8 @@ double wval(const Cfg& c, const WSet& w, int which, int e, int64_t n, int64_t kk
   const int64_t K = which == 1 ? c.H : c.I;
   const uint8_t* codes = which == 1 ? (sh ? w.sw1 : w.w1) : (sh ? w.sw2 : w.w2);
   const void* sc = which == 1 ? (sh ? w.sw1s : w.w1s) : (sh ? w.sw2s : w.w2s);
-  const int64_t ee = sh ? 0 : e;
+  // planted (10): every routed expert reads its neighbour's matrices
+  const int64_t ee = sh ? 0 : (g_mutation == 10 ? (e + 1) % c.E : e);
   if (c.wfmt == 0) {  // FP8 e4m3 + fp32 scale per wblk x wblk block
     const int64_t b = c.wblk;
     const double code = tab.e4m3[codes[(ee * N + n) * K + kk]];

@@ -270,6 +270,64 @@ def _torch_plain_mlp(wl, w, x):
     return (hd @ W2.T).numpy()
 
 
+def _torch_expert_mlp(wl, w1, w1s, w2, w2s, x):
+    """One expert's quantised MLP over every token, PyTorch ops only (as
+    _torch_plain_mlp, for the given expert matrices)."""
+    G = wl.act_group
+    xq, xs = _torch_quant_rows(x.float(), G)
+    xd = torch.from_numpy(xq).view(torch.float8_e4m3fn).to(torch.float64) * \
+        torch.from_numpy(xs).to(torch.float64).repeat_interleave(G, 1)
+    gu = xd @ _dequant_torch(w1, w1s, wl.wfmt, wl.wblk).T
+    h = (torch.nn.functional.silu(gu[:, : wl.I]) * gu[:, wl.I:]).to(torch.float32)
+    hq, hs = _torch_quant_rows(h, G)
+    hd = torch.from_numpy(hq).view(torch.float8_e4m3fn).to(torch.float64) * \
+        torch.from_numpy(hs).to(torch.float64).repeat_interleave(G, 1)
+    return (hd @ _dequant_torch(w2, w2s, wl.wfmt, wl.wblk).T).numpy()
+
+
+def _mixture_agrees(name):
+    """The oracle layer equals the layer written with PyTorch ops only: each
+    token's output is the sum over its slots, in slot order, of the routing
+    weight times that expert's quantised MLP (dense fp64 weights from
+    PyTorch's own format casts), plus the shared expert with weight 1; a
+    masked slot (id outside [0, E)) adds nothing.  It shares no decode table,
+    quantiser, grouping or indexing with the oracle."""
+    wl = SMALL[name]
+    T = 10
+    w = synth.gen_weights(wl, seed=13)
+    x, ids, tw = synth.gen_inputs(wl, T, seed=13)
+    ids = ids.clone()
+    ids[3, 0] = -1
+    ids[7, wl.topk - 1] = wl.E
+    got = oracle.layer_for(wl, T, w).layer(x, ids, tw)
+    mlp = [_torch_expert_mlp(wl, w.w1[e], w.w1s[e], w.w2[e], w.w2s[e], x) for e in range(wl.E)]
+    ref = np.zeros((T, wl.H), np.float64)
+    for t in range(T):
+        for j in range(wl.topk):
+            e = int(ids[t, j])
+            if 0 <= e < wl.E:
+                ref[t] += float(tw[t, j]) * mlp[e][t]
+    if wl.shared:
+        ref += _torch_expert_mlp(wl, w.sw1[0], w.sw1s[0], w.sw2[0], w.sw2s[0], x)
+    assert np.abs(ref).max() > 0
+    return np.abs(got - ref).max() <= 1e-9 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_equals_torch_mixture(name):
+    assert _mixture_agrees(name)
+
+
+def test_planted_expert_slice_mistake_is_caught_by_the_mixture():
+    """Every routed expert reading its neighbour's matrices (planted in the
+    weight decode, which the brute force shares) fails the PyTorch mixture."""
+    oracle.set_mutation(10)
+    try:
+        assert not any(_mixture_agrees(n) for n in SMALL)
+    finally:
+        oracle.set_mutation(0)
+
+
 @pytest.mark.parametrize("name", ["tiny_fp8", "mxfp4"])
 def test_single_expert_equals_plain_mlp(name):
     wl = SMALL[name].with_shape(E=1, topk=1)
